@@ -1,0 +1,200 @@
+"""Decoder step and encoder append of the block-diffusion model, written plainly in fp64.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+What the pages fix:
+  * an encoder-decoder whose encoder and decoder share one set of weights (diffusers
+    DiffusionGemmaPipeline docs, "PEFT adapters" and the ``model`` parameter);
+  * a causal encoder prefills the prompt into a KV cache and later reads every finished canvas,
+    whose keys and values are appended to that cache; the decoder denoises the canvas with
+    bidirectional attention over the canvas and cross-attention to the cached context
+    (DiffusionGemma model card, "Model overview"; diffusers docs, introduction);
+  * 30 layers, a sparse MoE with 8 of 128 experts active plus 1 shared expert, a ~262K
+    vocabulary, a 256-token canvas and a 1,024-token sliding window (model card dimension table);
+  * the model returns logits [batch, canvas_length, vocab_size] (diffusers docs, class text).
+
+Readings (the pages give no layer internals; each reading is listed in the design notes):
+  * pre-norm RMSNorm before attention, before the FFN and before the LM head, with a gain
+    vector and eps = 1e-6; the embedding is a row gather with no scale;
+  * attention: one joint softmax per query over the visible cache keys and the canvas keys,
+    scale 1/sqrt(head_dim), no positional encoding, no soft-cap; query head h reads KV head
+    floor(h * Hkv / Hq); the decoder sees every canvas key, the encoder canvas key j <= i;
+    a sliding-window layer lets canvas query i (absolute position len + i) see cache position j
+    only if (len + i) - j < window;  layer l is global iff window == 0 or
+    (l + 1) % global_every == 0;
+  * MoE: router logits r = u W_r^T, softmax over the experts, the top-k by logit (lowest index
+    on ties, listed in descending order), gates = softmax weights renormalised over the top-k;
+    the shared expert is added with weight 1; every FFN is SwiGLU:
+    (silu(u W_gate^T) * (u W_up^T)) W_down^T, where the gate rows come first in W_gate_up;
+  * the QKV projection is one [(Hq + 2 Hkv) * dh, d] matrix: queries, then keys, then values,
+    head-major inside each part;
+  * the appended keys and values are those each layer computes from its normed input for the
+    canvas positions; they are stored in bf16, the cache's storage type.
+
+Weights arrive as float64 arrays holding the bf16 (storage) values; activations are not rounded,
+except the logits (rounded to bf16 before the sampler reads them) and the stored cache entries.
+"""
+import numpy as np
+
+from .numerics import round_bf16
+
+
+def rms_norm(x, gain, eps):
+    """x / sqrt(mean(x^2) + eps) * gain along the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * gain
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def softmax(x, axis=-1):
+    m = np.max(x, axis=axis, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def layer_is_global(layer, dims):
+    return dims["window"] == 0 or (layer + 1) % dims["global_every"] == 0
+
+
+def visible_cache_mask(cache_len, canvas_len, window):
+    """[C, cache_len] bool: may canvas query i see cache position j (sliding-window rule)."""
+    i = np.arange(canvas_len)[:, None]
+    j = np.arange(cache_len)[None, :]
+    if window <= 0:
+        return np.ones((canvas_len, cache_len), dtype=bool)
+    return (cache_len + i) - j < window
+
+
+def attention(q, k_cache, v_cache, k_new, v_new, cache_mask, causal):
+    """Joint softmax attention for one canvas.
+
+    q [C, Hq, dh]; k_cache, v_cache [Hkv, L, dh]; k_new, v_new [C, Hkv, dh];
+    cache_mask [C, L] bool; causal: canvas query i sees canvas key j only if j <= i.
+    Returns [C, Hq, dh].
+    """
+    clen, hq, dh = q.shape
+    hkv = k_new.shape[1]
+    out = np.zeros_like(q)
+    canvas_mask = (np.tril(np.ones((clen, clen), dtype=bool)) if causal
+                   else np.ones((clen, clen), dtype=bool))
+    mask = np.concatenate([cache_mask, canvas_mask], axis=1)          # [C, L + C]
+    for h in range(hq):
+        g = (h * hkv) // hq
+        keys = np.concatenate([k_cache[g], k_new[:, g, :]], axis=0)   # [L + C, dh]
+        vals = np.concatenate([v_cache[g], v_new[:, g, :]], axis=0)
+        s = q[:, h, :] @ keys.T / np.sqrt(dh)
+        s = np.where(mask, s, -np.inf)
+        out[:, h, :] = softmax(s, axis=-1) @ vals
+    return out
+
+
+def swiglu_ffn(u, w_gate_up, w_down):
+    """(silu(u Wg^T) * (u Wu^T)) Wd^T with Wg = first half of the rows of w_gate_up."""
+    f = w_gate_up.shape[0] // 2
+    gu = u @ w_gate_up.T
+    return (silu(gu[..., :f]) * gu[..., f:]) @ w_down.T
+
+
+def route(u, w_router, top_k):
+    """Router: logits, top-k expert ids (descending logit, lowest id on ties) and gates."""
+    r = u @ w_router.T                                                # [T, E]
+    pi = softmax(r, axis=-1)
+    ntok, n_exp = r.shape
+    idx = np.zeros((ntok, top_k), dtype=np.int64)
+    for t in range(ntok):
+        order = sorted(range(n_exp), key=lambda e: (-r[t, e], e))
+        idx[t] = order[:top_k]
+    sel = np.take_along_axis(pi, idx, axis=1)
+    gates = sel / sel.sum(axis=1, keepdims=True)
+    return r, idx, gates
+
+
+def moe(u, lw, top_k):
+    """Sparse MoE FFN: sum over the top-k experts of gate * FFN_e(u), plus the shared expert."""
+    r, idx, gates = route(u, lw["w_router"], top_k)
+    ntok, d = u.shape
+    n_exp = lw["w_router"].shape[0]
+    y = np.zeros((ntok, top_k, d))
+    for e in range(n_exp):
+        t_list, j_list = np.nonzero(idx == e)
+        if t_list.size:
+            y[t_list, j_list] = swiglu_ffn(u[t_list], lw["w_gate_up"][e], lw["w_down"][e])
+    out = swiglu_ffn(u, lw["ws_gate_up"], lw["ws_down"])
+    for j in range(top_k):
+        out = out + gates[:, j:j + 1] * y[:, j]
+    return out, dict(router_logits=r, topk_idx=idx, gates=gates)
+
+
+def split_qkv(qkv, dims):
+    hq, hkv, dh = dims["hq"], dims["hkv"], dims["dh"]
+    q = qkv[..., :hq * dh].reshape(qkv.shape[:-1] + (hq, dh))
+    k = qkv[..., hq * dh:(hq + hkv) * dh].reshape(qkv.shape[:-1] + (hkv, dh))
+    v = qkv[..., (hq + hkv) * dh:].reshape(qkv.shape[:-1] + (hkv, dh))
+    return q, k, v
+
+
+def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
+    """One transformer layer over a batch of canvases.
+
+    h [B, C, d] residual stream; k_cache, v_cache [B, Hkv, cap, dh] (this layer);
+    cache_len [B].  Returns (new h, k [B, C, Hkv, dh], v, routing info).
+    """
+    eps = dims["eps"]
+    bsz, clen, d = h.shape
+    u = rms_norm(h, lw["attn_norm"], eps)
+    q, k, v = split_qkv(u @ lw["w_qkv"].T, dims)
+    window = 0 if layer_is_global(layer, dims) else dims["window"]
+    o = np.zeros_like(q)
+    for b in range(bsz):
+        n = int(cache_len[b])
+        mask = visible_cache_mask(n, clen, window)
+        o[b] = attention(q[b], k_cache[b, :, :n], v_cache[b, :, :n], k[b], v[b], mask, causal)
+    h = h + o.reshape(bsz, clen, -1) @ lw["w_o"].T
+    u = rms_norm(h, lw["ffn_norm"], eps)
+    f, info = moe(u.reshape(bsz * clen, d), lw, dims["top_k"])
+    h = h + f.reshape(bsz, clen, d)
+    return h, k, v, info
+
+
+def decoder_forward(canvas, model, cache):
+    """Decoder pass over canvases [B, C] -> logits [B, C, V] (bf16-rounded, as float64).
+
+    cache: dict(k, v: lists over layers of [B, Hkv, cap, dh], len [B]).
+    Also returns the fp64 logits before rounding and per-layer routing info.
+    """
+    dims = model["dims"]
+    h = model["embed"][np.asarray(canvas)]
+    infos = []
+    for layer, lw in enumerate(model["layers"]):
+        h, _, _, info = layer_forward(h, lw, dims, layer, cache["k"][layer], cache["v"][layer],
+                                      cache["len"], causal=False)
+        infos.append(info)
+    z = rms_norm(h, model["final_norm"], dims["eps"]) @ model["w_lm"].T
+    return round_bf16(z), z, infos
+
+
+def encoder_append(tokens, model, cache, round_stored=True):
+    """Encoder pass over finished canvases [B, C]: causal inside the canvas, sees the cache.
+
+    Each layer stores its keys and values at [len, len + C), rounded to bf16 (the cache's storage
+    type) unless ``round_stored`` is False; len += C.  The cache dict is updated in place.
+    """
+    dims = model["dims"]
+    tokens = np.asarray(tokens)
+    bsz, clen = tokens.shape
+    h = model["embed"][tokens]
+    for layer, lw in enumerate(model["layers"]):
+        kc, vc = cache["k"][layer], cache["v"][layer]
+        if np.any(cache["len"] + clen > kc.shape[2]):
+            raise ValueError("cache capacity exceeded")
+        h, k, v, _ = layer_forward(h, lw, dims, layer, kc, vc, cache["len"], causal=True)
+        for b in range(bsz):
+            n = int(cache["len"][b])
+            store = round_bf16 if round_stored else np.asarray
+            kc[b, :, n:n + clen] = store(k[b].transpose(1, 0, 2))
+            vc[b, :, n:n + clen] = store(v[b].transpose(1, 0, 2))
+    cache["len"] = cache["len"] + clen
+    return cache
