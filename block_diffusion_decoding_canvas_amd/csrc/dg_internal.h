@@ -1,0 +1,230 @@
+// Internal declarations shared by the HIP translation units of libdg.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+// ---------------------------------------------------------------------------------------------
+// device helpers
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// XCD-aware slot remap: hardware hands consecutive workgroup ids to the 8 XCDs round-robin;
+// this maps them so that consecutive *logical* ids land on the same XCD (and share its L2).
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  const int per = grid >> 3;  // grid is a multiple of 8
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Running softmax statistics of a set of scaled logits y (in log2 units), merged exactly:
+//   m = max y, idx = lowest index holding m, R = sum over the other entries of 2^(y - m),
+//   A = sum over all entries of (y - m) 2^(y - m).
+// Entropy in nats of softmax over the set: ln(1 + R) - ln2 * A / (1 + R).
+struct SoftStats {
+  float m;
+  int idx;
+  float r;
+  float a;
+};
+
+__device__ __forceinline__ SoftStats stats_merge(SoftStats x, SoftStats y) {
+  const bool y_wins = (y.m > x.m) || (y.m == x.m && y.idx < x.idx);
+  SoftStats w = y_wins ? y : x;
+  SoftStats l = y_wins ? x : y;
+  if (l.m == -INFINITY) return w;
+  const float d = l.m - w.m;  // <= 0
+  const float s = exp2f(d);
+  w.r = w.r + (1.0f + l.r) * s;
+  w.a = w.a + (l.a + d * (1.0f + l.r)) * s;
+  return w;
+}
+
+__device__ __forceinline__ SoftStats stats_shfl_xor(SoftStats s, int o) {
+  SoftStats t;
+  t.m = __shfl_xor(s.m, o, 64);
+  t.idx = __shfl_xor(s.idx, o, 64);
+  t.r = __shfl_xor(s.r, o, 64);
+  t.a = __shfl_xor(s.a, o, 64);
+  return t;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): multipliers 0xD2511F53 / 0xCD9E8D57, Weyl key
+// increments 0x9E3779B9 / 0xBB67AE85, ten rounds, key advanced between rounds.
+struct Philox4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ Philox4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{c0, c1, c2, c3};
+}
+
+// Sampler counter layout: (w0, position, step tag, (canvas_id << 1) | stream).
+constexpr uint32_t kInitStepTag = 0xFFFFFFFFu;
+
+__device__ __forceinline__ int32_t uniform_token(uint64_t seed, uint32_t canvas_id,
+                                                 uint32_t step_tag, uint32_t pos,
+                                                 uint32_t vocab) {
+  const Philox4 r = philox10(0u, pos, step_tag, (canvas_id << 1) | 0u,
+                             static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  return static_cast<int32_t>((static_cast<uint64_t>(r.x) * vocab) >> 32);
+}
+
+// ---------------------------------------------------------------------------------------------
+// host-side launch interface (implemented in the .hip files)
+
+struct WGemmArgs {
+  const uint16_t* X;      // token rows (bf16)
+  int ldx;
+  const int32_t* x_rows;  // gather: X row of tile row r (NULL = r)
+  const uint16_t* W;      // weights [experts][N][K] (bf16)
+  long long w_estride;    // elements between experts
+  const uint16_t* W_sh;   // shared expert weights (expert id == n_experts)
+  int K;
+  int N;                  // output features (paired: F, the gate/up split)
+  int N_sh;               // shared expert's N
+  int n_experts;
+  const int32_t* chunks;  // grouped tiles: [slot] = (expert, row0, nrows); NULL = dense
+  const int32_t* n_chunks;
+  int ntok;               // dense: rows
+  int n_nblk;             // N blocks per tile
+  int grid_tiles;         // tile slots
+  void* out;
+  int ldo;
+  float* resid;           // residual (fp32) for the add epilogue
+  // LM-head statistics epilogue
+  float inv_t_log2e;      // log2(e) / T as fp32
+  SoftStats* part;        // [rows][n_nblk]
+};
+
+enum Epi { EPI_BF16 = 0, EPI_ADD_F32 = 1, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
+
+// launchers; each returns the hip error of the launch
+hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out bf16 [rows][N]
+hipError_t launch_gemm_dense_add(const WGemmArgs& a, hipStream_t s);      // resid += X W^T
+hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // out fp32
+hipError_t launch_gemm_moe_gateup(const WGemmArgs& a, hipStream_t s);     // SwiGLU act
+hipError_t launch_gemm_moe_down(const WGemmArgs& a, hipStream_t s);       // Y rows bf16
+hipError_t launch_gemm_lmhead(const WGemmArgs& a, hipStream_t s);         // logits + stats
+int gemm_lmhead_rows_per_block();
+int gemm_moe_gateup_cols_per_block();
+int gemm_moe_down_rows_per_block();
+int gemm_moe_tile_rows();
+
+struct AttnArgs {
+  const uint16_t* qkv;    // [B*C][(Hq+2Hkv)*dh]
+  const uint16_t* kc;     // this layer's cache K [B][Hkv][cap][dh]
+  const uint16_t* vc;
+  int cap;
+  int B, C, Hq, Hkv, dh;
+  int len[64];            // visible cache length per canvas (host copy)
+  int window;             // 0 = global
+  int causal;             // encoder: canvas key j visible to query i iff j <= i
+  float scale_log2e;      // log2(e) / sqrt(dh)
+  int n_split;
+  float* o_part;          // [n_split][B][Hkv][R][dh] (R = Hq/Hkv * C)
+  float* ml_part;         // [n_split][B][Hkv][R][2]
+  uint16_t* out;          // [B*C][Hq*dh]
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys);
+
+// per-token kernels
+hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, int ntok, int d,
+                        hipStream_t s);
+hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u, int ntok, int d,
+                          float eps, hipStream_t s);
+hipError_t launch_topk(const float* logits, int ntok, int n_exp, int top_k, int32_t* idx,
+                       float* gates, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int ntok, int top_k, int n_exp, int tile_rows,
+                          int32_t* perm, int32_t* inv, int32_t* chunks, int32_t* n_chunks,
+                          int max_chunks, hipStream_t s);
+hipError_t launch_combine(float* h, const uint16_t* Y, const int32_t* inv, const float* gates,
+                          int ntok, int top_k, int d, const uint16_t* next_gain,
+                          uint16_t* u_next, float eps, hipStream_t s);
+hipError_t launch_kv_write(const uint16_t* qkv, uint16_t* kc, uint16_t* vc, int B, int C,
+                           int Hq, int Hkv, int dh, int cap, const int* len, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t n, hipStream_t s);
+
+// sampler kernels
+struct EbArgs {
+  int B, C, V, step, max_steps;
+  float inv_t;            // fp32(1 / T_s)
+  float inv_t_log2e;      // fp32(inv_t * log2 e)
+  double bound;
+  double stop_entropy;
+  int stability;
+  uint64_t seed;
+  dg_eb_state st;
+  dg_step_out out;
+  const uint16_t* logits;
+  SoftStats* part;        // [B*C][n_part]
+  int n_part;
+  uint8_t* need_cand;     // [B*C] rows that take a Gumbel candidate this step
+  double* cand_score;     // [B*C][n_cand_chunks]
+  int32_t* cand_idx;
+  int n_cand_chunks;
+};
+hipError_t launch_logit_stats(const EbArgs& a, hipStream_t s);   // partials from logits
+int logit_stats_chunks(int V);
+hipError_t launch_stats_merge(const EbArgs& a, hipStream_t s);   // partials -> H, argmax
+hipError_t launch_eb_commit(const EbArgs& a, hipStream_t s);     // stop / select / renoise
+hipError_t launch_candidates(const EbArgs& a, hipStream_t s);    // Gumbel-max partials
+hipError_t launch_cand_apply(const EbArgs& a, hipStream_t s);    // write candidates
+int cand_chunks(int V);
+hipError_t launch_canvas_init(uint64_t seed, dg_eb_state st, int B, int C, int V, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,399 @@
+// Entropy-bound sampler kernels (DiffusionGemma model card, Best Practices section 1; diffusers
+// DiffusionGemmaPipeline docs, "Schedulers" and "Adaptive stopping").
+//
+//   logit_stats  bf16 logits -> per-(row, chunk) softmax statistics of y = z / T_s   (HBM bound)
+//   stats_merge  chunk statistics -> entropy (nats) and argmax per position
+//   eb_commit    one workgroup per canvas: stability, stop / finalise, stable sort of the
+//                uncommitted entropies, fp64 running sum against the bound, Philox renoise
+//   candidates   Gumbel-max draw over the vocabulary, only for rows committed by the bound
+//   cand_apply   merge the candidate partials and write the committed tokens
+//   canvas_init  uniform placeholder tokens (uniform corruption, no mask token)
+#include <float.h>
+
+#include "dg_internal.h"
+
+namespace dg {
+
+namespace {
+
+constexpr int kStatsThreads = 256;
+constexpr int kStatsChunk = 16384;   // vocabulary entries per statistics workgroup
+constexpr int kCandThreads = 256;
+constexpr int kCandChunk = 4096;     // vocabulary entries per candidate workgroup
+
+// Fold a group of 8 consecutive logits (indices base .. base+7) into running statistics.
+// The group is visited in index order, so the lowest index wins ties.
+__device__ __forceinline__ void stats_fold8(SoftStats& s, bool& bad, const uint4 raw, int base,
+                                            float c) {
+  float y[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    y[2 * k] = __uint_as_float(w[k] << 16) * c;
+    y[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * c;
+  }
+  float gm = y[0];
+  int gi = 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    if (y[k] > gm) {
+      gm = y[k];
+      gi = k;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) bad |= !(fabsf(y[k]) <= FLT_MAX);
+  int skip = -1;
+  if (gm > s.m) {
+    if (s.m == -INFINITY) {
+      s.r = 0.f;
+      s.a = 0.f;
+    } else {
+      const float d = s.m - gm;
+      const float sc = exp2f(d);
+      s.a = (s.a + d * (1.0f + s.r)) * sc;
+      s.r = (1.0f + s.r) * sc;
+    }
+    s.m = gm;
+    s.idx = base + gi;
+    skip = gi;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = y[k] - s.m;
+    const float e = (k == skip) ? 0.f : exp2f(d);
+    s.r += e;
+    s.a += d * e;
+  }
+}
+
+__device__ __forceinline__ SoftStats stats_empty() { return SoftStats{-INFINITY, 0x7fffffff, 0.f, 0.f}; }
+
+__device__ __forceinline__ SoftStats stats_merge_nan(SoftStats x, SoftStats y) {
+  const bool nan = isnan(x.r) || isnan(y.r);
+  SoftStats w = stats_merge(x, y);
+  if (nan) w.r = NAN;
+  return w;
+}
+
+// workgroup-wide merge of per-thread statistics (fixed tree order); result valid in thread 0
+__device__ SoftStats stats_block_reduce(SoftStats s) {
+  __shared__ SoftStats red[kStatsThreads / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s = stats_merge_nan(s, stats_shfl_xor(s, o));
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) red[wv] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < static_cast<int>(blockDim.x >> 6); ++k) s = stats_merge_nan(s, red[k]);
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(kStatsThreads) void k_logit_stats(EbArgs a) {
+  const int row = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int v0 = chunk * kStatsChunk;
+  const int v1 = min(a.V, v0 + kStatsChunk);
+  const uint16_t* z = a.logits + static_cast<size_t>(row) * a.V;
+  SoftStats s = stats_empty();
+  bool bad = false;
+  for (int v = v0 + threadIdx.x * 8; v < v1; v += kStatsThreads * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(z + v);
+    stats_fold8(s, bad, raw, v, a.inv_t_log2e);
+  }
+  if (bad) s.r = NAN;
+  s = stats_block_reduce(s);
+  if (threadIdx.x == 0) a.part[static_cast<size_t>(row) * a.n_part + chunk] = s;
+}
+
+// one wave per row
+__global__ __launch_bounds__(256) void k_stats_merge(EbArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.B * a.C) return;
+  const SoftStats* p = a.part + static_cast<size_t>(row) * a.n_part;
+  SoftStats s = stats_empty();
+  for (int k = lane; k < a.n_part; k += 64) s = stats_merge_nan(s, p[k]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s = stats_merge_nan(s, stats_shfl_xor(s, o));
+  if (lane == 0) {
+    float h = log1pf(s.r) - 0.69314718055994531f * s.a / (1.0f + s.r);
+    h = (h < 0.f) ? 0.f : h;  // keeps NaN
+    a.out.entropy[row] = h;
+    a.out.argmax[row] = s.idx;
+  }
+}
+
+// one workgroup of 1024 threads per canvas; position i = thread i (C <= 1024)
+__global__ __launch_bounds__(1024) void k_eb_commit(EbArgs a) {
+  __shared__ uint64_t keys[1024];
+  __shared__ double dsum[1024];
+  __shared__ uint8_t sel[1024];
+  __shared__ int n_sel;
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool live = i < a.C;
+  const size_t at = static_cast<size_t>(b) * a.C + i;
+  const int32_t* done_p = a.st.done + b;
+  if (*done_p) {  // a frozen canvas never changes
+    if (live) {
+      a.out.commit_now[at] = 0;
+      a.need_cand[at] = 0;
+    }
+    return;
+  }
+  const float h = live ? a.out.entropy[at] : 0.f;
+  const int am = live ? a.out.argmax[at] : 0;
+  const bool committed = live ? (a.st.committed[at] != 0) : true;
+  const int prev = live ? a.st.prev_argmax[at] : 0;
+
+  const int bad = __syncthreads_or(live && !(fabsf(h) <= FLT_MAX));
+  if (bad) {  // non-finite logits: sticky status, the canvas is frozen unchanged
+    if (live) {
+      a.out.commit_now[at] = 0;
+      a.need_cand[at] = 0;
+    }
+    if (i == 0) {
+      if (a.st.dev_status) atomicExch(a.st.dev_status, static_cast<int>(DG_ERR_NONFINITE));
+      a.st.done[b] = 1;
+    }
+    return;
+  }
+  const int all_same = __syncthreads_and(!live || am == prev);
+  const int stable = (a.step >= 1 && all_same) ? a.st.stable_count[b] + 1 : 0;
+  if (live) a.st.prev_argmax[at] = am;
+
+  // mean entropy: fp64 sum in a fixed tree order
+  dsum[i] = live ? static_cast<double>(h) : 0.0;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (i < o) dsum[i] += dsum[i + o];
+    __syncthreads();
+  }
+  const double mean_h = dsum[0] / a.C;
+  const int any_unc = __syncthreads_or(live && !committed);
+  const bool stop = a.stop_entropy >= 0.0 && stable >= a.stability && mean_h < a.stop_entropy;
+  if (i == 0) a.st.stable_count[b] = stable;
+
+  if (stop || a.step == a.max_steps - 1 || !any_unc) {  // finalise: remaining take the argmax
+    if (live) {
+      a.need_cand[at] = 0;
+      if (!committed) {
+        a.st.canvas[at] = am;
+        a.st.committed[at] = 1;
+        a.out.commit_now[at] = 1;
+      } else {
+        a.out.commit_now[at] = 0;
+      }
+    }
+    if (i == 0) a.st.done[b] = 1;
+    return;
+  }
+
+  // ascending (entropy, position) order of the uncommitted positions; entropies are >= 0,
+  // so their binary32 patterns order like their values
+  keys[i] = (live && !committed)
+                ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(i))
+                : ~0ull;
+  sel[i] = 0;
+  __syncthreads();
+  for (int k = 2; k <= 1024; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = i ^ j;
+      if (p > i) {
+        const uint64_t x = keys[i], y = keys[p];
+        const bool up = (i & k) == 0;
+        if ((x > y) == up) {
+          keys[i] = y;
+          keys[p] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (i == 0) {  // longest prefix whose fp64 running sum stays <= bound (sequential order)
+    double acc = 0.0;
+    int n = 0;
+    for (; n < 1024; ++n) {
+      const uint64_t kk = keys[n];
+      if (kk == ~0ull) break;
+      const double hv = static_cast<double>(__uint_as_float(static_cast<uint32_t>(kk >> 32)));
+      if (acc + hv <= a.bound) {
+        acc += hv;
+      } else {
+        break;
+      }
+    }
+    n_sel = n;
+  }
+  __syncthreads();
+  if (i < n_sel) sel[static_cast<uint32_t>(keys[i])] = 1;
+  __syncthreads();
+  const bool chosen = live && sel[i];
+  if (live) {
+    if (!committed) {
+      if (chosen) {
+        a.need_cand[at] = 1;
+        a.out.commit_now[at] = 1;
+        a.st.committed[at] = 1;
+      } else {  // full renoise: a fresh uniform token
+        a.need_cand[at] = 0;
+        a.out.commit_now[at] = 0;
+        a.st.canvas[at] = uniform_token(a.seed, a.st.canvas_id[b], static_cast<uint32_t>(a.step),
+                                        static_cast<uint32_t>(i), static_cast<uint32_t>(a.V));
+      }
+    } else {
+      a.need_cand[at] = 0;
+      a.out.commit_now[at] = 0;
+    }
+  }
+  const int all_committed = __syncthreads_and(!live || committed || chosen);
+  if (i == 0 && all_committed) a.st.done[b] = 1;
+}
+
+// Gumbel-max over one vocabulary chunk of one row: score_v = z_v * (1/T) + g_v in fp64,
+// g_v = -ln(-ln u_v), u_v = (x_v + 0.5) 2^-32 from Philox stream 1, word v & 3 of counter
+// (v >> 2, position, step, (canvas_id << 1) | 1).
+__global__ __launch_bounds__(kCandThreads) void k_candidates(EbArgs a) {
+  const int row = blockIdx.x;
+  if (!a.need_cand[row]) return;
+  const int chunk = blockIdx.y;
+  const int b = row / a.C, pos = row % a.C;
+  const uint32_t cid = a.st.canvas_id[b];
+  const uint32_t k0 = static_cast<uint32_t>(a.seed), k1 = static_cast<uint32_t>(a.seed >> 32);
+  const uint16_t* z = a.logits + static_cast<size_t>(row) * a.V;
+  const double inv_t = static_cast<double>(a.inv_t);
+  const int v0 = chunk * kCandChunk;
+  const int v1 = min(a.V, v0 + kCandChunk);
+  double best = -INFINITY;
+  int best_v = 0x7fffffff;
+  for (int v = v0 + threadIdx.x * 8; v < v1; v += kCandThreads * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(z + v);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const Philox4 r0 = philox10(static_cast<uint32_t>(v >> 2), pos, a.step, (cid << 1) | 1u, k0, k1);
+    const Philox4 r1 = philox10(static_cast<uint32_t>((v >> 2) + 1), pos, a.step, (cid << 1) | 1u,
+                                k0, k1);
+    const uint32_t x[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float zf = __uint_as_float(k & 1 ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+      const double u = (static_cast<double>(x[k]) + 0.5) * 0x1p-32;
+      const double g = -log(-log(u));
+      const double sc = static_cast<double>(zf) * inv_t + g;
+      if (sc > best) {
+        best = sc;
+        best_v = v + k;
+      }
+    }
+  }
+  // reduce (max score, lowest index)
+  __shared__ double rs[kCandThreads / 64];
+  __shared__ int ri[kCandThreads / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ob = __shfl_xor(best, o, 64);
+    const int ov = __shfl_xor(best_v, o, 64);
+    if (ob > best || (ob == best && ov < best_v)) {
+      best = ob;
+      best_v = ov;
+    }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    rs[wv] = best;
+    ri[wv] = best_v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kCandThreads / 64; ++k) {
+      if (rs[k] > best || (rs[k] == best && ri[k] < best_v)) {
+        best = rs[k];
+        best_v = ri[k];
+      }
+    }
+    a.cand_score[static_cast<size_t>(row) * a.n_cand_chunks + chunk] = best;
+    a.cand_idx[static_cast<size_t>(row) * a.n_cand_chunks + chunk] = best_v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cand_apply(EbArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.B * a.C || !a.need_cand[row]) return;
+  double best = -INFINITY;
+  int best_v = 0x7fffffff;
+  for (int k = lane; k < a.n_cand_chunks; k += 64) {
+    const double sc = a.cand_score[static_cast<size_t>(row) * a.n_cand_chunks + k];
+    const int v = a.cand_idx[static_cast<size_t>(row) * a.n_cand_chunks + k];
+    if (sc > best || (sc == best && v < best_v)) {
+      best = sc;
+      best_v = v;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ob = __shfl_xor(best, o, 64);
+    const int ov = __shfl_xor(best_v, o, 64);
+    if (ob > best || (ob == best && ov < best_v)) {
+      best = ob;
+      best_v = ov;
+    }
+  }
+  if (lane == 0) a.st.canvas[row] = best_v;
+}
+
+__global__ __launch_bounds__(256) void k_canvas_init(uint64_t seed, dg_eb_state st, int B, int C,
+                                                     int V) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * C) return;
+  const int b = t / C, i = t % C;
+  st.canvas[t] = uniform_token(seed, st.canvas_id[b], kInitStepTag, static_cast<uint32_t>(i),
+                               static_cast<uint32_t>(V));
+  st.committed[t] = 0;
+  st.prev_argmax[t] = 0;
+  if (i == 0) {
+    st.stable_count[b] = 0;
+    st.done[b] = 0;
+  }
+  if (t == 0 && st.dev_status) *st.dev_status = 0;
+}
+
+}  // namespace
+
+int logit_stats_chunks(int V) { return (V + kStatsChunk - 1) / kStatsChunk; }
+int cand_chunks(int V) { return (V + kCandChunk - 1) / kCandChunk; }
+
+hipError_t launch_logit_stats(const EbArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.C, logit_stats_chunks(a.V));
+  hipLaunchKernelGGL(k_logit_stats, grid, dim3(kStatsThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_merge(const EbArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_stats_merge, dim3((a.B * a.C + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_eb_commit(const EbArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_eb_commit, dim3(a.B), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_candidates(const EbArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.C, a.n_cand_chunks);
+  hipLaunchKernelGGL(k_candidates, grid, dim3(kCandThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cand_apply(const EbArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_cand_apply, dim3((a.B * a.C + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_canvas_init(uint64_t seed, dg_eb_state st, int B, int C, int V, hipStream_t s) {
+  hipLaunchKernelGGL(k_canvas_init, dim3((B * C + 255) / 256), dim3(256), 0, s, seed, st, B, C, V);
+  return hipGetLastError();
+}
+
+}  // namespace dg

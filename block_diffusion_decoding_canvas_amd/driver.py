@@ -1,0 +1,219 @@
+"""Thin Python driver over the C ABI: torch owns device memory and streams, libdg.so computes.
+
+Names follow include/dg.h.  Nothing here computes any part of the path; it allocates caller-owned
+buffers, fills the C structs and checks statuses.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import check, ptr, stream_ptr
+
+
+def eb_params(max_steps=48, t_max=0.8, t_min=0.4, entropy_bound=0.1, stop_entropy=0.005,
+              stability=1, seed=2):
+    """Sampler constants; the defaults are the model card's (Best Practices section 1)."""
+    return _lib.dg_eb_params(int(max_steps), float(t_max), float(t_min), float(entropy_bound),
+                             float(stop_entropy), int(stability), int(seed))
+
+
+def eb_params_from_dict(p, seed):
+    return eb_params(p["max_steps"], p["t_max"], p["t_min"], p["entropy_bound"],
+                     p["stop_entropy"], p["stability"], seed)
+
+
+class SamplerState:
+    """Per-canvas sampler state (device tensors), see dg_eb_state."""
+
+    def __init__(self, batch, canvas_len, device="cuda", canvas_ids=None):
+        self.B, self.C = batch, canvas_len
+        self.canvas = torch.zeros((batch, canvas_len), dtype=torch.int32, device=device)
+        self.committed = torch.zeros((batch, canvas_len), dtype=torch.uint8, device=device)
+        self.prev_argmax = torch.zeros((batch, canvas_len), dtype=torch.int32, device=device)
+        self.stable_count = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.done = torch.zeros(batch, dtype=torch.int32, device=device)
+        ids = np.arange(batch, dtype=np.int64) if canvas_ids is None else np.asarray(canvas_ids)
+        self.canvas_id = torch.tensor(ids.astype(np.int32), dtype=torch.int32, device=device)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def struct(self):
+        return _lib.dg_eb_state(*(ptr(t) for t in (self.canvas, self.committed, self.prev_argmax,
+                                                   self.stable_count, self.done, self.canvas_id,
+                                                   self.dev_status)))
+
+    def host(self):
+        return dict(canvas=self.canvas.cpu().numpy().astype(np.int64),
+                    committed=self.committed.cpu().numpy().astype(bool),
+                    prev_argmax=self.prev_argmax.cpu().numpy().astype(np.int64),
+                    stable_count=self.stable_count.cpu().numpy().astype(np.int64),
+                    done=self.done.cpu().numpy().astype(bool))
+
+    def load_host(self, st):
+        self.canvas.copy_(torch.from_numpy(np.asarray(st["canvas"], dtype=np.int32)))
+        self.committed.copy_(torch.from_numpy(np.asarray(st["committed"], dtype=np.uint8)))
+        self.prev_argmax.copy_(torch.from_numpy(np.asarray(st["prev_argmax"], dtype=np.int32)))
+        self.stable_count.copy_(torch.from_numpy(np.asarray(st["stable_count"], dtype=np.int32)))
+        self.done.copy_(torch.from_numpy(np.asarray(st["done"], dtype=np.int32)))
+
+
+class StepOut:
+    """Per-step outputs, see dg_step_out."""
+
+    def __init__(self, batch, canvas_len, vocab, device="cuda", with_logits=True):
+        self.entropy = torch.zeros((batch, canvas_len), dtype=torch.float32, device=device)
+        self.argmax = torch.zeros((batch, canvas_len), dtype=torch.int32, device=device)
+        self.commit_now = torch.zeros((batch, canvas_len), dtype=torch.uint8, device=device)
+        self.logits = (torch.zeros((batch, canvas_len, vocab), dtype=torch.bfloat16,
+                                   device=device) if with_logits else None)
+
+    def struct(self):
+        return _lib.dg_step_out(ptr(self.entropy), ptr(self.argmax), ptr(self.commit_now),
+                                ptr(self.logits))
+
+
+def workspace(nbytes, device="cuda"):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def canvas_init(params, state, vocab, stream=None):
+    lib = _lib.load()
+    st = state.struct()
+    check(lib.dg_canvas_init(ctypes.byref(params), ctypes.byref(st), state.B, state.C, vocab,
+                             stream_ptr(stream)), "dg_canvas_init")
+
+
+def eb_sample(logits, step, params, state, out, ws=None, stream=None):
+    """Standalone EB sampler on bf16 logits [B, C, V] (device)."""
+    lib = _lib.load()
+    b, c, v = logits.shape
+    need = lib.dg_eb_workspace_bytes(b, c, v)
+    if ws is None:
+        ws = workspace(need, logits.device)
+    st, o = state.struct(), out.struct()
+    check(lib.dg_eb_sample(ptr(logits), b, c, v, step, ctypes.byref(params), ctypes.byref(st),
+                           ctypes.byref(o), ptr(ws), ws.numel(), stream_ptr(stream)),
+          "dg_eb_sample")
+    return ws
+
+
+def dims_struct(d):
+    return _lib.dg_dims(d["n_layers"], d["d"], d["hq"], d["hkv"], d["dh"], d["E"], d["top_k"],
+                        d["F"], d["Fs"], d["V"], d["C"], d["window"], d["global_every"],
+                        _lib.DG_BF16, d["eps"])
+
+
+class Model:
+    """A dg_model handle over device weights (dict from synth.model_to_device or
+    synth.make_model_device).  Keeps the tensors alive for the handle's lifetime."""
+
+    LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up", "w_down",
+                  "ws_gate_up", "ws_down")
+
+    def __init__(self, weights):
+        lib = _lib.load()
+        self.weights = weights
+        self.dims = dict(weights["dims"])
+        n = self.dims["n_layers"]
+        layers = (_lib.dg_layer_w * n)()
+        for i, lw in enumerate(weights["layers"]):
+            for k in self.LAYER_KEYS:
+                assert lw[k].dtype == torch.bfloat16 and lw[k].is_contiguous(), k
+                setattr(layers[i], k, lw[k].data_ptr())
+        self._dims = dims_struct(self.dims)
+        h = ctypes.c_void_p()
+        check(lib.dg_model_create(ctypes.byref(self._dims), layers, ptr(weights["embed"]),
+                                  ptr(weights["final_norm"]), ptr(weights["w_lm"]),
+                                  ctypes.byref(h)), "dg_model_create")
+        self.handle = h
+
+    def workspace_bytes(self, batch):
+        return _lib.load().dg_workspace_bytes(self.handle, batch)
+
+    def close(self):
+        if self.handle:
+            _lib.load().dg_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class KVCache:
+    """Static KV cache: bf16 [n_layers][B][Hkv][cap][dh] K and V, host lengths."""
+
+    def __init__(self, dims, batch, cap, device="cuda", k=None, v=None, lengths=None):
+        shape = (dims["n_layers"], batch, dims["hkv"], cap, dims["dh"])
+        self.k = k if k is not None else torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.v = v if v is not None else torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
+        self.batch, self.cap = batch, cap
+        self.len = (ctypes.c_int32 * batch)(*([0] * batch if lengths is None else
+                                              [int(x) for x in lengths]))
+
+    @classmethod
+    def from_host(cls, dims, cache, cap, device="cuda"):
+        k = torch.from_numpy(np.stack(cache["k"])).to(device=device, dtype=torch.bfloat16)
+        v = torch.from_numpy(np.stack(cache["v"])).to(device=device, dtype=torch.bfloat16)
+        return cls(dims, k.shape[1], cap, device, k, v, cache["len"])
+
+    def struct(self):
+        return _lib.dg_kv(ptr(self.k), ptr(self.v), self.batch, self.cap, self.len)
+
+    def lengths(self):
+        return [self.len[i] for i in range(self.batch)]
+
+
+def decoder_step(model, kv, step, params, state, out, ws, stream=None):
+    lib = _lib.load()
+    kvs, st, o = kv.struct(), state.struct(), out.struct()
+    check(lib.dg_decoder_step(model.handle, ctypes.byref(kvs), step, ctypes.byref(params),
+                              ctypes.byref(st), ctypes.byref(o), ptr(ws), ws.numel(),
+                              stream_ptr(stream)), "dg_decoder_step")
+
+
+def kv_append_canvas(model, kv, tokens, ws, stream=None):
+    lib = _lib.load()
+    kvs = kv.struct()
+    check(lib.dg_kv_append_canvas(model.handle, ctypes.byref(kvs), ptr(tokens), ptr(ws),
+                                  ws.numel(), stream_ptr(stream)), "dg_kv_append_canvas")
+
+
+def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=None,
+                  gates=None, stream=None):
+    lib = _lib.load()
+    kvs = kv.struct()
+    check(lib.dg_layer_forward(model.handle, ctypes.byref(kvs), layer, int(causal), ptr(h),
+                               ptr(router_logits), ptr(topk_idx), ptr(gates), ptr(ws),
+                               ws.numel(), stream_ptr(stream)), "dg_layer_forward")
+
+
+def copy_bytes(dst, src, nbytes, stream=None):
+    check(_lib.load().dg_copy_bytes(ptr(dst), ptr(src), nbytes, stream_ptr(stream)),
+          "dg_copy_bytes")
+
+
+class KernelTimer:
+    """HIP-event timing of library kernel classes (dg_prof_*)."""
+
+    def __init__(self):
+        self.lib = _lib.load()
+        n = self.lib.dg_prof_num_classes()
+        self.names = [self.lib.dg_prof_class_name(i).decode() for i in range(n)]
+
+    def enable(self, on=True):
+        check(self.lib.dg_prof_enable(int(on)), "dg_prof_enable")
+
+    def reset(self):
+        check(self.lib.dg_prof_reset(), "dg_prof_reset")
+
+    def read(self, name):
+        ms = ctypes.c_double()
+        cnt = ctypes.c_int64()
+        check(self.lib.dg_prof_read(self.names.index(name), ctypes.byref(ms), ctypes.byref(cnt)),
+              "dg_prof_read")
+        return ms.value, cnt.value

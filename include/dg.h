@@ -1,0 +1,187 @@
+/*
+ * dg.h - C ABI of libdg.so: one denoising step of a block-diffusion decoder over a token canvas,
+ * fused with the entropy-bound (EB) sampler, and the append of a finished canvas to the KV cache.
+ *
+ * What the calls compute comes from these passages:
+ *   - DiffusionGemma model card, "Model overview": an encoder prefills the prompt into a KV cache;
+ *     a decoder denoises a block ("canvas") of tokens with bidirectional attention over the canvas
+ *     and cross-attention to the cached context; a finished canvas is processed by the encoder
+ *     and appended to the KV cache before the next canvas starts.  Dimension table: 30 layers,
+ *     8 of 128 experts active plus 1 shared, canvas 256, vocabulary ~262K, sliding window 1,024.
+ *   - DiffusionGemma model card, Best Practices section 1 (diffusion sampling settings): at most
+ *     48 steps; temperature decaying linearly 0.8 -> 0.4 for logit shaping; each step selects the
+ *     lowest-entropy tokens while their bound stays under the entropy bound 0.1; unselected tokens
+ *     are fully renoised; early stop only when the mean canvas entropy is below 0.005 and the
+ *     most likely tokens are unchanged over two consecutive steps.
+ *   - diffusers DiffusionGemmaPipeline docs: "Schedulers" (EntropyBoundScheduler, t_max/t_min,
+ *     entropy_bound), "Static cache and compilation" (fixed-shape cache, graph replay),
+ *     "Adaptive stopping" (per-sample freeze, stability_threshold, confidence_threshold=None
+ *     disables), the class text (uniform corruption, no mask token; logits [batch, canvas, vocab]).
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is DEVICE memory owned by the caller, unless marked "host".  The
+ *     library borrows pointers and never frees them; it never allocates device memory.
+ *   - bf16 tensors are passed as uint16_t bit patterns (or const void*), row-major, with the
+ *     layouts stated below.  Weight matrices are [out_features, in_features].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous on it:
+ *     DG_OK means "validated and enqueued".  No call synchronises the host or allocates, so a
+ *     decoder step can be captured in a HIP graph.
+ *   - Validation is synchronous and happens before anything is enqueued: on a non-OK status
+ *     nothing was enqueued and dg_last_error() describes the problem.  No C++ exception crosses
+ *     the ABI.
+ *   - A model is immutable after dg_model_create.  Calls with distinct state, workspace and
+ *     stream may run concurrently; calls sharing a workspace must be ordered by the caller.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_NULL = 1,         /* a required pointer is NULL                                     */
+  DG_ERR_SHAPE = 2,        /* inconsistent or unsupported dimensions                          */
+  DG_ERR_DTYPE = 3,        /* unsupported weight dtype                                        */
+  DG_ERR_CAPACITY = 4,     /* len[b] + canvas_len > KV capacity                               */
+  DG_ERR_WORKSPACE = 5,    /* workspace smaller than the size query returned                  */
+  DG_ERR_STATE = 6,        /* step index outside [0, max_steps) or bad sampler parameters     */
+  DG_ERR_UNSUPPORTED = 7,  /* valid request this build does not implement                     */
+  DG_ERR_HIP = 8,          /* a HIP runtime call failed                                        */
+  DG_ERR_NONFINITE = 9     /* written to *dev_status when a logit row is not finite           */
+} dg_status;
+
+enum { DG_BF16 = 0 };
+
+/* Model dimensions.  head_dim, d_model, ffn_inner and shared_inner must be multiples of 32;
+ * n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts <= 256; vocab a multiple of 256;
+ * 1 <= canvas_len <= 1024; window == 0 (every layer global) or window >= canvas_len. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, ffn_inner, shared_inner, vocab, canvas_len;
+  int32_t window;        /* sliding window in tokens; 0 = every layer global                  */
+  int32_t global_every;  /* layer l is global iff window == 0 || (l + 1) % global_every == 0   */
+  int32_t wdtype;        /* DG_BF16                                                           */
+  float norm_eps;        /* RMSNorm epsilon (1e-6)                                            */
+} dg_dims;
+
+/* One layer's weights (device, bf16).  Shapes with d = d_model, Hq, Hkv, dh, E, F, Fs:
+ *   attn_norm, ffn_norm [d]            RMSNorm gains
+ *   w_qkv   [(Hq + 2 Hkv) dh, d]       rows: queries, keys, values; head-major in each part
+ *   w_o     [d, Hq dh]
+ *   w_router[E, d]
+ *   w_gate_up [E][2F][d]               per expert: F gate rows, then F up rows
+ *   w_down    [E][d][F]
+ *   ws_gate_up[2Fs][d], ws_down [d][Fs]  the shared expert                                   */
+typedef struct {
+  const void *attn_norm, *w_qkv, *w_o, *ffn_norm, *w_router;
+  const void *w_gate_up, *w_down, *ws_gate_up, *ws_down;
+} dg_layer_w;
+
+typedef struct dg_model dg_model;
+
+/* Build a model handle that BORROWS every pointer until dg_model_destroy.  The encoder and the
+ * decoder share these weights (diffusers docs, "PEFT adapters": base weights are tied).
+ * layers: host array [n_layers]; embed [V, d]; final_norm [d]; w_lm [V, d] (may alias embed). */
+dg_status dg_model_create(const dg_dims* dims, const dg_layer_w* layers, const void* embed,
+                          const void* final_norm, const void* w_lm, dg_model** out);
+void dg_model_destroy(dg_model* model);
+
+/* Static KV cache (diffusers docs, "Static cache and compilation").
+ * k, v: bf16 [n_layers][batch][Hkv][cap][dh]; len: HOST array [batch] of valid lengths. */
+typedef struct {
+  void *k, *v;
+  int32_t batch, cap;
+  int32_t* len;
+} dg_kv;
+
+/* Sampler constants; defaults are the model card's (Best Practices section 1). */
+typedef struct {
+  int32_t max_steps;      /* 48                                                               */
+  double t_max, t_min;    /* 0.8 -> 0.4, linear over steps 0 .. max_steps-1                   */
+  double entropy_bound;   /* 0.1: summed entropy of the positions committed in one step       */
+  double stop_entropy;    /* 0.005: stop when mean entropy < this; negative disables the stop */
+  int32_t stability;      /* 1: argmax unchanged over two consecutive steps                   */
+  uint64_t seed;          /* Philox4x32-10 key                                                */
+} dg_eb_params;
+
+/* Per-canvas sampler state (device, caller-owned, carried across calls).  Shapes [B, C] or [B]. */
+typedef struct {
+  int32_t* canvas;        /* [B, C] token ids, in/out                                         */
+  uint8_t* committed;     /* [B, C] 1 = committed (kept)                                      */
+  int32_t* prev_argmax;   /* [B, C] argmax of the previous step                               */
+  int32_t* stable_count;  /* [B] consecutive steps with an unchanged argmax                    */
+  int32_t* done;          /* [B] 1 = frozen; later calls never modify this canvas              */
+  const uint32_t* canvas_id; /* [B] Philox stream id of each canvas (< 2^31)                  */
+  int32_t* dev_status;    /* [1] sticky; set to DG_ERR_NONFINITE on a non-finite logit row    */
+} dg_eb_state;
+
+/* Per-step outputs (device, caller-owned). */
+typedef struct {
+  float* entropy;         /* [B, C] entropy (nats) of softmax(logits / T_s)                   */
+  int32_t* argmax;        /* [B, C] argmax of the logits, lowest index on ties                */
+  uint8_t* commit_now;    /* [B, C] positions committed by this step (incl. finalised ones)   */
+  uint16_t* logits;       /* [B, C, V] bf16 logits (dg_decoder_step writes them)              */
+} dg_step_out;
+
+/* Workspace sizes in bytes (0 on invalid arguments). */
+size_t dg_workspace_bytes(const dg_model* model, int32_t batch);
+size_t dg_eb_workspace_bytes(int32_t batch, int32_t canvas_len, int32_t vocab);
+
+/* Initial canvases: uniform placeholder tokens (uniform corruption, no mask token), committed = 0,
+ * stable_count = 0, done = 0.  C <= 1024. */
+dg_status dg_canvas_init(const dg_eb_params* params, dg_eb_state* state, int32_t batch,
+                         int32_t canvas_len, int32_t vocab, void* stream);
+
+/* One denoising step at step index `step` (0 <= step < max_steps): decoder forward over the
+ * canvases (bidirectional canvas attention joined with cross-attention to kv, routed + shared
+ * MoE, LM head), then the EB sampler update of `state`.  Writes out->logits/entropy/argmax/
+ * commit_now.  kv is read only; kv->len[b] + canvas_len <= kv->cap is not required here. */
+dg_status dg_decoder_step(const dg_model* model, const dg_kv* kv, int32_t step,
+                          const dg_eb_params* params, dg_eb_state* state, dg_step_out* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The EB sampler alone on given bf16 logits [B, C, V] (out->logits is ignored). */
+dg_status dg_eb_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len, int32_t vocab,
+                       int32_t step, const dg_eb_params* params, dg_eb_state* state,
+                       dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Encoder pass over finished canvases tokens [B, C] (causal inside the canvas, sees the cache);
+ * every layer writes its keys/values at [len[b], len[b] + C).  On DG_OK the HOST array kv->len
+ * is advanced by C immediately (the device writes are enqueued). */
+dg_status dg_kv_append_canvas(const dg_model* model, dg_kv* kv, const int32_t* tokens,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* dg_last_error(void);
+
+/* ---- stage entry points used by the parity tests and the benchmark ------------------------ */
+
+/* One decoder (causal = 0) or encoder (causal = 1) layer on a residual stream h [B*C, d] fp32,
+ * updated in place.  Optional trace outputs (NULL to skip): router logits fp32 [B*C, E],
+ * top-k ids int32 [B*C, k] (descending logit), gates fp32 [B*C, k]. */
+dg_status dg_layer_forward(const dg_model* model, const dg_kv* kv, int32_t layer, int32_t causal,
+                           float* h, float* router_logits, int32_t* topk_idx, float* gates,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Plain device copy of n bytes (bandwidth / counter calibration). */
+dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream);
+
+/* Kernel timing: when enabled, the library records HIP events around every launch of the named
+ * kernel class on the call's stream and accumulates their durations.  Classes are listed by
+ * dg_prof_class_name(i) for i in [0, dg_prof_num_classes()). */
+int32_t dg_prof_num_classes(void);
+const char* dg_prof_class_name(int32_t cls);
+dg_status dg_prof_enable(int32_t on);
+/* Synchronises the recorded events and returns the total milliseconds and launch count. */
+dg_status dg_prof_read(int32_t cls, double* total_ms, int64_t* launches);
+dg_status dg_prof_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI library: it loads without a GPU, exports every declared symbol, and
+host-side validation rejects bad calls before anything is enqueued (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_decoding_canvas_amd import _lib, driver
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "dg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(_lib.EXPORTED)
+
+
+def _tiny_dims(**kw):
+    d = dict(n_layers=2, d=64, hq=4, hkv=4, dh=16, E=8, top_k=2, F=128, Fs=128, V=512, C=16,
+             window=0, global_every=1, eps=1e-6)
+    d.update(kw)
+    return driver.dims_struct(d)
+
+
+def _create(dims, null_layer=False):
+    lib = _lib.load()
+    n = dims.n_layers
+    layers = (_lib.dg_layer_w * n)()
+    fake = 0x1000
+    for i in range(n):
+        for k in driver.Model.LAYER_KEYS:
+            setattr(layers[i], k, fake)
+    if null_layer:
+        layers[n - 1].w_down = None
+    h = ctypes.c_void_p()
+    st = lib.dg_model_create(ctypes.byref(dims), layers, ctypes.c_void_p(fake),
+                             ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.byref(h))
+    return st, h
+
+
+def test_model_create_validation():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    assert st == 0 and h.value
+    assert lib.dg_workspace_bytes(h, 1) > 0
+    lib.dg_model_destroy(h)
+    bad = [dict(hq=6, hkv=4), dict(top_k=9), dict(d=48), dict(F=100), dict(V=500),
+           dict(C=0), dict(C=2000), dict(window=8), dict(dh=8)]
+    for kw in bad:
+        st, _ = _create(_tiny_dims(**kw))
+        assert st == 2, kw                       # DG_ERR_SHAPE
+        assert lib.dg_last_error()
+    st, _ = _create(_tiny_dims(), null_layer=True)
+    assert st == 1                               # DG_ERR_NULL
+    d = _tiny_dims()
+    d.wdtype = 7
+    st, _ = _create(d)
+    assert st == 3                               # DG_ERR_DTYPE
+
+
+def test_eb_sample_validation_before_launch():
+    lib = _lib.load()
+    p = driver.eb_params()
+    fake = ctypes.c_void_p(0x1000)
+    state = _lib.dg_eb_state(*([0x1000] * 7))
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0)
+    need = lib.dg_eb_workspace_bytes(1, 256, 262144)
+    assert need > 0
+
+    def call(step=0, b=1, c=256, v=262144, ws=need, params=p, st=state, o=out, logits=fake):
+        return lib.dg_eb_sample(logits, b, c, v, step, ctypes.byref(params),
+                                ctypes.byref(st) if st is not None else None,
+                                ctypes.byref(o), fake, ws, None)
+
+    assert call(step=48) == 6                    # DG_ERR_STATE
+    assert call(step=-1) == 6
+    assert call(ws=need - 1) == 5                # DG_ERR_WORKSPACE
+    assert call(v=1000) == 2                     # DG_ERR_SHAPE
+    assert call(c=2048) == 2
+    assert call(logits=None) == 1                # DG_ERR_NULL
+    st2 = _lib.dg_eb_state(*([0x1000] * 7))
+    st2.done = None
+    assert call(st=st2) == 1
+    bad = driver.eb_params(t_min=0.0)
+    assert call(params=bad) == 6
+
+
+def test_decoder_calls_validate_kv_and_step():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    assert st == 0
+    lens = (ctypes.c_int32 * 1)(60)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens)
+    p = driver.eb_params(max_steps=8)
+    state = _lib.dg_eb_state(*([0x1000] * 7))
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0x1000)
+    ws = lib.dg_workspace_bytes(h, 1)
+    fake = ctypes.c_void_p(0x1000)
+    # append past capacity: 60 + 16 > 64
+    assert lib.dg_kv_append_canvas(h, ctypes.byref(kv), fake, fake, ws, None) == 4
+    assert lens[0] == 60
+    assert lib.dg_decoder_step(h, ctypes.byref(kv), 8, ctypes.byref(p), ctypes.byref(state),
+                               ctypes.byref(out), fake, ws, None) == 6
+    assert lib.dg_decoder_step(h, ctypes.byref(kv), 0, ctypes.byref(p), ctypes.byref(state),
+                               ctypes.byref(out), fake, ws - 1, None) == 5
+    out.logits = None
+    assert lib.dg_decoder_step(h, ctypes.byref(kv), 0, ctypes.byref(p), ctypes.byref(state),
+                               ctypes.byref(out), fake, ws, None) == 1
+    lib.dg_model_destroy(h)
+
+
+def test_prof_classes_named():
+    t = driver.KernelTimer()
+    assert "moe_gateup" in t.names and "lmhead" in t.names and "attention" in t.names

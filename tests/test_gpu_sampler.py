@@ -1,0 +1,199 @@
+"""GPU parity of the standalone EB sampler (dg_eb_sample, dg_canvas_init) against the oracle.
+
+Workload: bf16 logits [256, 262144] with 30% peaked rows (one logit 12, rest N(0,1)), 40% moderate
+rows N(0, 2) and 30% near-flat rows N(0, 0.1), at steps 0, 24, 36, 46 and 47 of 48, plus the full
+48-step sweep with state carried; edge cases on small shapes.
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_decoding_canvas_amd import driver, synth
+from oracle import sampler as osamp
+from tests.parity_util import assert_entropy_close, mean_is_robust, selection_is_robust
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def c2_logits():
+    z, cls = synth.sampler_logits(256, 262144, seed=1)
+    return z.reshape(1, 256, 262144), cls
+
+
+def _gpu_state_from_host(st, B, C, ids=None):
+    s = driver.SamplerState(B, C, DEV, canvas_ids=ids)
+    s.load_host(st)
+    return s
+
+
+def compare_step(z64, step, params, seed, ids, st_before, gpu_state, gpu_out, what):
+    """Run the oracle step from st_before and compare with the GPU outputs/state.
+    Returns the oracle state after the step, or None if a certified near-tie made them diverge."""
+    st = copy.deepcopy(st_before)
+    ref = osamp.eb_step(z64, step, params, st, seed, ids)
+    h_gpu = gpu_out.entropy.cpu().numpy().astype(np.float64)
+    a_gpu = gpu_out.argmax.cpu().numpy().astype(np.int64)
+    assert np.array_equal(a_gpu, ref["argmax"]), f"{what}: argmax differs"
+    assert_entropy_close(h_gpu, ref["entropy"], what)
+    g = gpu_state.host()
+    B, C = h_gpu.shape
+    for b in range(B):
+        if st_before["done"][b]:
+            assert np.array_equal(g["canvas"][b], st_before["canvas"][b]), "frozen canvas changed"
+            continue
+        eps = 2.0 * np.abs(h_gpu[b] - ref["entropy"][b]) + 1e-30
+        unc = ~st_before["committed"][b]
+        robust = selection_is_robust(ref["entropy"][b], eps, unc, params["entropy_bound"])
+        if params["stop_entropy"] >= 0:
+            robust &= mean_is_robust(ref["entropy"][b], eps, params["stop_entropy"])
+        if not robust:
+            return None
+        cn = gpu_out.commit_now.cpu().numpy().astype(bool)[b]
+        assert np.array_equal(cn, ref["commit_now"][b]), f"{what}: commit mask differs (b={b})"
+        for k in ("committed", "done", "stable_count", "prev_argmax"):
+            assert np.array_equal(g[k][b], st[k][b]), f"{what}: {k} differs (b={b})"
+        # candidate tokens: certified by the oracle's top-2 Gumbel score gap
+        for i in ref["selected"][b]:
+            _, gap = osamp.gumbel_candidate(z64[b, i], ref["inv_t"], seed, ids[b], step, i)
+            if gap > 1e-10:
+                assert g["canvas"][b][i] == st["canvas"][b][i], f"{what}: candidate at {i}"
+        others = [i for i in range(C) if i not in set(ref["selected"][b])]
+        assert np.array_equal(g["canvas"][b][others], st["canvas"][b][others]), \
+            f"{what}: renoised/finalised tokens differ"
+    return st
+
+
+def test_canvas_init_matches_oracle():
+    B, C, V = 4, 256, 262144
+    s = driver.SamplerState(B, C, DEV, canvas_ids=[0, 1, 5, 9])
+    s.done.fill_(7)
+    driver.canvas_init(driver.eb_params(seed=2), s, V)
+    ref = osamp.init_canvas(2, [0, 1, 5, 9], C, V)
+    h = s.host()
+    assert np.array_equal(h["canvas"], ref)
+    assert not h["committed"].any() and not h["done"].any()
+
+
+@pytest.mark.parametrize("step", [0, 24, 36, 46, 47])
+def test_c2_single_step(c2_logits, step):
+    z, _ = c2_logits
+    params = dict(osamp.default_params(), stop_entropy=-1.0)
+    seed, ids = 2, [0]
+    st0 = osamp.new_state(osamp.init_canvas(seed, ids, 256, 262144))
+    gs = _gpu_state_from_host(st0, 1, 256)
+    out = driver.StepOut(1, 256, 262144, DEV, with_logits=False)
+    zt = synth.to_device_bf16(z, DEV)
+    driver.eb_sample(zt, step, driver.eb_params_from_dict(params, seed), gs, out)
+    torch.cuda.synchronize()
+    st = compare_step(z.astype(np.float64), step, params, seed, ids, st0, gs, out, f"s={step}")
+    assert st is not None, "certified near-tie on the standalone workload"
+    n = int(out.commit_now.sum())
+    if step == 0:
+        assert n == 0
+    if step == 47:
+        assert n == 256 and int(gs.done[0]) == 1
+
+
+def test_c2_sweep_48_steps(c2_logits):
+    z, cls = c2_logits
+    params = dict(osamp.default_params(), stop_entropy=-1.0)
+    seed, ids = 2, [0]
+    st = osamp.new_state(osamp.init_canvas(seed, ids, 256, 262144))
+    gs = _gpu_state_from_host(st, 1, 256)
+    out = driver.StepOut(1, 256, 262144, DEV, with_logits=False)
+    zt = synth.to_device_bf16(z, DEV)
+    z64 = z.astype(np.float64)
+    p = driver.eb_params_from_dict(params, seed)
+    ws = None
+    compared = 0
+    for s in range(48):
+        ws = driver.eb_sample(zt, s, p, gs, out, ws)
+        torch.cuda.synchronize()
+        nxt = compare_step(z64, s, params, seed, ids, st, gs, out, f"sweep s={s}")
+        if nxt is None:
+            break
+        st = nxt
+        compared += 1
+    assert compared >= 40
+    if compared == 48:
+        h = gs.host()
+        assert h["done"][0] and h["committed"][0].all()
+        # peaked rows commit before the last step, the others only at finalisation
+        assert st["committed"][0].all()
+
+
+def _small_case(B, C, V, seed_logits, scale):
+    rng = np.random.default_rng(seed_logits)
+    z = synth.to_bf16_values(rng.standard_normal((B, C, V)).astype(np.float32) * scale)
+    return z
+
+
+@pytest.mark.parametrize("bound", [0.0, 0.1, 1e9])
+def test_small_ragged_batch_with_frozen_canvas(bound):
+    B, C, V = 3, 37, 512
+    params = dict(osamp.default_params(), entropy_bound=bound, max_steps=8)
+    seed, ids = 5, [3, 4, 11]
+    st = osamp.new_state(osamp.init_canvas(seed, ids, C, V))
+    st["done"][1] = True                     # frozen canvas must never change
+    gs = _gpu_state_from_host(st, B, C, ids)
+    out = driver.StepOut(B, C, V, DEV, with_logits=False)
+    p = driver.eb_params_from_dict(params, seed)
+    for s in range(8):
+        z = _small_case(B, C, V, 100 + s, 2.0 + 3.0 * s)
+        driver.eb_sample(synth.to_device_bf16(z, DEV), s, p, gs, out)
+        torch.cuda.synchronize()
+        nxt = compare_step(z.astype(np.float64), s, params, seed, ids, st, gs, out,
+                           f"bound={bound} s={s}")
+        if nxt is None:
+            break
+        st = nxt
+    h = gs.host()
+    assert h["done"].all()
+
+
+def test_adaptive_stop_and_determinism():
+    B, C, V = 2, 64, 1024
+    params = dict(osamp.default_params(), entropy_bound=0.0, max_steps=48)
+    seed, ids = 2, [0, 1]
+    z = np.full((B, C, V), -30.0, dtype=np.float32)
+    idx = np.random.default_rng(3).integers(0, V, size=(B, C))
+    for b in range(B):
+        z[b, np.arange(C), idx[b]] = 20.0
+    z = synth.to_bf16_values(z)
+    outs = []
+    for _ in range(2):
+        st = osamp.new_state(osamp.init_canvas(seed, ids, C, V))
+        gs = _gpu_state_from_host(st, B, C)
+        out = driver.StepOut(B, C, V, DEV, with_logits=False)
+        p = driver.eb_params_from_dict(params, seed)
+        zt = synth.to_device_bf16(z, DEV)
+        for s in range(3):
+            driver.eb_sample(zt, s, p, gs, out)
+            torch.cuda.synchronize()
+            nxt = compare_step(z.astype(np.float64), s, params, seed, ids, st, gs, out, f"s={s}")
+            assert nxt is not None
+            st = nxt
+        h = gs.host()
+        assert h["done"].all() and np.array_equal(h["canvas"], idx)
+        outs.append((h["canvas"].copy(), out.entropy.cpu().numpy().copy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])      # bitwise-identical entropies
+
+
+def test_nonfinite_logits_freeze_canvas_and_set_status():
+    B, C, V = 2, 16, 512
+    z = _small_case(B, C, V, 7, 1.0)
+    z[1, 3, 100] = np.nan
+    st = osamp.new_state(osamp.init_canvas(2, [0, 1], C, V))
+    gs = _gpu_state_from_host(st, B, C)
+    out = driver.StepOut(B, C, V, DEV, with_logits=False)
+    driver.eb_sample(synth.to_device_bf16(z, DEV), 0, driver.eb_params(), gs, out)
+    torch.cuda.synchronize()
+    h = gs.host()
+    assert int(gs.dev_status[0]) == 9          # DG_ERR_NONFINITE
+    assert h["done"][1] and np.array_equal(h["canvas"][1], st["canvas"][1])
+    assert not h["done"][0]
