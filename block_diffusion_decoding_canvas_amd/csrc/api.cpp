@@ -248,8 +248,9 @@ dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void
     return fail(DG_ERR_SHAPE, "non-positive or too small dimension");
   if (d->d_model % 32 || d->ffn_inner % 32 || d->shared_inner % 32)
     return fail(DG_ERR_SHAPE, "d_model, ffn_inner and shared_inner must be multiples of 32");
-  if (d->head_dim % 16 || d->head_dim > 256)
-    return fail(DG_ERR_SHAPE, "head_dim must be a multiple of 16 and <= 256");
+  if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128 &&
+      d->head_dim != 256)
+    return fail(DG_ERR_SHAPE, "head_dim must be one of 16, 32, 64, 128, 256");
   if (d->n_q_heads % d->n_kv_heads) return fail(DG_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
   if (d->n_experts < 1 || d->n_experts > 256 || d->top_k < 1 || d->top_k > d->n_experts ||
       d->top_k > 16)
@@ -363,18 +364,290 @@ dg_status dg_prof_reset(void) {
 
 }  // extern "C"
 
-// ---- decoder entry points (filled in with the decoder kernels) ----------------------------
+// ---- decoder: workspace layout and kernel sequence ------------------------------------------
+
+namespace {
+
+constexpr int kRouterSplit = 8;   // k-splits of the router projection (summed by topk)
+constexpr int kOProjSplit = 4;    // k-splits of the attention output projection
+
+struct DecWs {
+  float* h;           // [T][d] residual stream (fp32)
+  uint16_t* u;        // [T][d] normed activations (bf16)
+  uint16_t* qkv;      // [T][(Hq + 2 Hkv) dh]
+  uint16_t* attn;     // [T][Hq dh]
+  float* o_part;      // attention split partials
+  float* ml_part;
+  int max_split;
+  float* proj_part;   // [kOProjSplit][T][d] output-projection partials
+  float* router_part; // [kRouterSplit][T][E]
+  int32_t* topk;      // [T][k]
+  float* gates;       // [T][k]
+  int32_t* perm;      // [T k + T]
+  int32_t* inv;       // [T k]
+  int32_t* chunks;    // [max_chunks][3]
+  int32_t* n_chunks;  // [1]
+  int max_chunks;
+  uint16_t* act;      // [T k + T][max(F, Fs)]
+  uint16_t* y;        // [T k + T][d]
+  EbWs eb;            // LM-head statistics partials and the sampler's scratch
+};
+
+int attn_base_blocks(const dg_dims& d, int B) {
+  const int R = (d.n_q_heads / d.n_kv_heads) * d.canvas_len;
+  return B * d.n_kv_heads * ((R + 63) / 64);
+}
+
+DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
+  DecWs w;
+  const size_t T = static_cast<size_t>(B) * d.canvas_len;
+  const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const int fmax = std::max(d.ffn_inner, d.shared_inner);
+  const size_t rows = T * d.top_k + T;
+  w.h = c.take<float>(T * d.d_model);
+  w.u = c.take<uint16_t>(T * d.d_model);
+  w.qkv = c.take<uint16_t>(T * dq);
+  w.attn = c.take<uint16_t>(T * d.n_q_heads * d.head_dim);
+  w.max_split = std::max(1, 1024 / attn_base_blocks(d, B));
+  const size_t prow = static_cast<size_t>(B) * d.n_q_heads * d.canvas_len;
+  w.o_part = c.take<float>(static_cast<size_t>(w.max_split) * prow * d.head_dim);
+  w.ml_part = c.take<float>(static_cast<size_t>(w.max_split) * prow * 2);
+  w.proj_part = c.take<float>(static_cast<size_t>(kOProjSplit) * T * d.d_model);
+  w.router_part = c.take<float>(static_cast<size_t>(kRouterSplit) * T * d.n_experts);
+  w.topk = c.take<int32_t>(T * d.top_k);
+  w.gates = c.take<float>(T * d.top_k);
+  w.perm = c.take<int32_t>(rows);
+  w.inv = c.take<int32_t>(T * d.top_k);
+  const int tr = dg::gemm_moe_tile_rows();
+  w.max_chunks = d.n_experts + static_cast<int>((T * d.top_k + tr - 1) / tr) +
+                 static_cast<int>((T + tr - 1) / tr);
+  w.chunks = c.take<int32_t>(static_cast<size_t>(w.max_chunks) * 3);
+  w.n_chunks = c.take<int32_t>(1);
+  w.act = c.take<uint16_t>(rows * fmax);
+  w.y = c.take<uint16_t>(rows * d.d_model);
+  w.eb = carve_eb(c, static_cast<int>(T), d.vocab / dg::gemm_lmhead_rows_per_block(), d.vocab);
+  return w;
+}
+
+bool layer_global(const dg_dims& d, int l) {
+  return d.window == 0 || (l + 1) % d.global_every == 0;
+}
+
+size_t kv_layer_elems(const dg_dims& d, const dg_kv* kv) {
+  return static_cast<size_t>(kv->batch) * d.n_kv_heads * kv->cap * d.head_dim;
+}
+
+dg_status check_kv(const dg_model* m, const dg_kv* kv, bool need_room) {
+  if (!kv || !kv->k || !kv->v || !kv->len) return fail(DG_ERR_NULL, "kv or a kv pointer is NULL");
+  if (kv->batch < 1 || kv->batch > 64) return fail(DG_ERR_SHAPE, "kv batch must be in [1, 64]");
+  if (kv->cap < 1) return fail(DG_ERR_SHAPE, "kv capacity must be >= 1");
+  for (int b = 0; b < kv->batch; ++b) {
+    if (kv->len[b] < 0 || kv->len[b] > kv->cap)
+      return fail(DG_ERR_CAPACITY, "kv len[%d] = %d outside [0, cap = %d]", b, kv->len[b], kv->cap);
+    if (need_room && kv->len[b] + m->dims.canvas_len > kv->cap)
+      return fail(DG_ERR_CAPACITY, "kv len[%d] + canvas_len = %d exceeds cap %d", b,
+                  kv->len[b] + m->dims.canvas_len, kv->cap);
+  }
+  return DG_OK;
+}
+
+// One transformer layer on ws.h (the attention norm of this layer must already be in ws.u).
+// causal: encoder pass (causal canvas, writes K/V into the cache); next_gain: the norm of the
+// following consumer applied to the new h (NULL: none).  Optional router traces.
+dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecWs& w,
+                    const uint16_t* next_gain, bool skip_ffn, float* trace_logits,
+                    int32_t* trace_idx, float* trace_gates, hipStream_t s) {
+  const dg_dims& d = m->dims;
+  const dg_layer_w& lw = m->layers[l];
+  const int B = kv->batch, C = d.canvas_len, T = B * C;
+  const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const size_t kvl = kv_layer_elems(d, kv);
+  uint16_t* kc = static_cast<uint16_t*>(kv->k) + kvl * l;
+  uint16_t* vc = static_cast<uint16_t*>(kv->v) + kvl * l;
+
+  dg::WGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  // QKV projection
+  g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_qkv);
+  g.K = g.K_sh = d.d_model; g.N = g.N_sh = dq; g.ntok = T; g.out = w.qkv; g.ldo = dq; g.ksplit = 1;
+  DG_LAUNCH(PC_GEMM_QKV, s, dg::launch_gemm_dense_bf16(g, s));
+
+  // attention over [visible cache ; canvas]
+  dg::AttnArgs at;
+  memset(&at, 0, sizeof(at));
+  at.qkv = w.qkv; at.kc = kc; at.vc = vc; at.cap = kv->cap;
+  at.B = B; at.C = C; at.Hq = d.n_q_heads; at.Hkv = d.n_kv_heads; at.dh = d.head_dim;
+  at.window = layer_global(d, l) ? 0 : d.window;
+  at.causal = causal ? 1 : 0;
+  int max_keys = 0;
+  for (int b = 0; b < B; ++b) {
+    at.len[b] = kv->len[b];
+    const int lo = at.window > 0 ? std::max(0, kv->len[b] - at.window + 1) : 0;
+    max_keys = std::max(max_keys, kv->len[b] - lo + C);
+  }
+  at.scale_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.head_dim)));
+  at.n_split = std::min(w.max_split,
+                        dg::attention_pick_split(B, C, d.n_q_heads, d.n_kv_heads, max_keys));
+  at.o_part = w.o_part; at.ml_part = w.ml_part; at.out = w.attn;
+  DG_LAUNCH(PC_ATTENTION, s, dg::launch_attention(at, s));
+  if (causal) {
+    DG_LAUNCH(PC_KV_WRITE, s, dg::launch_kv_write(w.qkv, kc, vc, B, C, d.n_q_heads, d.n_kv_heads,
+                                                  d.head_dim, kv->cap, kv->len, s));
+  }
+  if (skip_ffn) return DG_OK;
+
+  // output projection (k-split partials) + residual + pre-FFN norm
+  memset(&g, 0, sizeof(g));
+  g.X = w.attn; g.ldx = d.n_q_heads * d.head_dim; g.W = static_cast<const uint16_t*>(lw.w_o);
+  g.K = g.K_sh = d.n_q_heads * d.head_dim; g.N = g.N_sh = d.d_model; g.ntok = T;
+  g.out = w.proj_part; g.ldo = d.d_model; g.ksplit = kOProjSplit;
+  g.split_stride = static_cast<long long>(T) * d.d_model;
+  DG_LAUNCH(PC_GEMM_O, s, dg::launch_gemm_dense_f32(g, s));
+  DG_LAUNCH(PC_RMSNORM, s, dg::launch_resid_norm(w.h, w.proj_part, kOProjSplit, T, d.d_model,
+                                                 static_cast<const uint16_t*>(lw.ffn_norm), w.u,
+                                                 d.norm_eps, s));
+  // router
+  memset(&g, 0, sizeof(g));
+  g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_router);
+  g.K = g.K_sh = d.d_model; g.N = g.N_sh = d.n_experts; g.ntok = T;
+  g.out = w.router_part; g.ldo = d.n_experts; g.ksplit = kRouterSplit;
+  g.split_stride = static_cast<long long>(T) * d.n_experts;
+  DG_LAUNCH(PC_GEMM_ROUTER, s, dg::launch_gemm_dense_f32(g, s));
+  int32_t* idx = trace_idx ? trace_idx : w.topk;
+  float* gates = trace_gates ? trace_gates : w.gates;
+  DG_LAUNCH(PC_TOPK, s, dg::launch_topk(w.router_part, kRouterSplit, T, d.n_experts, d.top_k, idx,
+                                        gates, trace_logits, s));
+  DG_LAUNCH(PC_PERMUTE, s, dg::launch_permute(idx, T, d.top_k, d.n_experts,
+                                              dg::gemm_moe_tile_rows(), w.perm, w.inv, w.chunks,
+                                              w.n_chunks, w.max_chunks, s));
+  // routed + shared experts: gate/up with SwiGLU, then down
+  const int fmax = std::max(d.ffn_inner, d.shared_inner);
+  memset(&g, 0, sizeof(g));
+  g.X = w.u; g.ldx = d.d_model; g.x_rows = w.perm;
+  g.W = static_cast<const uint16_t*>(lw.w_gate_up);
+  g.w_estride = 2LL * d.ffn_inner * d.d_model;
+  g.W_sh = static_cast<const uint16_t*>(lw.ws_gate_up);
+  g.K = g.K_sh = d.d_model; g.N = d.ffn_inner; g.N_sh = d.shared_inner;
+  g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
+  g.grid_tiles = w.max_chunks; g.out = w.act; g.ldo = fmax; g.ksplit = 1;
+  DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_gemm_moe_gateup(g, s));
+  memset(&g, 0, sizeof(g));
+  g.X = w.act; g.ldx = fmax; g.W = static_cast<const uint16_t*>(lw.w_down);
+  g.w_estride = static_cast<long long>(d.d_model) * d.ffn_inner;
+  g.W_sh = static_cast<const uint16_t*>(lw.ws_down);
+  g.K = d.ffn_inner; g.K_sh = d.shared_inner; g.N = g.N_sh = d.d_model;
+  g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
+  g.grid_tiles = w.max_chunks; g.out = w.y; g.ldo = d.d_model; g.ksplit = 1;
+  DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_gemm_moe_down(g, s));
+  DG_LAUNCH(PC_COMBINE, s, dg::launch_combine(w.h, w.y, w.inv, gates, T, d.top_k, d.d_model,
+                                              next_gain, w.u, d.norm_eps, s));
+  return DG_OK;
+}
+
+dg_status check_model(const dg_model* m) {
+  if (!m) return fail(DG_ERR_NULL, "model is NULL");
+  return DG_OK;
+}
+
+}  // namespace
+
 extern "C" {
-size_t dg_workspace_bytes(const dg_model* m, int32_t batch) { (void)m; (void)batch; return 0; }
-dg_status dg_decoder_step(const dg_model*, const dg_kv*, int32_t, const dg_eb_params*,
-                          dg_eb_state*, dg_step_out*, void*, size_t, void*) {
-  return fail(DG_ERR_UNSUPPORTED, "dg_decoder_step not built yet");
+
+size_t dg_workspace_bytes(const dg_model* m, int32_t batch) {
+  if (!m || batch < 1 || batch > 64) return 0;
+  Carver c(nullptr);
+  carve_dec(c, m->dims, batch);
+  return c.off + 256;
 }
-dg_status dg_kv_append_canvas(const dg_model*, dg_kv*, const int32_t*, void*, size_t, void*) {
-  return fail(DG_ERR_UNSUPPORTED, "dg_kv_append_canvas not built yet");
+
+dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, const dg_eb_params* p,
+                          dg_eb_state* st, dg_step_out* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, false)) != DG_OK) return s;
+  if ((s = check_params(p, step)) != DG_OK) return s;
+  if ((s = check_state(st)) != DG_OK) return s;
+  if ((s = check_out(out, true)) != DG_OK) return s;
+  if (!ws) return fail(DG_ERR_NULL, "workspace is NULL");
+  const size_t need = dg_workspace_bytes(m, kv->batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const dg_dims& d = m->dims;
+  const int B = kv->batch, C = d.canvas_len, T = B * C;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, B);
+
+  DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(st->canvas, m->embed, w.h, T, d.d_model, d.vocab, hs));
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
+                                               w.u, T, d.d_model, d.norm_eps, hs));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const uint16_t* next = (l + 1 < d.n_layers)
+                               ? static_cast<const uint16_t*>(m->layers[l + 1].attn_norm)
+                               : m->final_norm;
+    if ((s = run_layer(m, kv, l, false, w, next, false, nullptr, nullptr, nullptr, hs)) != DG_OK)
+      return s;
+  }
+  // LM head with the tempered statistics, then the sampler
+  dg::EbArgs a = eb_args(p, B, C, d.vocab, step, st, out, out->logits, w.eb);
+  dg::WGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.X = w.u; g.ldx = d.d_model; g.W = m->w_lm; g.K = g.K_sh = d.d_model;
+  g.N = g.N_sh = d.vocab; g.ntok = T; g.out = out->logits; g.ldo = d.vocab; g.ksplit = 1;
+  g.inv_t_log2e = a.inv_t_log2e; g.part = w.eb.part;
+  DG_LAUNCH(PC_LMHEAD, hs, dg::launch_gemm_lmhead(g, hs));
+  return run_sampler_tail(a, hs);
 }
-dg_status dg_layer_forward(const dg_model*, const dg_kv*, int32_t, int32_t, float*, float*,
-                           int32_t*, float*, void*, size_t, void*) {
-  return fail(DG_ERR_UNSUPPORTED, "dg_layer_forward not built yet");
+
+dg_status dg_kv_append_canvas(const dg_model* m, dg_kv* kv, const int32_t* tokens, void* ws,
+                              size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, true)) != DG_OK) return s;
+  if (!tokens || !ws) return fail(DG_ERR_NULL, "tokens or workspace is NULL");
+  const size_t need = dg_workspace_bytes(m, kv->batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const dg_dims& d = m->dims;
+  const int B = kv->batch, C = d.canvas_len, T = B * C;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, B);
+  DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(tokens, m->embed, w.h, T, d.d_model, d.vocab, hs));
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
+                                               w.u, T, d.d_model, d.norm_eps, hs));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const bool last = l + 1 == d.n_layers;  // its keys/values are all the last layer adds
+    const uint16_t* next = last ? nullptr : static_cast<const uint16_t*>(m->layers[l + 1].attn_norm);
+    if ((s = run_layer(m, kv, l, true, w, next, last, nullptr, nullptr, nullptr, hs)) != DG_OK)
+      return s;
+  }
+  for (int b = 0; b < B; ++b) kv->len[b] += C;
+  return DG_OK;
 }
+
+dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, int32_t causal,
+                           float* h, float* router_logits, int32_t* topk_idx, float* gates,
+                           void* ws, size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, causal != 0)) != DG_OK) return s;
+  if (!h || !ws) return fail(DG_ERR_NULL, "h or workspace is NULL");
+  if (layer < 0 || layer >= m->dims.n_layers) return fail(DG_ERR_SHAPE, "layer out of range");
+  const size_t need = dg_workspace_bytes(m, kv->batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const dg_dims& d = m->dims;
+  const int T = kv->batch * d.canvas_len;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, kv->batch);
+  DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].attn_norm),
+                                               w.u, T, d.d_model, d.norm_eps, hs));
+  if ((s = run_layer(m, kv, layer, causal != 0, w, nullptr, false, router_logits, topk_idx, gates,
+                     hs)) != DG_OK)
+    return s;
+  DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  return DG_OK;
 }
+
+}  // extern "C"

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "dg.h"
 
 namespace dg {
@@ -13,6 +15,8 @@ namespace dg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// native 16-byte vector (register-friendly; HIP's uint4 struct can force private-memory copies)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -30,10 +34,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
 }
 
-__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -134,9 +141,13 @@ struct WGemmArgs {
   long long w_estride;    // elements between experts
   const uint16_t* W_sh;   // shared expert weights (expert id == n_experts)
   int K;
+  int K_sh;               // shared expert's K
   int N;                  // output features (paired: F, the gate/up split)
   int N_sh;               // shared expert's N
   int n_experts;
+  int ksplit;             // dense fp32 epilogue: k splits (partials summed by the consumer)
+  int k_per_split;        // set by the launcher
+  long long split_stride; // elements between split partial planes
   const int32_t* chunks;  // grouped tiles: [slot] = (expert, row0, nrows); NULL = dense
   const int32_t* n_chunks;
   int ntok;               // dense: rows
@@ -144,24 +155,20 @@ struct WGemmArgs {
   int grid_tiles;         // tile slots
   void* out;
   int ldo;
-  float* resid;           // residual (fp32) for the add epilogue
   // LM-head statistics epilogue
   float inv_t_log2e;      // log2(e) / T as fp32
   SoftStats* part;        // [rows][n_nblk]
 };
 
-enum Epi { EPI_BF16 = 0, EPI_ADD_F32 = 1, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
+enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 
 // launchers; each returns the hip error of the launch
 hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out bf16 [rows][N]
-hipError_t launch_gemm_dense_add(const WGemmArgs& a, hipStream_t s);      // resid += X W^T
-hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // out fp32
+hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // fp32 split partials
 hipError_t launch_gemm_moe_gateup(const WGemmArgs& a, hipStream_t s);     // SwiGLU act
 hipError_t launch_gemm_moe_down(const WGemmArgs& a, hipStream_t s);       // Y rows bf16
 hipError_t launch_gemm_lmhead(const WGemmArgs& a, hipStream_t s);         // logits + stats
 int gemm_lmhead_rows_per_block();
-int gemm_moe_gateup_cols_per_block();
-int gemm_moe_down_rows_per_block();
 int gemm_moe_tile_rows();
 
 struct AttnArgs {
@@ -184,11 +191,13 @@ int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys);
 
 // per-token kernels
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, int ntok, int d,
-                        hipStream_t s);
+                        int vocab, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u, int ntok, int d,
                           float eps, hipStream_t s);
-hipError_t launch_topk(const float* logits, int ntok, int n_exp, int top_k, int32_t* idx,
-                       float* gates, hipStream_t s);
+hipError_t launch_topk(const float* logits, int ksplit, int ntok, int n_exp, int top_k,
+                       int32_t* idx, float* gates, float* logits_out, hipStream_t s);
+hipError_t launch_resid_norm(float* h, const float* part, int ksplit, int ntok, int d,
+                             const uint16_t* gain, uint16_t* u, float eps, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int ntok, int top_k, int n_exp, int tile_rows,
                           int32_t* perm, int32_t* inv, int32_t* chunks, int32_t* n_chunks,
                           int max_chunks, hipStream_t s);

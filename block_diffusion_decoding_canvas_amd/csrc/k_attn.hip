@@ -1,0 +1,286 @@
+// Canvas attention: every canvas query attends, in one softmax, to the visible cached keys and
+// to the canvas keys (DiffusionGemma model card, "Model overview": bidirectional attention over
+// the canvas plus cross-attention to the cached context; the encoder reads a finished canvas
+// causally).  GQA: query head h reads KV head floor(h * Hkv / Hq); scale 1/sqrt(head_dim).
+// Sliding-window layers: canvas query i at absolute position len + i sees cache position j
+// only if (len + i) - j < window (model card dimension table: 1,024-token window).
+//
+// Layout of the work: one workgroup = (canvas b, KV head g, 64 query rows, one split of the
+// key range).  The query rows of a KV head are its Hq/Hkv query heads times the canvas
+// positions, so the K/V tiles staged in LDS serve every query head that reads them.  Keys are
+// processed in tiles of 64 (K tile [key][dh] and V tile transposed [dh][key] in LDS).  Each wave
+// holds 16 query rows and computes S^T = K Q^T, so the probabilities come out of the MFMA in the
+// lane layout that the P V product takes as its B operand (O^T = V^T P^T) with no shuffle.
+// Splits of the key range write unnormalised partial outputs with their running max and sum,
+// merged afterwards by log-sum-exp.
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+constexpr int KT = 64;        // keys per tile
+constexpr int QB = 64;        // query rows per workgroup (4 waves x 16)
+
+template <int DH>
+struct AttnCfg {
+  static constexpr int KS_STRIDE = DH + 8;   // bf16 per K row in LDS
+  static constexpr int VT_STRIDE = KT + 8;   // bf16 per transposed V row in LDS
+  static constexpr int NKS = (DH + 31) / 32; // 32-wide dh steps of QK^T
+  static constexpr int NDT = DH / 16;        // 16-row dh tiles of O^T
+  static constexpr int LDS_BYTES = (KT * KS_STRIDE + DH * VT_STRIDE) * 2;
+};
+
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  using C = AttnCfg<DH>;
+  __shared__ __align__(16) uint16_t ks[KT * C::KS_STRIDE];
+  __shared__ __align__(16) uint16_t vt[DH * C::VT_STRIDE];
+
+  const int qblk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z / a.n_split;
+  const int split = blockIdx.z % a.n_split;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int hpg = a.Hq / a.Hkv;
+  const int R = hpg * a.C;
+  const int ldqkv = (a.Hq + 2 * a.Hkv) * DH;
+
+  const int len = a.len[b];
+  const int c_lo = a.window > 0 ? max(0, len - a.window + 1) : 0;
+  const int nc = len - c_lo;           // cache keys in the union of the visible ranges
+  const int nk = nc + a.C;             // + canvas keys
+  const int ntiles = (nk + KT - 1) / KT;
+  const int per = (ntiles + a.n_split - 1) / a.n_split;
+  const int t_beg = split * per;
+  const int t_end = min(ntiles, t_beg + per);
+
+  // this lane's query row (B operand column)
+  const int r = qblk * QB + wave * 16 + r16;
+  const bool r_ok = r < R;
+  const int rr = r_ok ? r : R - 1;
+  const int hl = rr / a.C, qi = rr % a.C;
+  const int h = g * hpg + hl;
+  const long long qrow = static_cast<long long>(b) * a.C + qi;
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 qf[C::NKS];
+  {
+    const uint16_t* qp = a.qkv + qrow * ldqkv + h * DH;
+#pragma unroll
+    for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
+      const int d0 = ks_ * 32 + lg * 8;
+      qf[ks_] = (d0 < DH) ? ld16(qp + d0) : zero4;
+    }
+  }
+
+  f32x4 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const uint16_t* kcache = a.kc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
+  const uint16_t* vcache = a.vc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
+  const uint16_t* kcanvas = a.qkv + static_cast<long long>(b) * a.C * ldqkv + (a.Hq + g) * DH;
+  const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
+  const int win_lo = len + qi - a.window + 1;  // first visible cache position (windowed layers)
+
+  for (int tt = t_beg; tt < t_end; ++tt) {
+    const int kbase = tt * KT;
+    __syncthreads();  // previous tile fully consumed
+    // stage K [key][dh] and V^T [dh][key]
+    for (int idx = tid; idx < KT * (DH / 8); idx += 256) {
+      const int key = idx % KT, c = idx / KT;
+      const int kk = kbase + key;
+      u32x4 kv = zero4, vv = zero4;
+      if (kk < nk) {
+        if (kk < nc) {
+          const long long off = static_cast<long long>(c_lo + kk) * DH + c * 8;
+          kv = ld16(kcache + off);
+          vv = ld16(vcache + off);
+        } else {
+          const long long off = static_cast<long long>(kk - nc) * ldqkv + c * 8;
+          kv = ld16(kcanvas + off);
+          vv = ld16(vcanvas + off);
+        }
+      }
+      st16(ks + key * C::KS_STRIDE + c * 8, kv);
+      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(c * 8 + 2 * e) * C::VT_STRIDE + key] = static_cast<uint16_t>(w[e] & 0xffffu);
+        vt[(c * 8 + 2 * e + 1) * C::VT_STRIDE + key] = static_cast<uint16_t>(w[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T[key][q] for 4 sub-tiles of 16 keys
+    f32x4 s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
+        const int d0 = ks_ * 32 + lg * 8;
+        const u32x4 kf = (d0 < DH) ? ld16(ks + (nt * 16 + r16) * C::KS_STRIDE + d0) : zero4;
+        s[nt] = mfma16x16x32(kf, qf[ks_], s[nt]);
+      }
+    }
+    // scale, mask, running max (lane's query = r16; its keys: nt*16 + 4 lg + j)
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = kbase + nt * 16 + 4 * lg + j;
+        bool vis = kk < nk;
+        if (kk < nc) {
+          if (a.window > 0) vis = vis && (c_lo + kk >= win_lo);
+        } else if (a.causal) {
+          vis = vis && (kk - nc <= qi);
+        }
+        const float v = vis ? s[nt][j] * a.scale_log2e : -INFINITY;
+        s[nt][j] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+    u32x4 pb[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = (m_new == -INFINITY) ? 0.f : exp2f(s[2 * kp][j] - m_new);
+        p[4 + j] = (m_new == -INFINITY) ? 0.f : exp2f(s[2 * kp + 1][j] - m_new);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l_run += p[j];
+      pb[kp] = u32x4{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
+                     pack_bf2(p[6], p[7])};
+    }
+    // O^T[dh][q] += V^T[dh][keys] P^T[keys][q]; the B operand's 8 keys per lane are
+    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}; the A operand reads the same keys
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const uint16_t* vrow = vt + (dt * 16 + r16) * C::VT_STRIDE + kp * 32 + 4 * lg;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        o[dt] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[kp], o[dt]);
+      }
+    }
+  }
+
+  // row sum over the 4 lanes that share this query
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!r_ok) return;
+  if (a.n_split == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = a.out + qrow * (a.Hq * DH) + h * DH;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      uint2 pk;
+      pk.x = pack_bf2(o[dt][0] * inv, o[dt][1] * inv);
+      pk.y = pack_bf2(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(op + dt * 16 + 4 * lg) = pk;
+    }
+  } else {
+    const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + r;
+    float* op = a.o_part + prow * DH;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+      *reinterpret_cast<float4*>(op + dt * 16 + 4 * lg) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (lg == 0) {
+      a.ml_part[prow * 2] = m_run;
+      a.ml_part[prow * 2 + 1] = l_run;
+    }
+  }
+}
+
+// merge of split partials: one thread per (query row, 4 dh values)
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int hpg = a.Hq / a.Hkv;
+  const int R = hpg * a.C;
+  const long long rows = static_cast<long long>(a.B) * a.Hkv * R;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = DH / 4;
+  if (idx >= rows * per_row) return;
+  const long long row = idx / per_row;  // (b, g, r)
+  const int c4 = static_cast<int>(idx % per_row) * 4;
+  const long long stride = rows;        // rows per split
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < a.n_split; ++sp) mmax = fmaxf(mmax, a.ml_part[(sp * stride + row) * 2]);
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float m = a.ml_part[(sp * stride + row) * 2];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mmax);
+    l += w * a.ml_part[(sp * stride + row) * 2 + 1];
+    const float4 v = *reinterpret_cast<const float4*>(a.o_part + (sp * stride + row) * DH + c4);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int r = static_cast<int>(row % R);
+  const long long bg = row / R;
+  const int g = static_cast<int>(bg % a.Hkv), b = static_cast<int>(bg / a.Hkv);
+  const int hl = r / a.C, qi = r % a.C;
+  const int h = g * hpg + hl;
+  uint16_t* op = a.out + (static_cast<long long>(b) * a.C + qi) * (a.Hq * DH) + h * DH + c4;
+  uint2 pk;
+  pk.x = pack_bf2(acc.x * inv, acc.y * inv);
+  pk.y = pack_bf2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(op) = pk;
+}
+
+template <int DH>
+hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
+  const int R = (a.Hq / a.Hkv) * a.C;
+  dim3 grid((R + QB - 1) / QB, a.Hkv, a.B * a.n_split);
+  hipLaunchKernelGGL(k_attn<DH>, grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const long long n = static_cast<long long>(a.B) * a.Hkv * R * (DH / 4);
+  hipLaunchKernelGGL(k_attn_merge<DH>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys) {
+  const int R = (Hq / Hkv) * C;
+  const int base = B * Hkv * ((R + QB - 1) / QB);
+  const int ntiles = (max_keys + KT - 1) / KT;
+  int n = (512 + base - 1) / base;
+  n = std::min(n, std::max(1, ntiles / 2));
+  n = std::min(n, std::max(1, 1024 / base));
+  return std::max(1, n);
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  switch (a.dh) {
+    case 16: return launch_dh<16>(a, s);
+    case 32: return launch_dh<32>(a, s);
+    case 64: return launch_dh<64>(a, s);
+    case 128: return launch_dh<128>(a, s);
+    case 256: return launch_dh<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dg

@@ -207,4 +207,4 @@ def eb_step(z, step, params, state, seed, canvas_ids):
         if state["committed"][b].all():
             state["done"][b] = True
     return dict(entropy=ent, argmax=amax, commit_now=commit_now, finalised=finalised,
-                selected=selected, sums=sums_all, inv_t=inv_t)
+                selected=selected, sums=sums_all, inv_t=inv_t, step=step)
