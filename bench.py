@@ -1,0 +1,206 @@
+"""Benchmark of the canvas denoising hot path on one MI355X.
+
+Workload (one bench "step" = one pass of the whole path): the full-width synthetic decoder
+(30 layers, d_model 2816, 16/8 heads of 256, 128 experts top-8 + 1 shared with inner width 704,
+262,144-entry vocabulary, about 25B parameters, bf16, random N(0, 0.02^2) weights) with a
+256-token canvas against an 8,192-token N(0,1) cached prompt: canvas 1 runs up to 48
+entropy-bound steps with adaptive stop, is encoded and appended to the cache, then canvas 2 runs
+the same on the 8,448-token cache and is appended.  Inputs are resident in HBM before timing.
+
+Reported: denoising steps/s (value), tokens/s, the HBM roofline fraction of the MoE gate/up
+kernel (the dominant kernel) from HIP events recorded around its launches in the timed region,
+and the plain CPU oracle timed on a bounded sample of the same step on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "canvas denoise steps/s + tokens/s (256-tok canvas, 1 GPU), % of roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--cache", type=int, default=8192)
+    ap.add_argument("--canvases", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=1)
+    return ap.parse_args()
+
+
+def moe_gateup_bytes(dims, n_touched):
+    """Algorithmic HBM bytes of one gate/up launch: each touched expert's [2F, d] weights and
+    the shared expert's once, the token rows once, the SwiGLU activations written once."""
+    d, f, fs, k, t = dims["d"], dims["F"], dims["Fs"], dims["top_k"], dims["C"]
+    weights = (n_touched * 2 * f * d + 2 * fs * d) * 2
+    acts = t * d * 2 + (t * k * f + t * fs) * 2
+    return weights + acts
+
+
+def cpu_baseline(dims, n_layers_sample, cache_len):
+    """The oracle (fp64 numpy) on a bounded sample of one decoder step: `n_layers_sample`
+    full-width layers over the 256-token canvas with the N(0,1) cache, the LM head and the EB
+    sampler; the per-step time is scaled to the full depth."""
+    import numpy as np
+    from block_diffusion_decoding_canvas_amd import synth
+    from oracle import model as om
+    from oracle import sampler as osamp
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    C, d = dims["C"], dims["d"]
+    h = synth.hidden_states(C, d, seed=1).astype(np.float64)[None]
+    t_layers = 0.0
+    for _ in range(n_layers_sample):
+        lw = {k: v.astype(np.float64) for k, v in synth.make_layer(dims, rng).items()}
+        cache = synth.make_cache(dict(dims, n_layers=1), 1, cache_len, cache_len, seed=1)
+        kc = cache["k"][0].astype(np.float64)
+        vc = cache["v"][0].astype(np.float64)
+        t0 = time.perf_counter()
+        h, _, _, _ = om.layer_forward(h, lw, dims, 0, kc, vc, cache["len"], causal=False)
+        t_layers += time.perf_counter() - t0
+        log(f"oracle layer: {t_layers:.1f} s")
+        del lw, kc, vc
+    w_lm = synth.to_bf16_values(rng.standard_normal((dims["V"], d), dtype=np.float32) * 0.02)
+    w_lm = w_lm.astype(np.float64)
+    fn = np.ones(d)
+    t0 = time.perf_counter()
+    z = om.rms_norm(h, fn, dims["eps"]) @ w_lm.T
+    from oracle.numerics import round_bf16
+    zr = round_bf16(z)
+    t_lm = time.perf_counter() - t0
+    del w_lm, z
+    st = osamp.new_state(osamp.init_canvas(2, [0], C, dims["V"]))
+    t0 = time.perf_counter()
+    osamp.eb_step(zr, 0, osamp.default_params(), st, 2, [0])
+    t_samp = time.perf_counter() - t0
+    per_step = t_layers / n_layers_sample * dims["n_layers"] + t_lm + t_samp
+    return dict(value=1.0 / per_step, unit="steps/s", cores=cores, kind="oracle",
+                sample=(f"{n_layers_sample} full-width layer(s) ({t_layers:.1f} s) + LM head "
+                        f"({t_lm:.1f} s) + EB sampler ({t_samp:.1f} s) of one 256-token step on "
+                        f"a {cache_len}-token cache, fp64 numpy; per-step time = layers scaled "
+                        f"to {dims['n_layers']} + LM head + sampler"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
+              f"across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_diffusion_decoding_canvas_amd import driver, synth
+
+    dev = "cuda"
+    dims = synth.dims_full(n_layers=args.layers)
+    C, B = dims["C"], 1
+    cap = args.cache + C * args.canvases
+    weights = synth.make_model_device(dims, dev, seed=0)
+    kc, vc = synth.make_cache_device(dims, B, cap, args.cache, dev, seed=1)
+    model = driver.Model(weights)
+    kv = driver.KVCache(dims, B, cap, dev, kc, vc, [args.cache])
+    ws = driver.workspace(model.workspace_bytes(B), dev)
+    params = driver.eb_params()        # the model card's sampler constants, adaptive stop on
+    state = driver.SamplerState(B, C, dev)
+    out = driver.StepOut(B, C, dims["V"], dev)
+    timer = driver.KernelTimer()
+    torch.cuda.synchronize()
+
+    def one_pass():
+        """Generate `canvases` canvases back to back; returns decoder steps run."""
+        kv.len[0] = args.cache
+        steps = 0
+        for _ in range(args.canvases):
+            driver.canvas_init(params, state, dims["V"])
+            for s in range(params.max_steps):
+                driver.decoder_step(model, kv, s, params, state, out, ws)
+                steps += 1
+                if bool(state.done.all()):
+                    break
+            driver.kv_append_canvas(model, kv, state.canvas, ws)
+        return steps
+
+    log("model and cache resident; warming up")
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    log("warmup done; timing")
+    timer.reset()
+    timer.enable(["moe_gateup"])      # events only around the dominant kernel while timing
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_steps = 0
+    for i in range(args.steps):
+        total_steps += one_pass()
+        log(f"timed pass {i + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timer.enable([])
+    ms_gu, n_gu = timer.read("moe_gateup")
+    # per-kernel breakdown from one more (untimed) pass with every class timed
+    timer.reset()
+    timer.enable()
+    one_pass()
+    torch.cuda.synchronize()
+    timer.enable([])
+    per_class = {n: timer.read(n) for n in timer.names}
+
+    # experts touched in a layer: count distinct routed experts on layer 0's router
+    h0 = torch.zeros((B * C, dims["d"]), dtype=torch.float32, device=dev)
+    h0.copy_(torch.index_select(weights["embed"], 0, state.canvas.view(-1).long()).float())
+    ti = torch.zeros((B * C, dims["top_k"]), dtype=torch.int32, device=dev)
+    kv.len[0] = args.cache
+    driver.layer_forward(model, kv, 0, 0, h0, ws, None, ti, None)
+    torch.cuda.synchronize()
+    n_touched = int(torch.unique(ti).numel())
+
+    avg_gu = ms_gu / max(n_gu, 1) * 1e-3
+    bytes_gu = moe_gateup_bytes(dims, n_touched)
+    achieved = bytes_gu / avg_gu / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="moe_gateup", bytes_per_launch=bytes_gu,
+                    avg_launch_us=round(avg_gu * 1e6, 2), launches=n_gu,
+                    experts_touched=n_touched)
+    kernel_ms = {n: round(v[0], 3) for n, v in per_class.items() if v[1]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(dims, args.cpu_layers, args.cache)
+
+    steps_per_s = total_steps / elapsed
+    tokens = B * C * args.canvases * args.steps
+    line = dict(
+        metric=METRIC, value=round(steps_per_s, 3), unit="steps/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(elapsed / args.steps * 1e3, 2),
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic: random-init N(0,0.02^2) weights, N(0,1) bf16 KV cache, Philox canvases",
+        config=dict(workload=(f"{args.layers}-layer full-width decoder, 128 experts top-8 + "
+                              f"shared, V 262144, B {B} x 256-token canvas, {args.cache}-token "
+                              f"cache, {args.canvases} canvases (48 EB steps max each, adaptive "
+                              f"stop) + append per step"),
+                    layers=args.layers, canvas=C, batch=B, cache=args.cache,
+                    canvases_per_step=args.canvases, decoder_steps=total_steps),
+        tokens_per_s=round(tokens / elapsed, 2),
+        decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
+        roofline=roofline, cpu_baseline=cpu, kernel_ms_per_bench_step=kernel_ms)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

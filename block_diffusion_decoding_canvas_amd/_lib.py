@@ -70,9 +70,10 @@ _SIGS = {
     "dg_layer_forward": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_copy_bytes": (i32, [c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_pack_weight": (i32, [c_void_p, c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p]),
     "dg_prof_num_classes": (i32, []),
     "dg_prof_class_name": (ctypes.c_char_p, [i32]),
-    "dg_prof_enable": (i32, [i32]),
+    "dg_prof_enable": (i32, [ctypes.c_uint32]),
     "dg_prof_read": (i32, [i32, P(ctypes.c_double), P(ctypes.c_int64)]),
     "dg_prof_reset": (i32, []),
 }

@@ -53,7 +53,7 @@ const char* kProfNames[PC_COUNT] = {
 
 struct Prof {
   std::mutex mu;
-  bool on = false;
+  uint32_t mask = 0;
   struct Pair {
     hipEvent_t a, b;
     int cls;
@@ -93,7 +93,7 @@ dg_status prof_harvest() {
 template <class F>
 dg_status launch(int cls, hipStream_t s, F&& f) {
   hipEvent_t ea = nullptr, eb = nullptr;
-  if (g_prof.on) {
+  if (g_prof.mask & (1u << cls)) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.pending.size() > 20000) {
       dg_status st = prof_harvest();
@@ -320,6 +320,16 @@ dg_status dg_eb_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, 
   return run_sampler_tail(a, hs);
 }
 
+dg_status dg_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* stream) {
+  if (!src || !dst) return fail(DG_ERR_NULL, "NULL pointer");
+  if (rows < 16 || cols < 32 || rows % 16 || cols % 32)
+    return fail(DG_ERR_SHAPE, "rows must be a multiple of 16 and cols a multiple of 32");
+  if (src == dst) return fail(DG_ERR_SHAPE, "src and dst must not alias");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  DG_LAUNCH(PC_COPY, hs, dg::launch_pack(src, dst, rows, cols, hs));
+  return DG_OK;
+}
+
 dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream) {
   if (!dst || !src) return fail(DG_ERR_NULL, "NULL pointer");
   if (n % 16) return fail(DG_ERR_SHAPE, "n must be a multiple of 16");
@@ -334,9 +344,9 @@ const char* dg_prof_class_name(int32_t cls) {
   return (cls >= 0 && cls < PC_COUNT) ? kProfNames[cls] : "";
 }
 
-dg_status dg_prof_enable(int32_t on) {
+dg_status dg_prof_enable(uint32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  g_prof.on = on != 0;
+  g_prof.mask = mask;
   return DG_OK;
 }
 
@@ -418,7 +428,7 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
   w.gates = c.take<float>(T * d.top_k);
   w.perm = c.take<int32_t>(rows);
   w.inv = c.take<int32_t>(T * d.top_k);
-  const int tr = dg::gemm_moe_tile_rows();
+  const int tr = dg::moe_tile_rows();
   w.max_chunks = d.n_experts + static_cast<int>((T * d.top_k + tr - 1) / tr) +
                  static_cast<int>((T + tr - 1) / tr);
   w.chunks = c.take<int32_t>(static_cast<size_t>(w.max_chunks) * 3);
@@ -518,7 +528,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   DG_LAUNCH(PC_TOPK, s, dg::launch_topk(w.router_part, kRouterSplit, T, d.n_experts, d.top_k, idx,
                                         gates, trace_logits, s));
   DG_LAUNCH(PC_PERMUTE, s, dg::launch_permute(idx, T, d.top_k, d.n_experts,
-                                              dg::gemm_moe_tile_rows(), w.perm, w.inv, w.chunks,
+                                              dg::moe_tile_rows(), w.perm, w.inv, w.chunks,
                                               w.n_chunks, w.max_chunks, s));
   // routed + shared experts: gate/up with SwiGLU, then down
   const int fmax = std::max(d.ffn_inner, d.shared_inner);
@@ -530,7 +540,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   g.K = g.K_sh = d.d_model; g.N = d.ffn_inner; g.N_sh = d.shared_inner;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.act; g.ldo = fmax; g.ksplit = 1;
-  DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_gemm_moe_gateup(g, s));
+  DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, s));
   memset(&g, 0, sizeof(g));
   g.X = w.act; g.ldx = fmax; g.W = static_cast<const uint16_t*>(lw.w_down);
   g.w_estride = static_cast<long long>(d.d_model) * d.ffn_inner;
@@ -538,7 +548,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   g.K = d.ffn_inner; g.K_sh = d.shared_inner; g.N = g.N_sh = d.d_model;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.y; g.ldo = d.d_model; g.ksplit = 1;
-  DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_gemm_moe_down(g, s));
+  DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, s));
   DG_LAUNCH(PC_COMBINE, s, dg::launch_combine(w.h, w.y, w.inv, gates, T, d.top_k, d.d_model,
                                               next_gain, w.u, d.norm_eps, s));
   return DG_OK;

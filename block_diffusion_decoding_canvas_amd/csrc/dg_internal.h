@@ -165,11 +165,13 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 // launchers; each returns the hip error of the launch
 hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out bf16 [rows][N]
 hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // fp32 split partials
-hipError_t launch_gemm_moe_gateup(const WGemmArgs& a, hipStream_t s);     // SwiGLU act
-hipError_t launch_gemm_moe_down(const WGemmArgs& a, hipStream_t s);       // Y rows bf16
 hipError_t launch_gemm_lmhead(const WGemmArgs& a, hipStream_t s);         // logits + stats
 int gemm_lmhead_rows_per_block();
-int gemm_moe_tile_rows();
+// expert products over fragment-major ("packed") weights, tiles of moe_tile_rows() tokens
+hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s);          // SwiGLU act
+hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s);            // Y rows bf16
+int moe_tile_rows();
+hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* qkv;    // [B*C][(Hq+2Hkv)*dh]

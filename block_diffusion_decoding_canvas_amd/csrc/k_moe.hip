@@ -1,0 +1,222 @@
+// Expert (routed + shared) SwiGLU FFN products: the HBM-bound core of the step.
+//
+// The MoE layer (DiffusionGemma model card, dimension table: 8 of 128 experts active plus 1
+// shared) touches every expert's weights once per step while each expert sees only ~16 of the
+// canvas tokens, so the products stream ~1.5 GB per layer at ~16 flop/byte.  Layout and schedule:
+//   * expert weights are stored fragment-major ("tiled"): each 16-row x 32-k MFMA A fragment is a
+//     contiguous 1 KiB block with lane i's 8 elements at 16 i bytes, so one wave load instruction
+//     reads 1 KiB contiguous (dg_pack_weight makes the layout);
+//   * a workgroup (4 waves) takes one token tile (<= 32 rows of one expert, gathered through the
+//     permutation) and 4 x 16 output features; each wave streams its 32 weight rows through a
+//     register ring PS steps deep (one step = 32 k), pinned with scheduling barriers so that the
+//     in-order vector-memory counter only waits for the oldest step;
+//   * the token rows are staged in LDS in 512-k segments, double buffered, loaded one segment
+//     ahead, so they are read from L2 once per workgroup instead of once per wave and MFMA;
+//   * gate/up: the wave holds 16 gate rows and the matching 16 up rows and applies SwiGLU in
+//     the epilogue; down: 2 tiles of 16 output rows; outputs are bf16 rows in permuted order.
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+constexpr int MT_ROWS = 32;           // token rows per tile
+constexpr int SEG = 512;              // k per staged token segment
+constexpr int SEG_STRIDE = SEG + 8;   // bf16 per staged row (1040 B: conflict-free fragments)
+constexpr int PS = 8;                 // register ring depth in 32-k steps
+constexpr int XL = MT_ROWS * (SEG / 8) / 256;  // 16-byte token loads per thread per segment
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_moe(WGemmArgs a) {
+  __shared__ __align__(16) uint16_t xs_lds[2][MT_ROWS * SEG_STRIDE];
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int nb = slot % a.n_nblk;
+  const int tile = slot / a.n_nblk;
+  if (tile >= a.grid_tiles || tile >= *a.n_chunks) return;
+  const int expert = a.chunks[3 * tile];
+  const int row0 = a.chunks[3 * tile + 1];
+  const int nrows = a.chunks[3 * tile + 2];
+  const bool shared = expert == a.n_experts;
+  const uint16_t* W = shared ? a.W_sh : a.W + static_cast<long long>(expert) * a.w_estride;
+  const int N = shared ? a.N_sh : a.N;      // gate/up: F; down: d
+  const int K = shared ? a.K_sh : a.K;
+  constexpr bool GU = EPI == EPI_SWIGLU;
+  const int n0 = nb * (GU ? 64 : 128);      // first output feature of the workgroup
+  if (n0 >= N) return;                      // uniform across the workgroup
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ksteps = K / 32;
+
+  // the wave's two row tiles (fragment-major weights: tile rt, step s at (rt * ksteps + s) KiB)
+  int feat[2];
+  const uint16_t* wfrag[2];
+  bool wave_live;
+  if (GU) {
+    const int f = n0 + wave * 16;
+    wave_live = f < N;
+    const int fc = wave_live ? f : N - 16;
+    feat[0] = feat[1] = f;
+    wfrag[0] = W + (static_cast<long long>(fc / 16) * ksteps) * 512 + lane * 8;        // gate
+    wfrag[1] = W + (static_cast<long long>((N + fc) / 16) * ksteps) * 512 + lane * 8;  // up
+  } else {
+    const int r = n0 + wave * 32;
+    wave_live = r < N;
+    const int rc = wave_live ? r : N - 32;
+    feat[0] = r;
+    feat[1] = r + 16;
+    wfrag[0] = W + (static_cast<long long>(rc / 16) * ksteps) * 512 + lane * 8;
+    wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 512 + lane * 8;
+  }
+
+  // token staging: thread loads XL 16-byte pieces of the 32 x 512 segment
+  const uint16_t* xsrc[XL];
+  int xdst[XL];
+#pragma unroll
+  for (int it = 0; it < XL; ++it) {
+    const int idx = tid + it * 256;
+    const int r = idx / (SEG / 8), c16 = idx % (SEG / 8);
+    const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
+    const int xr = a.x_rows ? a.x_rows[rr] : rr;
+    xsrc[it] = a.X + static_cast<long long>(xr) * a.ldx + c16 * 8;
+    xdst[it] = r * SEG_STRIDE + c16 * 8;
+  }
+  const int nseg = (K + SEG - 1) / SEG;
+  u32x4 xr_[XL];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto load_seg = [&](int sg) __attribute__((always_inline)) {
+    const int k0 = sg * SEG;
+#pragma unroll
+    for (int it = 0; it < XL; ++it) {
+      const int kk = k0 + (xdst[it] % SEG_STRIDE);
+      xr_[it] = (kk < K) ? ld16(xsrc[it] + k0) : zero4;
+    }
+  };
+  auto store_seg = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it]);
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) acc[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weight ring: step s lives in stage s % PS
+  u32x4 wst[PS][2];
+  auto load_step = [&](int s, u32x4 (&w)[2]) __attribute__((always_inline)) {
+    const int sc = min(s, ksteps - 1);    // steps past the end reload the last one (zeroed later)
+    w[0] = ld_nt(wfrag[0] + sc * 512);
+    w[1] = ld_nt(wfrag[1] + sc * 512);
+  };
+
+  load_seg(0);
+#pragma unroll
+  for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
+  store_seg(0);
+  if (nseg > 1) load_seg(1);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int sg = 0; sg < nseg; ++sg) {
+    const uint16_t* xb = xs_lds[sg & 1];
+    const int s_beg = sg * (SEG / 32);
+    const int s_end = min(ksteps, s_beg + SEG / 32);
+    for (int s0 = s_beg; s0 < s_end; s0 += PS) {
+#pragma unroll
+      for (int q = 0; q < PS; ++q) {
+        const int s = s0 + q;                 // s0 is a multiple of PS: stage q holds step s
+        const bool live = s < s_end;      // steps past the end: stale (finite) data, zero weights
+        const int kin = (s - s_beg) * 32 + g * 8;
+        const u32x4 b0 = ld16(xb + r16 * SEG_STRIDE + kin);
+        const u32x4 b1 = ld16(xb + (16 + r16) * SEG_STRIDE + kin);
+        const u32x4 w0 = live ? wst[q][0] : zero4;
+        const u32x4 w1 = live ? wst[q][1] : zero4;
+        acc[0][0] = mfma16x16x32(w0, b0, acc[0][0]);
+        acc[0][1] = mfma16x16x32(w0, b1, acc[0][1]);
+        acc[1][0] = mfma16x16x32(w1, b0, acc[1][0]);
+        acc[1][1] = mfma16x16x32(w1, b1, acc[1][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(s + PS, wst[q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (sg + 1 < nseg) {
+      store_seg((sg + 1) & 1);
+      if (sg + 2 < nseg) load_seg(sg + 2);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (!wave_live) return;
+
+  // epilogue: lane holds out[feature tile + 4g + j][token tb*16 + r16]
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int t = tb * 16 + r16;
+    if (t >= nrows) continue;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<long long>(row0 + t) * a.ldo;
+    if (GU) {
+      const int f = feat[0] + 4 * g;
+      uint2 pk;
+      pk.x = pack_bf2(silu_f(acc[0][tb][0]) * acc[1][tb][0], silu_f(acc[0][tb][1]) * acc[1][tb][1]);
+      pk.y = pack_bf2(silu_f(acc[0][tb][2]) * acc[1][tb][2], silu_f(acc[0][tb][3]) * acc[1][tb][3]);
+      *reinterpret_cast<uint2*>(orow + f) = pk;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        uint2 pk;
+        pk.x = pack_bf2(acc[rt][tb][0], acc[rt][tb][1]);
+        pk.y = pack_bf2(acc[rt][tb][2], acc[rt][tb][3]);
+        *reinterpret_cast<uint2*>(orow + feat[rt] + 4 * g) = pk;
+      }
+    }
+  }
+}
+
+// fragment-major packing of a [rows][cols] bf16 matrix (rows % 16 == 0, cols % 32 == 0):
+// element (n, k) goes to ((n/16 * cols/32 + k/32) * 64 + (k%32)/8 * 16 + n%16) * 8 + k%8
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* src, uint16_t* dst, long long rows,
+                                              long long cols) {
+  const long long frags = (rows / 16) * (cols / 32);
+  const long long i = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (i >= frags) return;
+  const int lane = threadIdx.x & 63;
+  const long long rt = i / (cols / 32), s = i % (cols / 32);
+  const long long n = rt * 16 + (lane & 15), k = s * 32 + (lane >> 4) * 8;
+  st16(dst + i * 512 + lane * 8, ld16(src + n * cols + k));
+}
+
+template <int EPI>
+hipError_t launch_moe(WGemmArgs a, hipStream_t s) {
+  const int per = EPI == EPI_SWIGLU ? 64 : 128;
+  a.n_nblk = (std::max(a.N, a.N_sh) + per - 1) / per;
+  int grid = a.grid_tiles * a.n_nblk;
+  grid = (grid + 7) & ~7;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_moe<EPI>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int moe_tile_rows() { return MT_ROWS; }
+
+hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) { return launch_moe<EPI_SWIGLU>(a, s); }
+hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) { return launch_moe<EPI_BF16>(a, s); }
+
+hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {
+  const long long frags = (rows / 16) * (cols / 32);
+  if (frags == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack, dim3(static_cast<unsigned>((frags + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace dg

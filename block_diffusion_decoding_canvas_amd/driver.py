@@ -110,11 +110,18 @@ class Model:
 
     LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up", "w_down",
                   "ws_gate_up", "ws_down")
+    PACKED_KEYS = ("w_gate_up", "w_down", "ws_gate_up", "ws_down")
 
-    def __init__(self, weights):
+    def __init__(self, weights, packed=False):
+        """weights: row-major device tensors; unless ``packed``, the expert matrices are
+        repacked in place (one layer's worth of scratch) into the fragment-major layout."""
         lib = _lib.load()
         self.weights = weights
         self.dims = dict(weights["dims"])
+        if not packed:
+            for lw in weights["layers"]:
+                for k in self.PACKED_KEYS:
+                    pack_weight_(lw[k])
         n = self.dims["n_layers"]
         layers = (_lib.dg_layer_w * n)()
         for i, lw in enumerate(weights["layers"]):
@@ -192,6 +199,21 @@ def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=
                                ws.numel(), stream_ptr(stream)), "dg_layer_forward")
 
 
+def pack_weight(src, dst, stream=None):
+    """dst <- fragment-major layout of the bf16 matrix src ([..., N, K] viewed as [rows, K])."""
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    check(_lib.load().dg_pack_weight(ptr(src), ptr(dst), rows, cols, stream_ptr(stream)),
+          "dg_pack_weight")
+
+
+def pack_weight_(w, stream=None):
+    """In-place repack of a bf16 device matrix into the fragment-major layout."""
+    tmp = torch.empty_like(w)
+    pack_weight(w, tmp, stream)
+    w.copy_(tmp)
+
+
 def copy_bytes(dst, src, nbytes, stream=None):
     check(_lib.load().dg_copy_bytes(ptr(dst), ptr(src), nbytes, stream_ptr(stream)),
           "dg_copy_bytes")
@@ -205,8 +227,13 @@ class KernelTimer:
         n = self.lib.dg_prof_num_classes()
         self.names = [self.lib.dg_prof_class_name(i).decode() for i in range(n)]
 
-    def enable(self, on=True):
-        check(self.lib.dg_prof_enable(int(on)), "dg_prof_enable")
+    def enable(self, names=None):
+        """Time the named kernel classes (all when None; [] turns timing off)."""
+        names = self.names if names is None else names
+        mask = 0
+        for n in names:
+            mask |= 1 << self.names.index(n)
+        check(self.lib.dg_prof_enable(mask), "dg_prof_enable")
 
     def reset(self):
         check(self.lib.dg_prof_reset(), "dg_prof_reset")

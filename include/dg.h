@@ -74,9 +74,12 @@ typedef struct {
  *   w_qkv   [(Hq + 2 Hkv) dh, d]       rows: queries, keys, values; head-major in each part
  *   w_o     [d, Hq dh]
  *   w_router[E, d]
- *   w_gate_up [E][2F][d]               per expert: F gate rows, then F up rows
- *   w_down    [E][d][F]
- *   ws_gate_up[2Fs][d], ws_down [d][Fs]  the shared expert                                   */
+ *   w_gate_up [E][2F][d]               per expert: F gate rows, then F up rows      (PACKED)
+ *   w_down    [E][d][F]                                                             (PACKED)
+ *   ws_gate_up[2Fs][d], ws_down [d][Fs]  the shared expert                          (PACKED)
+ * PACKED matrices are stored fragment-major, as dg_pack_weight writes them: the expert weights
+ * are streamed from HBM once per step, and this layout makes every wave load one contiguous KiB.
+ * All other matrices are plain row-major [out, in]. */
 typedef struct {
   const void *attn_norm, *w_qkv, *w_o, *ffn_norm, *w_router;
   const void *w_gate_up, *w_down, *ws_gate_up, *ws_down;
@@ -168,15 +171,21 @@ dg_status dg_layer_forward(const dg_model* model, const dg_kv* kv, int32_t layer
                            float* h, float* router_logits, int32_t* topk_idx, float* gates,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* Packs a row-major bf16 matrix [rows][cols] (rows % 16 == 0, cols % 32 == 0; an [E][N][K]
+ * expert tensor is passed as rows = E N) into the fragment-major layout the expert kernels
+ * read: element (n, k) moves to ((n/16 * cols/32 + k/32) * 64 + (k%32)/8 * 16 + n%16) * 8 + k%8.
+ * src and dst are distinct device buffers of rows * cols bf16; asynchronous on `stream`. */
+dg_status dg_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* stream);
+
 /* Plain device copy of n bytes (bandwidth / counter calibration). */
 dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream);
 
-/* Kernel timing: when enabled, the library records HIP events around every launch of the named
- * kernel class on the call's stream and accumulates their durations.  Classes are listed by
- * dg_prof_class_name(i) for i in [0, dg_prof_num_classes()). */
+/* Kernel timing: the library records HIP events around every launch of the kernel classes set
+ * in `mask` (bit i = class i; 0 = off) on the call's stream and accumulates their durations.
+ * Classes are listed by dg_prof_class_name(i) for i in [0, dg_prof_num_classes()). */
 int32_t dg_prof_num_classes(void);
 const char* dg_prof_class_name(int32_t cls);
-dg_status dg_prof_enable(int32_t on);
+dg_status dg_prof_enable(uint32_t mask);
 /* Synchronises the recorded events and returns the total milliseconds and launch count. */
 dg_status dg_prof_read(int32_t cls, double* total_ms, int64_t* launches);
 dg_status dg_prof_reset(void);
