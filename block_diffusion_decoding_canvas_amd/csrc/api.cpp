@@ -252,6 +252,8 @@ dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void
       d->head_dim != 256)
     return fail(DG_ERR_SHAPE, "head_dim must be one of 16, 32, 64, 128, 256");
   if (d->n_q_heads % d->n_kv_heads) return fail(DG_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+  if (((d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim) % 32 || (d->n_q_heads * d->head_dim) % 32)
+    return fail(DG_ERR_SHAPE, "(Hq + 2 Hkv) head_dim and Hq head_dim must be multiples of 32");
   if (d->n_experts < 1 || d->n_experts > 256 || d->top_k < 1 || d->top_k > d->n_experts ||
       d->top_k > 16)
     return fail(DG_ERR_SHAPE, "need 1 <= top_k <= min(16, n_experts), n_experts <= 256");
@@ -480,7 +482,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   // QKV projection
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_qkv);
   g.K = g.K_sh = d.d_model; g.N = g.N_sh = dq; g.ntok = T; g.out = w.qkv; g.ldo = dq; g.ksplit = 1;
-  DG_LAUNCH(PC_GEMM_QKV, s, dg::launch_gemm_dense_bf16(g, s));
+  DG_LAUNCH(PC_GEMM_QKV, s, dg::launch_dense_packed_bf16(g, s));
 
   // attention over [visible cache ; canvas]
   dg::AttnArgs at;
@@ -512,7 +514,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   g.K = g.K_sh = d.n_q_heads * d.head_dim; g.N = g.N_sh = d.d_model; g.ntok = T;
   g.out = w.proj_part; g.ldo = d.d_model; g.ksplit = kOProjSplit;
   g.split_stride = static_cast<long long>(T) * d.d_model;
-  DG_LAUNCH(PC_GEMM_O, s, dg::launch_gemm_dense_f32(g, s));
+  DG_LAUNCH(PC_GEMM_O, s, dg::launch_dense_packed_f32(g, s));
   DG_LAUNCH(PC_RMSNORM, s, dg::launch_resid_norm(w.h, w.proj_part, kOProjSplit, T, d.d_model,
                                                  static_cast<const uint16_t*>(lw.ffn_norm), w.u,
                                                  d.norm_eps, s));

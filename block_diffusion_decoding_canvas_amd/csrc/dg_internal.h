@@ -171,6 +171,9 @@ int gemm_lmhead_rows_per_block();
 hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s);          // SwiGLU act
 hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s);            // Y rows bf16
 int moe_tile_rows();
+// dense products over packed weights, 64-token tiles (bf16 out, or fp32 k-split partials)
+hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s);
+hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s);
 
 struct AttnArgs {

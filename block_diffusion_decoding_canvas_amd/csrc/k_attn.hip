@@ -5,7 +5,7 @@
 // Sliding-window layers: canvas query i at absolute position len + i sees cache position j
 // only if (len + i) - j < window (model card dimension table: 1,024-token window).
 //
-// Layout of the work: one workgroup = (canvas b, KV head g, 64 query rows, one split of the
+// Layout of the work: one workgroup = (canvas b, KV head g, 128 query rows, one split of the
 // key range).  The query rows of a KV head are its Hq/Hkv query heads times the canvas
 // positions, so the K/V tiles staged in LDS serve every query head that reads them.  Keys are
 // processed in tiles of 64 (K tile [key][dh] and V tile transposed [dh][key] in LDS).  Each wave
@@ -19,7 +19,9 @@ namespace dg {
 namespace {
 
 constexpr int KT = 64;        // keys per tile
-constexpr int QB = 64;        // query rows per workgroup (4 waves x 16)
+constexpr int NWAVE = 8;      // waves per workgroup
+constexpr int QB = NWAVE * 16; // query rows per workgroup
+constexpr int NTHR = NWAVE * 64;
 
 template <int DH>
 struct AttnCfg {
@@ -31,19 +33,28 @@ struct AttnCfg {
 };
 
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   using C = AttnCfg<DH>;
+  constexpr int ITEMS = (KT / 2) * (DH / 8) / NTHR;  // (key pair, 8-dh chunk) items per thread
+  constexpr int IT = ITEMS >= 1 ? ITEMS : 1;
   __shared__ __align__(16) uint16_t ks[KT * C::KS_STRIDE];
   __shared__ __align__(16) uint16_t vt[DH * C::VT_STRIDE];
 
-  const int qblk = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z / a.n_split;
-  const int split = blockIdx.z % a.n_split;
+  // logical block -> (canvas, KV head, key split, query block); the query blocks that share a
+  // KV head and split are consecutive, so they run on one XCD and share its L2 for K/V tiles
+  const int R = (a.Hq / a.Hkv) * a.C;
+  const int n_qblk = (R + QB - 1) / QB;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int qblk = L % n_qblk;
+  int rest = L / n_qblk;
+  const int split = rest % a.n_split;
+  rest /= a.n_split;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  if (b >= a.B) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, lg = lane >> 4;
   const int hpg = a.Hq / a.Hkv;
-  const int R = hpg * a.C;
   const int ldqkv = (a.Hq + 2 * a.Hkv) * DH;
 
   const int len = a.len[b];
@@ -85,36 +96,58 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
   const int win_lo = len + qi - a.window + 1;  // first visible cache position (windowed layers)
 
-  for (int tt = t_beg; tt < t_end; ++tt) {
-    const int kbase = tt * KT;
-    __syncthreads();  // previous tile fully consumed
-    // stage K [key][dh] and V^T [dh][key]
-    for (int idx = tid; idx < KT * (DH / 8); idx += 256) {
-      const int key = idx % KT, c = idx / KT;
-      const int kk = kbase + key;
-      u32x4 kv = zero4, vv = zero4;
-      if (kk < nk) {
-        if (kk < nc) {
-          const long long off = static_cast<long long>(c_lo + kk) * DH + c * 8;
-          kv = ld16(kcache + off);
-          vv = ld16(vcache + off);
-        } else {
-          const long long off = static_cast<long long>(kk - nc) * ldqkv + c * 8;
-          kv = ld16(kcanvas + off);
-          vv = ld16(vcanvas + off);
-        }
-      }
-      st16(ks + key * C::KS_STRIDE + c * 8, kv);
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  // staging items: (key pair p, dh chunk c): two keys' rows of K, and of V written transposed
+  u32x4 pk0[IT], pk1[IT], pv0[IT], pv1[IT];
+  auto key_ptr = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
+    return kk < nc ? cache + static_cast<long long>(c_lo + kk) * DH
+                   : canvas + static_cast<long long>(kk - nc) * ldqkv;
+  };
+  auto fetch = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(c * 8 + 2 * e) * C::VT_STRIDE + key] = static_cast<uint16_t>(w[e] & 0xffffu);
-        vt[(c * 8 + 2 * e + 1) * C::VT_STRIDE + key] = static_cast<uint16_t>(w[e] >> 16);
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * NTHR;
+      const bool on = idx < (KT / 2) * (DH / 8);
+      const int p = idx % (KT / 2), c = idx / (KT / 2);
+      const int k0 = tt * KT + 2 * p;
+      pk0[it] = pk1[it] = pv0[it] = pv1[it] = zero4;
+      if (on && k0 < nk) {
+        pk0[it] = ld16(key_ptr(k0, kcache, kcanvas) + c * 8);
+        pv0[it] = ld16(key_ptr(k0, vcache, vcanvas) + c * 8);
+      }
+      if (on && k0 + 1 < nk) {
+        pk1[it] = ld16(key_ptr(k0 + 1, kcache, kcanvas) + c * 8);
+        pv1[it] = ld16(key_ptr(k0 + 1, vcache, vcanvas) + c * 8);
       }
     }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * NTHR;
+      if (idx >= (KT / 2) * (DH / 8)) continue;
+      const int p = idx % (KT / 2), c = idx / (KT / 2);
+      st16(ks + (2 * p) * C::KS_STRIDE + c * 8, pk0[it]);
+      st16(ks + (2 * p + 1) * C::KS_STRIDE + c * 8, pk1[it]);
+      // V^T[dh][key]: each 32-bit store holds keys 2p and 2p+1 of one dh
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a0 = pv0[it][e], a1 = pv1[it][e];
+        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e) * C::VT_STRIDE) + p;
+        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + p;
+        *row0 = (a0 & 0xffffu) | (a1 << 16);
+        *row1 = (a0 >> 16) | (a1 & 0xffff0000u);
+      }
+    }
+  };
+
+  for (int tt = t_beg; tt < t_end; ++tt) {
+    const int kbase = tt * KT;
+    fetch(tt);
+    __syncthreads();  // previous tile fully consumed
+    stage();
     __syncthreads();
 
-    // S^T[key][q] for 4 sub-tiles of 16 keys
+  // S^T[key][q] for 4 sub-tiles of 16 keys
     f32x4 s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -250,8 +283,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 template <int DH>
 hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   const int R = (a.Hq / a.Hkv) * a.C;
-  dim3 grid((R + QB - 1) / QB, a.Hkv, a.B * a.n_split);
-  hipLaunchKernelGGL(k_attn<DH>, grid, dim3(256), 0, s, a);
+  int grid = ((R + QB - 1) / QB) * a.Hkv * a.B * a.n_split;
+  grid = (grid + 7) & ~7;
+  hipLaunchKernelGGL(k_attn<DH>, dim3(grid), dim3(NTHR), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const long long n = static_cast<long long>(a.B) * a.Hkv * R * (DH / 4);

@@ -19,11 +19,7 @@
 namespace dg {
 namespace {
 
-constexpr int MT_ROWS = 32;           // token rows per tile
-constexpr int SEG = 512;              // k per staged token segment
-constexpr int SEG_STRIDE = SEG + 8;   // bf16 per staged row (1040 B: conflict-free fragments)
 constexpr int PS = 8;                 // register ring depth in 32-k steps
-constexpr int XL = MT_ROWS * (SEG / 8) / 256;  // 16-byte token loads per thread per segment
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
@@ -31,27 +27,48 @@ __device__ __forceinline__ u32x4 ld_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_moe(WGemmArgs a) {
-  __shared__ __align__(16) uint16_t xs_lds[2][MT_ROWS * SEG_STRIDE];
+// NTB: 16-token blocks per tile; SEG: k per staged token segment (a multiple of 32 PS).
+// EPI_SWIGLU: gate/up pairs, 64 features per workgroup; otherwise 128 output rows per workgroup,
+// EPI_BF16 stores bf16, EPI_F32 stores the fp32 partial of k-split ks in its own plane.
+template <int EPI, int NTB, int SEG>
+__global__ __launch_bounds__(256) void k_stream(WGemmArgs a) {
+  constexpr int MT = NTB * 16;                      // token rows per tile
+  constexpr int STRIDE = SEG + 8;                   // bf16 per staged row (conflict-free reads)
+  constexpr int XL = MT * (SEG / 8) / 256;          // 16-byte token loads per thread per segment
+  constexpr int SSTEPS = SEG / 32;
+  static_assert(SSTEPS % PS == 0 && XL >= 1, "segment must hold whole ring groups");
+  __shared__ __align__(16) uint16_t xs_lds[2][MT * STRIDE];
+
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
   const int nb = slot % a.n_nblk;
-  const int tile = slot / a.n_nblk;
-  if (tile >= a.grid_tiles || tile >= *a.n_chunks) return;
-  const int expert = a.chunks[3 * tile];
-  const int row0 = a.chunks[3 * tile + 1];
-  const int nrows = a.chunks[3 * tile + 2];
-  const bool shared = expert == a.n_experts;
+  const int tk = slot / a.n_nblk;
+  const int ks = tk % a.ksplit;
+  const int tile = tk / a.ksplit;
+  if (tile >= a.grid_tiles) return;
+  int expert = 0, row0, nrows;
+  if (a.chunks) {
+    if (tile >= *a.n_chunks) return;
+    expert = a.chunks[3 * tile];
+    row0 = a.chunks[3 * tile + 1];
+    nrows = a.chunks[3 * tile + 2];
+  } else {
+    row0 = tile * MT;
+    nrows = min(MT, a.ntok - row0);
+  }
+  const bool shared = a.chunks && expert == a.n_experts;
   const uint16_t* W = shared ? a.W_sh : a.W + static_cast<long long>(expert) * a.w_estride;
-  const int N = shared ? a.N_sh : a.N;      // gate/up: F; down: d
+  const int N = shared ? a.N_sh : a.N;      // gate/up: F; otherwise output rows
   const int K = shared ? a.K_sh : a.K;
   constexpr bool GU = EPI == EPI_SWIGLU;
   const int n0 = nb * (GU ? 64 : 128);      // first output feature of the workgroup
   if (n0 >= N) return;                      // uniform across the workgroup
+  const int k_beg = min(K, ks * a.k_per_split);   // a multiple of SEG
+  const int k_end = min(K, k_beg + a.k_per_split);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int ksteps = K / 32;
+  const int s_first = k_beg / 32, s_last = k_end / 32;   // this split's steps [s_first, s_last)
 
   // the wave's two row tiles (fragment-major weights: tile rt, step s at (rt * ksteps + s) KiB)
   int feat[2];
@@ -74,9 +91,9 @@ __global__ __launch_bounds__(256) void k_moe(WGemmArgs a) {
     wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 512 + lane * 8;
   }
 
-  // token staging: thread loads XL 16-byte pieces of the 32 x 512 segment
+  // token staging: thread loads XL 16-byte pieces of the MT x SEG segment
   const uint16_t* xsrc[XL];
-  int xdst[XL];
+  int xdst[XL], xcol[XL];
 #pragma unroll
   for (int it = 0; it < XL; ++it) {
     const int idx = tid + it * 256;
@@ -84,64 +101,67 @@ __global__ __launch_bounds__(256) void k_moe(WGemmArgs a) {
     const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
     const int xr = a.x_rows ? a.x_rows[rr] : rr;
     xsrc[it] = a.X + static_cast<long long>(xr) * a.ldx + c16 * 8;
-    xdst[it] = r * SEG_STRIDE + c16 * 8;
+    xdst[it] = r * STRIDE + c16 * 8;
+    xcol[it] = c16 * 8;
   }
-  const int nseg = (K + SEG - 1) / SEG;
+  const int nseg = (k_end - k_beg + SEG - 1) / SEG;
   u32x4 xr_[XL];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto load_seg = [&](int sg) __attribute__((always_inline)) {
-    const int k0 = sg * SEG;
+    const int k0 = k_beg + sg * SEG;
 #pragma unroll
-    for (int it = 0; it < XL; ++it) {
-      const int kk = k0 + (xdst[it] % SEG_STRIDE);
-      xr_[it] = (kk < K) ? ld16(xsrc[it] + k0) : zero4;
-    }
+    for (int it = 0; it < XL; ++it)
+      xr_[it] = (k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0) : zero4;
   };
   auto store_seg = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it]);
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[2][NTB];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) acc[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < NTB; ++tb) acc[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight ring: step s lives in stage s % PS
+  // weight ring: local step s (global step s_first + s) lives in stage s % PS
   u32x4 wst[PS][2];
   auto load_step = [&](int s, u32x4 (&w)[2]) __attribute__((always_inline)) {
-    const int sc = min(s, ksteps - 1);    // steps past the end reload the last one (zeroed later)
+    const int sc = min(s_first + s, max(s_last - 1, 0));  // past the end: reload (zeroed later)
     w[0] = ld_nt(wfrag[0] + sc * 512);
     w[1] = ld_nt(wfrag[1] + sc * 512);
   };
 
-  load_seg(0);
+  if (nseg > 0) {
+    load_seg(0);
 #pragma unroll
-  for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
-  store_seg(0);
-  if (nseg > 1) load_seg(1);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-
+    for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
+    store_seg(0);
+    if (nseg > 1) load_seg(1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nsteps = s_last - s_first;
   for (int sg = 0; sg < nseg; ++sg) {
     const uint16_t* xb = xs_lds[sg & 1];
-    const int s_beg = sg * (SEG / 32);
-    const int s_end = min(ksteps, s_beg + SEG / 32);
+    const int s_beg = sg * SSTEPS;
+    const int s_end = min(nsteps, s_beg + SSTEPS);
     for (int s0 = s_beg; s0 < s_end; s0 += PS) {
 #pragma unroll
       for (int q = 0; q < PS; ++q) {
         const int s = s0 + q;                 // s0 is a multiple of PS: stage q holds step s
-        const bool live = s < s_end;      // steps past the end: stale (finite) data, zero weights
+        const bool live = s < s_end;          // steps past the end: stale (finite) data, zero weights
         const int kin = (s - s_beg) * 32 + g * 8;
-        const u32x4 b0 = ld16(xb + r16 * SEG_STRIDE + kin);
-        const u32x4 b1 = ld16(xb + (16 + r16) * SEG_STRIDE + kin);
+        u32x4 b[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
         const u32x4 w0 = live ? wst[q][0] : zero4;
         const u32x4 w1 = live ? wst[q][1] : zero4;
-        acc[0][0] = mfma16x16x32(w0, b0, acc[0][0]);
-        acc[0][1] = mfma16x16x32(w0, b1, acc[0][1]);
-        acc[1][0] = mfma16x16x32(w1, b0, acc[1][0]);
-        acc[1][1] = mfma16x16x32(w1, b1, acc[1][1]);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
+          acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         load_step(s + PS, wst[q]);
         __builtin_amdgcn_sched_barrier(0);
@@ -158,24 +178,33 @@ __global__ __launch_bounds__(256) void k_moe(WGemmArgs a) {
 
   // epilogue: lane holds out[feature tile + 4g + j][token tb*16 + r16]
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < NTB; ++tb) {
     const int t = tb * 16 + r16;
     if (t >= nrows) continue;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<long long>(row0 + t) * a.ldo;
-    if (GU) {
+    const long long orow = row0 + t;
+    if constexpr (GU) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow * a.ldo;
       const int f = feat[0] + 4 * g;
       uint2 pk;
       pk.x = pack_bf2(silu_f(acc[0][tb][0]) * acc[1][tb][0], silu_f(acc[0][tb][1]) * acc[1][tb][1]);
       pk.y = pack_bf2(silu_f(acc[0][tb][2]) * acc[1][tb][2], silu_f(acc[0][tb][3]) * acc[1][tb][3]);
-      *reinterpret_cast<uint2*>(orow + f) = pk;
-    } else {
+      *reinterpret_cast<uint2*>(o + f) = pk;
+    } else if constexpr (EPI == EPI_BF16) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow * a.ldo;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         uint2 pk;
         pk.x = pack_bf2(acc[rt][tb][0], acc[rt][tb][1]);
         pk.y = pack_bf2(acc[rt][tb][2], acc[rt][tb][3]);
-        *reinterpret_cast<uint2*>(orow + feat[rt] + 4 * g) = pk;
+        *reinterpret_cast<uint2*>(o + feat[rt] + 4 * g) = pk;
       }
+    } else {
+      float* o = static_cast<float*>(a.out) + static_cast<long long>(ks) * a.split_stride +
+                 orow * a.ldo;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        *reinterpret_cast<float4*>(o + feat[rt] + 4 * g) =
+            make_float4(acc[rt][tb][0], acc[rt][tb][1], acc[rt][tb][2], acc[rt][tb][3]);
     }
   }
 }
@@ -193,23 +222,38 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* src, uint16_t* dst
   st16(dst + i * 512 + lane * 8, ld16(src + n * cols + k));
 }
 
-template <int EPI>
-hipError_t launch_moe(WGemmArgs a, hipStream_t s) {
+template <int EPI, int NTB, int SEG>
+hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
   const int per = EPI == EPI_SWIGLU ? 64 : 128;
-  a.n_nblk = (std::max(a.N, a.N_sh) + per - 1) / per;
-  int grid = a.grid_tiles * a.n_nblk;
+  a.n_nblk = (std::max(a.N, a.chunks ? a.N_sh : a.N) + per - 1) / per;
+  if (!a.chunks) a.grid_tiles = (a.ntok + NTB * 16 - 1) / (NTB * 16);
+  if (a.ksplit < 1) a.ksplit = 1;
+  const int kmax = a.chunks ? std::max(a.K, a.K_sh) : a.K;
+  const int nseg = (kmax + SEG - 1) / SEG;
+  a.k_per_split = ((nseg + a.ksplit - 1) / a.ksplit) * SEG;
+  int grid = a.grid_tiles * a.ksplit * a.n_nblk;
   grid = (grid + 7) & ~7;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_moe<EPI>, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int moe_tile_rows() { return MT_ROWS; }
+int moe_tile_rows() { return 32; }
 
-hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) { return launch_moe<EPI_SWIGLU>(a, s); }
-hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) { return launch_moe<EPI_BF16>(a, s); }
+hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_SWIGLU, 2, 512>(a, s);
+}
+hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_BF16, 2, 512>(a, s);
+}
+hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_BF16, 4, 256>(a, s);
+}
+hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_F32, 4, 256>(a, s);
+}
 
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {
   const long long frags = (rows / 16) * (cols / 32);

@@ -142,11 +142,19 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* idx, int ntok, 
   __syncthreads();
   for (int p = tid; p < npairs; p += 1024) atomicAdd(&cnt[idx[p]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int s = 0;
-    for (int e = 0; e < n_exp; ++e) {
-      base[e] = s;
-      s += cnt[e];
+  if (w == 0) {  // exclusive scan of the expert counts in one wave
+    int run = 0;
+    for (int e0 = 0; e0 < n_exp; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < n_exp ? cnt[e] : 0;
+      int sc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(sc, o, 64);
+        if (lane >= o) sc += u;
+      }
+      if (e < n_exp) base[e] = run + sc - c;
+      run += __shfl(sc, 63, 64);
     }
   }
   __syncthreads();
@@ -186,27 +194,42 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* idx, int ntok, 
     __syncthreads();
   }
   for (int t = tid; t < ntok; t += 1024) perm[npairs + t] = t;
-  // tile list: ceil(n_e / tile_rows) tiles per expert in expert order, then the shared tiles
-  if (tid == 0) {
-    int s = 0, off = 0;
-    for (int e = 0; e < n_exp; ++e) {
-      nch_off[e] = s;
-      s += (cnt[e] + tile_rows - 1) / tile_rows;
+  // tile list: ceil(n_e / tile_rows) tiles per expert in expert order, then the shared tiles.
+  // Exclusive scans over the experts (row offsets and tile offsets) in one wave.
+  __shared__ int row_off[257];
+  if (w == 0) {
+    int run_rows = 0, run_tiles = 0;
+    for (int e0 = 0; e0 < n_exp; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < n_exp ? cnt[e] : 0;
+      const int nt = (c + tile_rows - 1) / tile_rows;
+      int sr = c, st = nt;   // inclusive scans within the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int ur = __shfl_up(sr, o, 64), ut = __shfl_up(st, o, 64);
+        if (lane >= o) {
+          sr += ur;
+          st += ut;
+        }
+      }
+      if (e < n_exp) {
+        row_off[e] = run_rows + sr - c;
+        nch_off[e] = run_tiles + st - nt;
+      }
+      run_rows += __shfl(sr, 63, 64);
+      run_tiles += __shfl(st, 63, 64);
     }
-    nch_off[n_exp] = s;
-    (void)off;
+    if (lane == 0) {
+      row_off[n_exp] = run_rows;
+      nch_off[n_exp] = run_tiles;
+    }
   }
   __syncthreads();
+  // one thread per (expert, tile): experts use their own tile range
   for (int e = tid; e <= n_exp; e += 1024) {
-    int row0, n, k0 = nch_off[e];
-    if (e < n_exp) {
-      row0 = 0;
-      for (int q = 0; q < e; ++q) row0 += cnt[q];
-      n = cnt[e];
-    } else {
-      row0 = npairs;
-      n = ntok;
-    }
+    const int row0 = e < n_exp ? row_off[e] : npairs;
+    const int n = e < n_exp ? cnt[e] : ntok;
+    const int k0 = nch_off[e];
     for (int c = 0; c * tile_rows < n; ++c) {
       chunks[3 * (k0 + c)] = e;
       chunks[3 * (k0 + c) + 1] = row0 + c * tile_rows;

@@ -110,7 +110,7 @@ class Model:
 
     LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up", "w_down",
                   "ws_gate_up", "ws_down")
-    PACKED_KEYS = ("w_gate_up", "w_down", "ws_gate_up", "ws_down")
+    PACKED_KEYS = ("w_qkv", "w_o", "w_gate_up", "w_down", "ws_gate_up", "ws_down")
 
     def __init__(self, weights, packed=False):
         """weights: row-major device tensors; unless ``packed``, the expert matrices are

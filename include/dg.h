@@ -57,7 +57,8 @@ typedef enum {
 
 enum { DG_BF16 = 0 };
 
-/* Model dimensions.  head_dim, d_model, ffn_inner and shared_inner must be multiples of 32;
+/* Model dimensions.  d_model, ffn_inner, shared_inner, (Hq + 2 Hkv) head_dim and Hq head_dim must
+ * be multiples of 32; head_dim one of 16, 32, 64, 128, 256;
  * n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts <= 256; vocab a multiple of 256;
  * 1 <= canvas_len <= 1024; window == 0 (every layer global) or window >= canvas_len. */
 typedef struct {
@@ -71,14 +72,14 @@ typedef struct {
 
 /* One layer's weights (device, bf16).  Shapes with d = d_model, Hq, Hkv, dh, E, F, Fs:
  *   attn_norm, ffn_norm [d]            RMSNorm gains
- *   w_qkv   [(Hq + 2 Hkv) dh, d]       rows: queries, keys, values; head-major in each part
- *   w_o     [d, Hq dh]
+ *   w_qkv   [(Hq + 2 Hkv) dh, d]       rows: queries, keys, values; head-major     (PACKED)
+ *   w_o     [d, Hq dh]                                                           (PACKED)
  *   w_router[E, d]
  *   w_gate_up [E][2F][d]               per expert: F gate rows, then F up rows      (PACKED)
  *   w_down    [E][d][F]                                                             (PACKED)
  *   ws_gate_up[2Fs][d], ws_down [d][Fs]  the shared expert                          (PACKED)
- * PACKED matrices are stored fragment-major, as dg_pack_weight writes them: the expert weights
- * are streamed from HBM once per step, and this layout makes every wave load one contiguous KiB.
+ * PACKED matrices are stored fragment-major, as dg_pack_weight writes them: they are streamed
+ * from HBM once per step, and this layout makes every wave load one contiguous KiB.
  * All other matrices are plain row-major [out, in]. */
 typedef struct {
   const void *attn_norm, *w_qkv, *w_o, *ffn_norm, *w_router;
