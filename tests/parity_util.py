@@ -12,18 +12,24 @@ REL_TOL = 2e-2
 
 
 def assert_close_rel(gpu, ref, rel=REL_TOL, what=""):
-    """Hidden states and logits: ||a-b|| <= rel ||b|| and |a-b| <= rel |b| + rel * rms(b)."""
+    """Hidden states, logits, cache rows: every row (vector along the last axis) within
+    ||a - b||_2 <= rel ||b||_2, the whole array too, and no element beyond
+    rel |b| + 4 rel rms(row) (a guard against isolated gross errors)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
-    err = np.linalg.norm(gpu - ref)
-    nrm = np.linalg.norm(ref)
-    assert err <= rel * nrm + 1e-30, f"{what}: rel L2 error {err / max(nrm, 1e-30):.3e}"
-    rms = np.sqrt(np.mean(ref * ref))
-    bad = np.abs(gpu - ref) > rel * np.abs(ref) + rel * rms
-    assert not bad.any(), (f"{what}: {bad.sum()} elements outside tolerance, worst "
-                           f"{np.max(np.abs(gpu - ref)):.3e} (rms {rms:.3e})")
+    g2 = gpu.reshape(-1, gpu.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    err = np.linalg.norm(g2 - r2, axis=1)
+    nrm = np.linalg.norm(r2, axis=1)
+    worst = np.max(err / np.maximum(nrm, 1e-30))
+    assert np.all(err <= rel * nrm + 1e-30), f"{what}: worst row rel L2 error {worst:.3e}"
+    assert np.linalg.norm(g2 - r2) <= rel * np.linalg.norm(r2) + 1e-30
+    rms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
+    bad = np.abs(g2 - r2) > rel * np.abs(r2) + 4 * rel * rms
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond the outlier guard, worst "
+                           f"{np.max(np.abs(g2 - r2)):.3e}")
 
 
 def entropy_sensitivity(z_ref64, inv_t):
@@ -99,8 +105,11 @@ def compare_eb_step(what, params, seed, ids, st_before, st_after, ref, gpu_state
     """Compare one EB step of the GPU with the oracle's (run on the oracle's own logits).
 
     ref: result of oracle.sampler.eb_step; st_after: oracle state after it.  z_err[b, i]: bound
-    on |z_gpu - z_oracle| per row (0 when both read the same logits).  Returns False when a
-    certified near-tie prevents an exact comparison (the runs may diverge from here)."""
+    on |z_gpu - z_oracle| per row (None when both read the same logits).  Every canvas is
+    checked: exactly where the oracle's decisions are robust to the float error observed, and
+    for validity (the GPU's commit set is the rule's choice on its own entropies) where a
+    certified near-tie leaves more than one correct answer.  Returns the number of canvases
+    compared exactly (frozen canvases count as exact: they must not change at all)."""
     from oracle import sampler as osamp
     h_gpu = gpu_out.entropy.cpu().numpy().astype(np.float64)
     a_gpu = gpu_out.argmax.cpu().numpy().astype(np.int64)
@@ -115,39 +124,78 @@ def compare_eb_step(what, params, seed, ids, st_before, st_after, ref, gpu_state
                                 entropy_sensitivity(z_ref64, ref["inv_t"]))
     assert_entropy_close(h_gpu, ref["entropy"], what, tol)
     g = gpu_state_host
+    exact = 0
     for b in range(B):
         if st_before["done"][b]:
             assert np.array_equal(g["canvas"][b], st_before["canvas"][b]), "frozen canvas changed"
+            exact += 1
             continue
-        for i in range(C):
-            if a_gpu[b, i] != ref["argmax"][b, i]:
-                assert not argmax_certified(z_ref64[b, i], z_err[b, i]), \
-                    f"{what}: argmax differs at ({b},{i}) with a certified margin"
-                return False
+        mism = np.nonzero(a_gpu[b] != ref["argmax"][b])[0]
+        for i in mism:
+            assert not argmax_certified(z_ref64[b, i], z_err[b, i]), \
+                f"{what}: argmax differs at ({b},{i}) with a certified margin"
         eps = 2.0 * np.abs(h_gpu[b] - ref["entropy"][b]) + 1e-30
         unc = ~st_before["committed"][b]
-        robust = selection_is_robust(ref["entropy"][b], eps, unc, params["entropy_bound"])
+        robust = mism.size == 0
+        robust &= selection_is_robust(ref["entropy"][b], eps, unc, params["entropy_bound"])
         if params["stop_entropy"] >= 0:
             robust &= mean_is_robust(ref["entropy"][b], eps, params["stop_entropy"])
+        if robust:
+            for i in ref["selected"][b]:
+                _, gap = osamp.gumbel_candidate(z_ref64[b, i], ref["inv_t"], seed, ids[b],
+                                                ref["step"], i)
+                if gap <= 2.0 * z_err[b, i] * float(ref["inv_t"]) + 1e-10 and \
+                        g["canvas"][b][i] != st_after["canvas"][b][i]:
+                    robust = False          # a near-tie Gumbel draw: both answers are correct
         if not robust:
             # near-tie: the GPU's commit set must still be the rule's choice on its own entropies
-            if not ref["finalised"][b] and not g["done"][b]:
+            if not g["done"][b]:
                 sel, _, _ = osamp.select_commits(h_gpu[b], unc, params["entropy_bound"])
                 want = np.zeros(C, dtype=bool)
                 want[sel] = True
                 assert np.array_equal(cn_gpu[b], want), f"{what}: GPU commit set invalid (b={b})"
-            return False
+            committed_before = st_before["committed"][b]
+            assert np.array_equal(g["canvas"][b][committed_before],
+                                  st_before["canvas"][b][committed_before]), \
+                f"{what}: committed tokens changed (b={b})"
+            continue
         assert np.array_equal(cn_gpu[b], ref["commit_now"][b]), f"{what}: commit mask (b={b})"
         for k in ("committed", "done", "stable_count", "prev_argmax"):
             assert np.array_equal(g[k][b], st_after[k][b]), f"{what}: {k} differs (b={b})"
-        for i in ref["selected"][b]:
-            _, gap = osamp.gumbel_candidate(z_ref64[b, i], ref["inv_t"], seed, ids[b],
-                                            ref["step"], i)
-            if gap > 2.0 * z_err[b, i] * float(ref["inv_t"]) + 1e-10:
-                assert g["canvas"][b][i] == st_after["canvas"][b][i], f"{what}: candidate at {i}"
-            elif g["canvas"][b][i] != st_after["canvas"][b][i]:
-                return False
-        others = [i for i in range(C) if i not in set(ref["selected"][b])]
-        assert np.array_equal(g["canvas"][b][others], st_after["canvas"][b][others]), \
-            f"{what}: renoised/finalised tokens differ"
-    return True
+        assert np.array_equal(g["canvas"][b], st_after["canvas"][b]), \
+            f"{what}: canvas tokens differ (b={b})"
+        exact += 1
+    return exact
+
+
+def routing_certified(dims, mnp, model, kv, ws, cache64, tokens, causal=False, margin=4.0):
+    """Per-position masks of canvas rows whose expert sets are certified in every layer so far.
+
+    Each layer runs on the GPU (dg_layer_forward) from the oracle's own input to that layer
+    (oracle -> GPU only); a row is certified in a layer when the oracle's gap between its k-th
+    and (k+1)-th router logit exceeds `margin` times the largest router-logit error the GPU
+    shows on that layer.  Returns a list: entry l is the mask of rows certified in layers < l
+    (entry 0 is all True), for l = 0 .. n_layers.  causal: run the encoder layers (these write
+    the rows' keys and values at [len, len + C) of the cache)."""
+    import torch
+    from block_diffusion_decoding_canvas_amd import driver
+    from oracle import model as om
+    tokens = np.asarray(tokens)
+    B, C = tokens.shape
+    T, k = B * C, dims["top_k"]
+    h = mnp["embed"][tokens].astype(np.float64)
+    masks = [np.ones(T, dtype=bool)]
+    for layer in range(dims["n_layers"]):
+        h_next, _, _, info = om.layer_forward(h, mnp["layers"][layer], dims, layer,
+                                              cache64["k"][layer], cache64["v"][layer],
+                                              cache64["len"], causal=causal)
+        hg = torch.from_numpy(h.reshape(T, -1).astype(np.float32)).to("cuda")
+        rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device="cuda")
+        driver.layer_forward(model, kv, layer, int(causal), hg, ws, rl, None, None)
+        torch.cuda.synchronize()
+        r_ref = info["router_logits"]
+        rerr = np.abs(rl.cpu().numpy() - r_ref).max()
+        srt = -np.sort(-r_ref, axis=1)
+        masks.append(masks[-1] & ((srt[:, k - 1] - srt[:, k]) > margin * rerr + 1e-7))
+        h = h_next
+    return masks
