@@ -607,7 +607,7 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
   g.X = w.u; g.ldx = d.d_model; g.W = m->w_lm; g.K = g.K_sh = d.d_model;
   g.N = g.N_sh = d.vocab; g.ntok = T; g.out = out->logits; g.ldo = d.vocab; g.ksplit = 1;
   g.inv_t_log2e = a.inv_t_log2e; g.part = w.eb.part;
-  DG_LAUNCH(PC_LMHEAD, hs, dg::launch_gemm_lmhead(g, hs));
+  DG_LAUNCH(PC_LMHEAD, hs, dg::launch_lmhead_packed(g, hs));
   return run_sampler_tail(a, hs);
 }
 

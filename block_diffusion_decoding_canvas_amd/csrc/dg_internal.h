@@ -165,7 +165,7 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 // launchers; each returns the hip error of the launch
 hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out bf16 [rows][N]
 hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // fp32 split partials
-hipError_t launch_gemm_lmhead(const WGemmArgs& a, hipStream_t s);         // logits + stats
+hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s);       // logits + stats
 int gemm_lmhead_rows_per_block();
 // expert products over fragment-major ("packed") weights, tiles of moe_tile_rows() tokens
 hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s);          // SwiGLU act

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
   const int win_lo = len + qi - a.window + 1;  // first visible cache position (windowed layers)
 
-  // staging items: (key pair p, dh chunk c): two keys' rows of K, and of V written transposed
+  // staging items: (key pair p, dh chunk c): two keys' rows of K, and of V written transposed;
+  // the next tile's rows are prefetched into registers while the current one is computed
   u32x4 pk0[IT], pk1[IT], pv0[IT], pv1[IT];
   auto key_ptr = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
     return kk < nc ? cache + static_cast<long long>(c_lo + kk) * DH
@@ -140,12 +141,14 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
     }
   };
 
+  // the next tile's K/V rows are fetched into registers while the current tile is computed
+  if (t_beg < t_end) fetch(t_beg);
   for (int tt = t_beg; tt < t_end; ++tt) {
     const int kbase = tt * KT;
-    fetch(tt);
     __syncthreads();  // previous tile fully consumed
     stage();
     __syncthreads();
+    if (tt + 1 < t_end) fetch(tt + 1);
 
   // S^T[key][q] for 4 sub-tiles of 16 keys
     f32x4 s[4];

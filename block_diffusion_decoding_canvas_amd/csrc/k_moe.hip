@@ -19,22 +19,49 @@
 namespace dg {
 namespace {
 
-constexpr int PS = 8;                 // register ring depth in 32-k steps
-
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ u32x4 ld_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// NTB: 16-token blocks per tile; SEG: k per staged token segment (a multiple of 32 PS).
-// EPI_SWIGLU: gate/up pairs, 64 features per workgroup; otherwise 128 output rows per workgroup,
-// EPI_BF16 stores bf16, EPI_F32 stores the fp32 partial of k-split ks in its own plane.
-template <int EPI, int NTB, int SEG>
-__global__ __launch_bounds__(256) void k_stream(WGemmArgs a) {
+// statistics of 8 scaled logits given in increasing vocabulary order (4 at n_a.., 4 at n_b..)
+__device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
+  float m = y[0];
+  int k_best = 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k)
+    if (y[k] > m) {
+      m = y[k];
+      k_best = k;
+    }
+  float r = 0.f, acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = y[k] - m;
+    const float e = (k == k_best) ? 0.f : exp2f(d);
+    r += e;
+    acc += d * e;
+  }
+  SoftStats s;
+  s.m = m;
+  s.idx = k_best < 4 ? n_a + k_best : n_b + (k_best - 4);
+  s.r = r;
+  s.a = acc;
+  return s;
+}
+
+// NTB: 16-token blocks per tile; SEG: k per staged token segment (a multiple of 32 PS); WAVES
+// per workgroup; PS: depth of the weight register ring in 32-k steps.  EPI_SWIGLU: gate/up pairs, 16 features per wave; otherwise 32 output rows per
+// wave.  EPI_BF16 stores bf16; EPI_F32 stores the fp32 partial of k-split ks in its own plane;
+// EPI_LMHEAD stores bf16 logits and, per (token, workgroup block of rows), the softmax
+// statistics of the rounded logits scaled by log2(e)/T.
+template <int EPI, int NTB, int SEG, int WAVES, int PS>
+__global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
+  constexpr int NTHR = WAVES * 64;
   constexpr int MT = NTB * 16;                      // token rows per tile
   constexpr int STRIDE = SEG + 8;                   // bf16 per staged row (conflict-free reads)
-  constexpr int XL = MT * (SEG / 8) / 256;          // 16-byte token loads per thread per segment
+  constexpr int XL = MT * (SEG / 8) / NTHR;         // 16-byte token loads per thread per segment
   constexpr int SSTEPS = SEG / 32;
   static_assert(SSTEPS % PS == 0 && XL >= 1, "segment must hold whole ring groups");
   __shared__ __align__(16) uint16_t xs_lds[2][MT * STRIDE];
@@ -60,7 +87,7 @@ __global__ __launch_bounds__(256) void k_stream(WGemmArgs a) {
   const int N = shared ? a.N_sh : a.N;      // gate/up: F; otherwise output rows
   const int K = shared ? a.K_sh : a.K;
   constexpr bool GU = EPI == EPI_SWIGLU;
-  const int n0 = nb * (GU ? 64 : 128);      // first output feature of the workgroup
+  const int n0 = nb * (GU ? WAVES * 16 : WAVES * 32);  // first output feature of the workgroup
   if (n0 >= N) return;                      // uniform across the workgroup
   const int k_beg = min(K, ks * a.k_per_split);   // a multiple of SEG
   const int k_end = min(K, k_beg + a.k_per_split);
@@ -96,7 +123,7 @@ __global__ __launch_bounds__(256) void k_stream(WGemmArgs a) {
   int xdst[XL], xcol[XL];
 #pragma unroll
   for (int it = 0; it < XL; ++it) {
-    const int idx = tid + it * 256;
+    const int idx = tid + it * NTHR;
     const int r = idx / (SEG / 8), c16 = idx % (SEG / 8);
     const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
     const int xr = a.x_rows ? a.x_rows[rr] : rr;
@@ -174,6 +201,57 @@ __global__ __launch_bounds__(256) void k_stream(WGemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (EPI == EPI_LMHEAD) {
+    // bf16 logits; statistics of the rounded logits, merged over the 4 lanes of a token and then
+    // over the waves through LDS (the staging buffers are free after this barrier)
+    __syncthreads();
+    SoftStats* red = reinterpret_cast<SoftStats*>(&xs_lds[0][0]);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const int t = tb * 16 + r16;
+      const bool ok = t < nrows && wave_live;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + static_cast<long long>(row0 + t) * a.ldo;
+      float y[8];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        uint2 pk;
+        pk.x = pack_bf2(acc[rt][tb][0], acc[rt][tb][1]);
+        pk.y = pack_bf2(acc[rt][tb][2], acc[rt][tb][3]);
+        if (ok) *reinterpret_cast<uint2*>(o + feat[rt] + 4 * g) = pk;
+        y[rt * 4 + 0] = __uint_as_float(pk.x << 16) * a.inv_t_log2e;
+        y[rt * 4 + 1] = __uint_as_float(pk.x & 0xffff0000u) * a.inv_t_log2e;
+        y[rt * 4 + 2] = __uint_as_float(pk.y << 16) * a.inv_t_log2e;
+        y[rt * 4 + 3] = __uint_as_float(pk.y & 0xffff0000u) * a.inv_t_log2e;
+      }
+      SoftStats st = stats8(y, feat[0] + 4 * g, feat[1] + 4 * g);
+      bool bad = false;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bad |= !(fabsf(y[k]) <= 3.402823466e38f);
+      if (bad) st.r = NAN;
+#pragma unroll
+      for (int o2 = 16; o2 <= 32; o2 <<= 1) {
+        const SoftStats u = stats_shfl_xor(st, o2);
+        const bool nan = isnan(st.r) || isnan(u.r);
+        st = stats_merge(st, u);
+        if (nan) st.r = NAN;
+      }
+      if (g == 0) red[wave * MT + t] = st;
+    }
+    __syncthreads();
+    for (int t = tid; t < nrows; t += NTHR) {
+      SoftStats st = red[t];
+      bool nan = isnan(st.r);
+      for (int w = 1; w < WAVES; ++w) {
+        if (n0 + w * 32 >= N) break;
+        const SoftStats u = red[w * MT + t];
+        nan |= isnan(u.r);
+        st = stats_merge(st, u);
+      }
+      if (nan) st.r = NAN;
+      a.part[static_cast<long long>(row0 + t) * a.n_nblk + nb] = st;
+    }
+    return;
+  }
   if (!wave_live) return;
 
   // epilogue: lane holds out[feature tile + 4g + j][token tb*16 + r16]
@@ -222,9 +300,9 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* src, uint16_t* dst
   st16(dst + i * 512 + lane * 8, ld16(src + n * cols + k));
 }
 
-template <int EPI, int NTB, int SEG>
+template <int EPI, int NTB, int SEG, int WAVES, int PS>
 hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
-  const int per = EPI == EPI_SWIGLU ? 64 : 128;
+  const int per = EPI == EPI_SWIGLU ? WAVES * 16 : WAVES * 32;
   a.n_nblk = (std::max(a.N, a.chunks ? a.N_sh : a.N) + per - 1) / per;
   if (!a.chunks) a.grid_tiles = (a.ntok + NTB * 16 - 1) / (NTB * 16);
   if (a.ksplit < 1) a.ksplit = 1;
@@ -234,25 +312,29 @@ hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
   int grid = a.grid_tiles * a.ksplit * a.n_nblk;
   grid = (grid + 7) & ~7;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG, WAVES, PS>), dim3(grid), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int moe_tile_rows() { return 32; }
+int gemm_lmhead_rows_per_block() { return 8 * 32; }
 
 hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_SWIGLU, 2, 512>(a, s);
+  return launch_stream<EPI_SWIGLU, 2, 512, 4, 8>(a, s);
 }
 hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_BF16, 2, 512>(a, s);
+  return launch_stream<EPI_BF16, 2, 512, 4, 8>(a, s);
 }
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_BF16, 4, 256>(a, s);
+  return launch_stream<EPI_BF16, 4, 256, 4, 8>(a, s);
 }
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_F32, 4, 256>(a, s);
+  return launch_stream<EPI_F32, 4, 256, 4, 8>(a, s);
+}
+hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_LMHEAD, 16, 128, 8, 4>(a, s);
 }
 
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {

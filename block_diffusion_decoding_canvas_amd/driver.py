@@ -122,6 +122,9 @@ class Model:
             for lw in weights["layers"]:
                 for k in self.PACKED_KEYS:
                     pack_weight_(lw[k])
+            if weights["w_lm"].data_ptr() == weights["embed"].data_ptr():
+                weights["w_lm"] = weights["w_lm"].clone()
+            pack_weight_(weights["w_lm"])
         n = self.dims["n_layers"]
         layers = (_lib.dg_layer_w * n)()
         for i, lw in enumerate(weights["layers"]):

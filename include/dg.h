@@ -90,7 +90,8 @@ typedef struct dg_model dg_model;
 
 /* Build a model handle that BORROWS every pointer until dg_model_destroy.  The encoder and the
  * decoder share these weights (diffusers docs, "PEFT adapters": base weights are tied).
- * layers: host array [n_layers]; embed [V, d]; final_norm [d]; w_lm [V, d] (may alias embed). */
+ * layers: host array [n_layers]; embed [V, d] row-major; final_norm [d]; w_lm [V, d] PACKED
+ * (so w_lm cannot alias embed). */
 dg_status dg_model_create(const dg_dims* dims, const dg_layer_w* layers, const void* embed,
                           const void* final_norm, const void* w_lm, dg_model** out);
 void dg_model_destroy(dg_model* model);
