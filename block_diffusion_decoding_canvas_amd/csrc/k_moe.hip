@@ -134,11 +134,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   const int nseg = (k_end - k_beg + SEG - 1) / SEG;
   u32x4 xr_[XL];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // rows past the tile are zero-filled rather than loaded
+  bool xrow_live[XL];
+#pragma unroll
+  for (int it = 0; it < XL; ++it) xrow_live[it] = (tid + it * NTHR) / (SEG / 8) < nrows;
   auto load_seg = [&](int sg) __attribute__((always_inline)) {
     const int k0 = k_beg + sg * SEG;
 #pragma unroll
     for (int it = 0; it < XL; ++it)
-      xr_[it] = (k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0) : zero4;
+      xr_[it] = (xrow_live[it] && k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0) : zero4;
   };
   auto store_seg = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -161,8 +165,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
 
   if (nseg > 0) {
     load_seg(0);
+    if (wave_live) {
 #pragma unroll
-    for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
+      for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
+    }
     store_seg(0);
     if (nseg > 1) load_seg(1);
     __syncthreads();
@@ -172,7 +178,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   for (int sg = 0; sg < nseg; ++sg) {
     const uint16_t* xb = xs_lds[sg & 1];
     const int s_beg = sg * SSTEPS;
-    const int s_end = min(nsteps, s_beg + SSTEPS);
+    // waves past the last output row skip the stream (they only join the barriers)
+    const int s_end = wave_live ? min(nsteps, s_beg + SSTEPS) : s_beg;
     for (int s0 = s_beg; s0 < s_end; s0 += PS) {
 #pragma unroll
       for (int q = 0; q < PS; ++q) {
@@ -322,10 +329,10 @@ int moe_tile_rows() { return 32; }
 int gemm_lmhead_rows_per_block() { return 8 * 32; }
 
 hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_SWIGLU, 2, 512, 4, 8>(a, s);
+  return launch_stream<EPI_SWIGLU, 2, 256, 4, 4>(a, s);
 }
 hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_BF16, 2, 512, 4, 8>(a, s);
+  return launch_stream<EPI_BF16, 2, 256, 4, 4>(a, s);
 }
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_BF16, 4, 256, 4, 8>(a, s);
