@@ -39,7 +39,25 @@ def parse():
     ap.add_argument("--canvases", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=1)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run only the library's plain copy kernel on buffers of this many MiB "
+                         "(known bytes, to scale hardware byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib, launches=4):
+    """Plain device copy of `mib` MiB, `launches` times: each launch reads and writes exactly
+    mib MiB, the yardstick for FETCH_SIZE / WRITE_SIZE of the other kernels."""
+    import torch
+    from block_diffusion_decoding_canvas_amd import driver
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        driver.copy_bytes(dst, src, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    print(json.dumps(dict(copy_bytes_per_launch=n, launches=launches)))
 
 
 def moe_gateup_bytes(dims, n_touched):
@@ -49,6 +67,25 @@ def moe_gateup_bytes(dims, n_touched):
     weights = (n_touched * 2 * f * d + 2 * fs * d) * 2
     acts = t * d * 2 + (t * k * f + t * fs) * 2
     return weights + acts
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed PMC summary (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the copy-kernel yardstick), or None when the kernel sources no longer hash to the
+    ones the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "moe_gateup_pmc_traffic.txt")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                      if ": " in line and not line.startswith(" "))
+        csrc = os.path.join(ROOT, "block_diffusion_decoding_canvas_amd", "csrc")
+        src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                       for f in ("k_moe.hip", "dg_internal.h"))
+        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"].strip():
+            return None
+        return int(fields["moe_gateup_traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(dims, n_layers_sample, cache_len):
@@ -101,6 +138,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
               f"across GPUs in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import numpy as np
     import torch
     from block_diffusion_decoding_canvas_amd import driver, synth
@@ -172,7 +212,7 @@ def main():
     bytes_gu = moe_gateup_bytes(dims, n_touched)
     achieved = bytes_gu / avg_gu / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     kernel="moe_gateup", bytes_per_launch=bytes_gu,
                     avg_launch_us=round(avg_gu * 1e6, 2), launches=n_gu,
                     experts_touched=n_touched)
