@@ -13,7 +13,7 @@ What the pages fix:
     vocabulary, a 256-token canvas and a 1,024-token sliding window (model card dimension table);
   * the model returns logits [batch, canvas_length, vocab_size] (diffusers docs, class text).
 
-Readings (the pages give no layer internals; each reading is listed in the design notes):
+Readings (the pages give no layer internals, so each of these is a reading):
   * pre-norm RMSNorm before attention, before the FFN and before the LM head, with a gain
     vector and eps = 1e-6; the embedding is a row gather with no scale;
   * attention: one joint softmax per query over the visible cache keys and the canvas keys,
@@ -36,7 +36,7 @@ except the logits (rounded to bf16 before the sampler reads them) and the stored
 """
 import numpy as np
 
-from .numerics import round_bf16
+from .numerics import quantize_rows_e4m3, round_bf16
 
 
 def rms_norm(x, gain, eps):
@@ -91,11 +91,26 @@ def attention(q, k_cache, v_cache, k_new, v_new, cache_mask, causal):
     return out
 
 
-def swiglu_ffn(u, w_gate_up, w_down):
-    """(silu(u Wg^T) * (u Wu^T)) Wd^T with Wg = first half of the rows of w_gate_up."""
+def fp8_linear(x, w_q, s_w):
+    """x W^T with e4m3 weights (fp8 configuration): each row of x is quantised to e4m3 with its
+    own scale (numerics.quantize_rows_e4m3); the e4m3 products and their sums are exact in fp64;
+    the sum is multiplied by the row's input scale and the output channel's weight scale.
+    w_q [N, K] e4m3 values (float64), s_w [N]."""
+    q, s = quantize_rows_e4m3(x)
+    return (q @ w_q.T) * s[..., None] * np.asarray(s_w, dtype=np.float64)
+
+
+def linear(x, w, s_w=None):
+    """x W^T; with a weight scale vector the weights are e4m3 and the product is fp8_linear."""
+    return x @ w.T if s_w is None else fp8_linear(x, w, s_w)
+
+
+def swiglu_ffn(u, w_gate_up, w_down, s_gate_up=None, s_down=None):
+    """(silu(u Wg^T) * (u Wu^T)) Wd^T with Wg = first half of the rows of w_gate_up (with scales:
+    both products in fp8, the SwiGLU output quantised per row before the down product)."""
     f = w_gate_up.shape[0] // 2
-    gu = u @ w_gate_up.T
-    return (silu(gu[..., :f]) * gu[..., f:]) @ w_down.T
+    gu = linear(u, w_gate_up, s_gate_up)
+    return linear(silu(gu[..., :f]) * gu[..., f:], w_down, s_down)
 
 
 def route(u, w_router, top_k):
@@ -118,11 +133,14 @@ def moe(u, lw, top_k):
     ntok, d = u.shape
     n_exp = lw["w_router"].shape[0]
     y = np.zeros((ntok, top_k, d))
+    fp8 = "s_gate_up" in lw
     for e in range(n_exp):
         t_list, j_list = np.nonzero(idx == e)
         if t_list.size:
-            y[t_list, j_list] = swiglu_ffn(u[t_list], lw["w_gate_up"][e], lw["w_down"][e])
-    out = swiglu_ffn(u, lw["ws_gate_up"], lw["ws_down"])
+            y[t_list, j_list] = swiglu_ffn(u[t_list], lw["w_gate_up"][e], lw["w_down"][e],
+                                           lw["s_gate_up"][e] if fp8 else None,
+                                           lw["s_down"][e] if fp8 else None)
+    out = swiglu_ffn(u, lw["ws_gate_up"], lw["ws_down"], lw.get("ss_gate_up"), lw.get("ss_down"))
     for j in range(top_k):
         out = out + gates[:, j:j + 1] * y[:, j]
     return out, dict(router_logits=r, topk_idx=idx, gates=gates)
@@ -172,7 +190,7 @@ def decoder_forward(canvas, model, cache):
         h, _, _, info = layer_forward(h, lw, dims, layer, cache["k"][layer], cache["v"][layer],
                                       cache["len"], causal=False)
         infos.append(info)
-    z = rms_norm(h, model["final_norm"], dims["eps"]) @ model["w_lm"].T
+    z = linear(rms_norm(h, model["final_norm"], dims["eps"]), model["w_lm"], model.get("s_lm"))
     return round_bf16(z), z, infos
 
 
@@ -198,3 +216,21 @@ def encoder_append(tokens, model, cache, round_stored=True):
             vc[b, :, n:n + clen] = store(v[b].transpose(1, 0, 2))
     cache["len"] = cache["len"] + clen
     return cache
+
+
+def quantize_model_e4m3(model):
+    """The fp8 configuration of a model: the routed and shared expert matrices and the LM head
+    are quantised per output channel (row) with numerics.quantize_rows_e4m3, keeping their scales
+    (s_gate_up [E, 2F], s_down [E, d], ss_gate_up [2Fs], ss_down [d], s_lm [V]); attention, router,
+    norms and embedding stay in bf16.  Returns a new model dict (float64 arrays)."""
+    out = dict(dims=dict(model["dims"], wdtype="e4m3"), layers=[])
+    for lw in model["layers"]:
+        q = dict(lw)
+        for key, skey in (("w_gate_up", "s_gate_up"), ("w_down", "s_down"),
+                          ("ws_gate_up", "ss_gate_up"), ("ws_down", "ss_down")):
+            q[key], q[skey] = quantize_rows_e4m3(lw[key])
+        out["layers"].append(q)
+    for key in ("embed", "final_norm"):
+        out[key] = model[key]
+    out["w_lm"], out["s_lm"] = quantize_rows_e4m3(model["w_lm"])
+    return out

@@ -16,7 +16,7 @@ settings", in all three language versions; diffusers DiffusionGemmaPipeline docs
     step, i.e. on two consecutive steps; each sample in a batch freezes on its own;
     ``confidence_threshold=None`` always runs every step.
 
-Readings taken where the pages are silent (each listed in the design notes):
+Readings taken where the pages are silent:
   * entropy in nats; T_s = t_max + (t_min - t_max) * s / (S - 1) in fp64, S = max_steps
     (S = 1 gives t_max); the device multiplies by fp32(1 / T_s), and so does this oracle;
   * the statistics read the bf16 logits the decoder returns; argmax is over those logits,

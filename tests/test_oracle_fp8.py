@@ -1,0 +1,159 @@
+"""Pins of the oracle's fp8 (OCP e4m3) numerics and fp8 products against library routines,
+brute force and closed forms.
+
+The fp8 configuration quantises the expert and LM-head weights per output channel and their
+inputs per row (scale = amax / 448, nearest-even, saturating), with fp32 accumulation; the pages
+only name FP8 (the model card quotes its speed on H100 in FP8), so this is a reading.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle.numerics import (E4M3_MAX, e4m3_code, e4m3_value, quantize_rows_e4m3, round_e4m3)
+
+ALL_FINITE = e4m3_value(np.array([c for c in range(256) if (c & 0x7F) != 0x7F]))
+
+
+def _brute_nearest(y):
+    """Nearest finite e4m3 value by exhaustive search; ties to the even code (mantissa LSB 0);
+    beyond 448 saturates."""
+    vals = np.unique(ALL_FINITE)
+    out = []
+    for v in np.asarray(y, dtype=np.float64):
+        if abs(v) >= E4M3_MAX:
+            out.append(np.copysign(E4M3_MAX, v))
+            continue
+        d = np.abs(vals - v)
+        best = vals[d == d.min()]
+        if best.size > 1:
+            best = [b for b in best if int(e4m3_code(np.array([b]))[0]) % 2 == 0]
+        out.append(best[0])
+    return np.array(out)
+
+
+def test_round_matches_torch_float8_cast():
+    rng = np.random.default_rng(0)
+    # magnitudes across the subnormal, normal and near-max ranges
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-12, 8.7, 200000))).astype(np.float32)
+    x = x[np.abs(x) < E4M3_MAX]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(round_e4m3(x.astype(np.float64)), ref)
+
+
+def test_round_matches_brute_force_including_exact_ties():
+    vals = np.unique(ALL_FINITE)
+    vals = vals[vals >= 0]
+    mids = (vals[:-1] + vals[1:]) / 2              # exact midpoints: ties go to the even code
+    rng = np.random.default_rng(1)
+    y = np.concatenate([mids, -mids, rng.uniform(-450, 450, 3000),
+                        rng.uniform(-2.0 ** -5, 2.0 ** -5, 3000)])
+    assert np.array_equal(round_e4m3(y), _brute_nearest(y))
+
+
+def test_saturation_and_specials():
+    y = np.array([448.0, 460.0, 464.0, 470.0, 1e30, np.inf, -500.0, -np.inf, 0.0, -0.0, np.nan])
+    r = round_e4m3(y)
+    assert np.array_equal(r[:8], [448, 448, 448, 448, 448, 448, -448, -448])
+    assert r[8] == 0 and not np.signbit(r[8]) and r[9] == 0 and np.signbit(r[9])
+    assert np.isnan(r[10])
+    # closed forms: smallest subnormal, smallest normal, one, largest
+    assert e4m3_value(np.array([0x01, 0x08, 0x38, 0x7E, 0xFE]))[:5].tolist() == \
+        [2.0 ** -9, 2.0 ** -6, 1.0, 448.0, -448.0]
+    assert round_e4m3(np.array([2.0 ** -10]))[0] == 0.0           # half the smallest: tie to 0
+    assert round_e4m3(np.array([1.5 * 2.0 ** -10]))[0] == 2.0 ** -9
+
+
+def test_codes_match_torch_bit_patterns():
+    codes = np.arange(256, dtype=np.uint8)
+    tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    ov = e4m3_value(codes)
+    assert np.array_equal(np.isnan(tv), np.isnan(ov))
+    fin = ~np.isnan(ov)
+    assert np.array_equal(tv[fin], ov[fin])
+    assert np.array_equal(e4m3_code(ov[fin]), codes[fin])
+
+
+def test_quantize_rows_properties():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((64, 700)) * np.exp2(rng.uniform(-20, 20, (64, 1)))
+    x[3] = 0.0
+    q, s = quantize_rows_e4m3(x)
+    nz = np.arange(64) != 3
+    # the row maximum maps onto the largest code
+    assert np.all(np.abs(q[nz]).max(axis=1) == E4M3_MAX)
+    assert np.all(q[3] == 0) and s[3] == 1.0
+    # error bound: half a quantum, relative 2**-4 for normals, 2**-10 * s below 2**-6 * s
+    xf = x.astype(np.float32).astype(np.float64)
+    err = np.abs(xf - q * s[:, None])
+    assert np.all(err <= 2.0 ** -4 * np.abs(xf) + 2.0 ** -10 * s[:, None] * (1 + 1e-6)
+                  + 2 ** -20 * np.abs(xf))
+    # odd symmetry and exact power-of-two scaling (binary32 division commutes with 2**k)
+    q2, s2 = quantize_rows_e4m3(-x)
+    assert np.array_equal(q2, -q) and np.array_equal(s2, s)
+    q3, s3 = quantize_rows_e4m3(x * 2.0 ** 5)
+    assert np.array_equal(q3, q) and np.array_equal(s3[nz], s[nz] * 2.0 ** 5) and s3[3] == 1.0
+
+
+def test_quantize_rows_is_binary32_decision():
+    """The scale and the quotient are binary32 operations: recompute them with torch float32."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((16, 300)).astype(np.float32)
+    q, s = quantize_rows_e4m3(x)
+    t = torch.from_numpy(x)
+    st = t.abs().amax(dim=1) / torch.tensor(448.0, dtype=torch.float32)
+    qt = (t / st[:, None]).to(torch.float8_e4m3fn).float()
+    assert np.array_equal(s, st.double().numpy())
+    assert np.array_equal(q, qt.double().numpy())
+
+
+def test_fp8_linear_exact_on_representable_inputs_and_brute_force():
+    rng = np.random.default_rng(4)
+    n, k, t = 24, 64, 10
+    wq = round_e4m3(rng.uniform(-448, 448, (n, k)))
+    sw = np.exp2(rng.integers(-8, 0, n)).astype(np.float64)
+    # inputs already on the e4m3 grid with amax 448 * 2**-3 per row: quantisation is exact
+    xq = round_e4m3(rng.uniform(-448, 448, (t, k)))
+    xq[:, 0] = 448.0
+    x = xq * 2.0 ** -3
+    y = om.fp8_linear(x, wq, sw)
+    assert np.array_equal(y, x @ (wq * sw[:, None]).T)
+    # brute force on arbitrary inputs: quantise, multiply-add term by term, scale
+    xr = rng.standard_normal((t, k))
+    q, s = quantize_rows_e4m3(xr)
+    ref = np.zeros((t, n))
+    for i in range(t):
+        for j in range(n):
+            acc = 0.0
+            for m in range(k):
+                acc += q[i, m] * wq[j, m]
+            ref[i, j] = acc * s[i] * sw[j]
+    assert np.allclose(om.fp8_linear(xr, wq, sw), ref, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("top_k", [8])
+def test_fp8_moe_with_all_experts_is_dense_mixture(top_k):
+    """k = E in the fp8 configuration equals the softmax-weighted dense mixture of the fp8
+    experts plus the fp8 shared expert."""
+    rng = np.random.default_rng(5)
+    d, f, e = 32, 64, top_k
+    lw = dict(w_router=rng.standard_normal((e, d)) * 0.3,
+              w_gate_up=rng.standard_normal((e, 2 * f, d)) * 0.2,
+              w_down=rng.standard_normal((e, d, f)) * 0.2,
+              ws_gate_up=rng.standard_normal((2 * f, d)) * 0.2,
+              ws_down=rng.standard_normal((d, f)) * 0.2)
+    model = dict(dims=dict(n_layers=1), layers=[lw], embed=np.zeros((4, d)),
+                 final_norm=np.ones(d), w_lm=np.zeros((4, d)))
+    qlw = om.quantize_model_e4m3(model)["layers"][0]
+    u = rng.standard_normal((20, d))
+    out, info = om.moe(u, qlw, e)
+    pi = om.softmax(u @ lw["w_router"].T)
+    ref = om.swiglu_ffn(u, qlw["ws_gate_up"], qlw["ws_down"], qlw["ss_gate_up"], qlw["ss_down"])
+    for j in range(e):
+        ref = ref + pi[:, j:j + 1] * om.swiglu_ffn(u, qlw["w_gate_up"][j], qlw["w_down"][j],
+                                                   qlw["s_gate_up"][j], qlw["s_down"][j])
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # the quantised experts stay close to the bf16 ones (e4m3 relative step 2**-3)
+    dense = om.swiglu_ffn(u, lw["ws_gate_up"], lw["ws_down"])
+    q = om.swiglu_ffn(u, qlw["ws_gate_up"], qlw["ws_down"], qlw["ss_gate_up"], qlw["ss_down"])
+    assert np.linalg.norm(q - dense) <= 0.1 * np.linalg.norm(dense)
