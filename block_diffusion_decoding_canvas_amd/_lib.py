@@ -15,6 +15,7 @@ STATUS_NAMES = ["DG_OK", "DG_ERR_NULL", "DG_ERR_SHAPE", "DG_ERR_DTYPE", "DG_ERR_
                 "DG_ERR_WORKSPACE", "DG_ERR_STATE", "DG_ERR_UNSUPPORTED", "DG_ERR_HIP",
                 "DG_ERR_NONFINITE"]
 DG_BF16 = 0
+DG_FP8_E4M3 = 1
 
 c_void_p = ctypes.c_void_p
 i32 = ctypes.c_int32
@@ -29,7 +30,8 @@ class dg_dims(ctypes.Structure):
 
 class dg_layer_w(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router",
-                                        "w_gate_up", "w_down", "ws_gate_up", "ws_down")]
+                                        "w_gate_up", "w_down", "ws_gate_up", "ws_down",
+                                        "s_gate_up", "s_down", "ss_gate_up", "ss_down")]
 
 
 class dg_kv(ctypes.Structure):
@@ -56,7 +58,7 @@ P = ctypes.POINTER
 _SIGS = {
     "dg_last_error": (ctypes.c_char_p, []),
     "dg_model_create": (i32, [P(dg_dims), P(dg_layer_w), c_void_p, c_void_p, c_void_p,
-                              P(c_void_p)]),
+                              c_void_p, P(c_void_p)]),
     "dg_model_destroy": (None, [c_void_p]),
     "dg_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32]),
     "dg_eb_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32]),
@@ -69,6 +71,13 @@ _SIGS = {
                                   c_void_p]),
     "dg_layer_forward": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_ffn_forward": (i32, [c_void_p, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_lm_head_forward": (i32, [c_void_p, i32, c_void_p, i32, P(dg_eb_params), P(dg_step_out),
+                                 c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_quantize_rows_fp8": (i32, [c_void_p, i32, c_void_p, c_void_p, ctypes.c_int64,
+                                   ctypes.c_int64, c_void_p]),
+    "dg_pack_weight_fp8": (i32, [c_void_p, c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p]),
     "dg_copy_bytes": (i32, [c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_pack_weight": (i32, [c_void_p, c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p]),
     "dg_prof_num_classes": (i32, []),

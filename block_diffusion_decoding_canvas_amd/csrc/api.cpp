@@ -16,7 +16,9 @@ struct dg_model {
   std::vector<dg_layer_w> layers;
   const uint16_t* embed;
   const uint16_t* final_norm;
-  const uint16_t* w_lm;
+  const void* w_lm;        // packed bf16, or packed e4m3 codes (fp8 configuration)
+  const float* s_lm;       // fp8: per-row scales of w_lm
+  bool fp8() const { return dims.wdtype == DG_FP8_E4M3; }
 };
 
 namespace {
@@ -44,12 +46,12 @@ dg_status fail(dg_status st, const char* fmt, ...) {
 enum ProfClass {
   PC_EMBED, PC_RMSNORM, PC_GEMM_QKV, PC_ATTENTION, PC_GEMM_O, PC_GEMM_ROUTER, PC_TOPK,
   PC_PERMUTE, PC_MOE_GATEUP, PC_MOE_DOWN, PC_COMBINE, PC_LMHEAD, PC_STATS, PC_STATS_MERGE,
-  PC_EB_COMMIT, PC_CANDIDATES, PC_CAND_APPLY, PC_KV_WRITE, PC_COPY, PC_COUNT
+  PC_EB_COMMIT, PC_CANDIDATES, PC_CAND_APPLY, PC_KV_WRITE, PC_COPY, PC_QUANT, PC_COUNT
 };
 const char* kProfNames[PC_COUNT] = {
     "embed", "rmsnorm", "gemm_qkv", "attention", "gemm_o", "gemm_router", "topk",
     "permute", "moe_gateup", "moe_down", "combine", "lmhead", "logit_stats", "stats_merge",
-    "eb_commit", "candidates", "cand_apply", "kv_write", "copy"};
+    "eb_commit", "candidates", "cand_apply", "kv_write", "copy", "quant"};
 
 struct Prof {
   std::mutex mu;
@@ -238,11 +240,17 @@ extern "C" {
 const char* dg_last_error(void) { return g_err; }
 
 dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void* embed,
-                          const void* final_norm, const void* w_lm, dg_model** out) {
+                          const void* final_norm, const void* w_lm, const float* s_lm,
+                          dg_model** out) {
   if (!d || !layers || !embed || !final_norm || !w_lm || !out)
     return fail(DG_ERR_NULL, "dg_model_create: NULL argument");
   *out = nullptr;
-  if (d->wdtype != DG_BF16) return fail(DG_ERR_DTYPE, "only DG_BF16 weights are supported");
+  if (d->wdtype != DG_BF16 && d->wdtype != DG_FP8_E4M3)
+    return fail(DG_ERR_DTYPE, "wdtype must be DG_BF16 or DG_FP8_E4M3");
+  const bool fp8 = d->wdtype == DG_FP8_E4M3;
+  if (fp8 && (d->d_model % 64 || d->ffn_inner % 64 || d->shared_inner % 64))
+    return fail(DG_ERR_SHAPE, "fp8 weights need d_model, ffn_inner, shared_inner multiples of 64");
+  if (fp8 && !s_lm) return fail(DG_ERR_NULL, "fp8 weights need s_lm");
   if (d->n_layers < 1 || d->d_model < 32 || d->n_q_heads < 1 || d->n_kv_heads < 1 ||
       d->head_dim < 16)
     return fail(DG_ERR_SHAPE, "non-positive or too small dimension");
@@ -269,6 +277,8 @@ dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void
     if (!w.attn_norm || !w.w_qkv || !w.w_o || !w.ffn_norm || !w.w_router || !w.w_gate_up ||
         !w.w_down || !w.ws_gate_up || !w.ws_down)
       return fail(DG_ERR_NULL, "layer %d has a NULL weight", l);
+    if (fp8 && (!w.s_gate_up || !w.s_down || !w.ss_gate_up || !w.ss_down))
+      return fail(DG_ERR_NULL, "layer %d: fp8 weights need their scales", l);
   }
   dg_model* m = new (std::nothrow) dg_model;
   if (!m) return fail(DG_ERR_HIP, "host allocation failed");
@@ -276,7 +286,8 @@ dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void
   m->layers.assign(layers, layers + d->n_layers);
   m->embed = static_cast<const uint16_t*>(embed);
   m->final_norm = static_cast<const uint16_t*>(final_norm);
-  m->w_lm = static_cast<const uint16_t*>(w_lm);
+  m->w_lm = w_lm;
+  m->s_lm = fp8 ? s_lm : nullptr;
   *out = m;
   return DG_OK;
 }
@@ -403,6 +414,12 @@ struct DecWs {
   uint16_t* act;      // [T k + T][max(F, Fs)]
   uint16_t* y;        // [T k + T][d]
   EbWs eb;            // LM-head statistics partials and the sampler's scratch
+  // fp8 configuration only (NULL otherwise)
+  uint8_t* u8;        // [T][d] e4m3 codes of the FFN / LM-head input
+  float* u8s;         // [T] their row scales
+  float* act32;       // [T k + T][max(F, Fs)] fp32 SwiGLU output
+  uint8_t* act8;      // its e4m3 codes
+  float* act8s;       // [T k + T] row scales
 };
 
 int attn_base_blocks(const dg_dims& d, int B) {
@@ -438,6 +455,14 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
   w.act = c.take<uint16_t>(rows * fmax);
   w.y = c.take<uint16_t>(rows * d.d_model);
   w.eb = carve_eb(c, static_cast<int>(T), d.vocab / dg::gemm_lmhead_rows_per_block(), d.vocab);
+  w.u8 = nullptr; w.u8s = nullptr; w.act32 = nullptr; w.act8 = nullptr; w.act8s = nullptr;
+  if (d.wdtype == DG_FP8_E4M3) {
+    w.u8 = c.take<uint8_t>(T * d.d_model);
+    w.u8s = c.take<float>(T);
+    w.act32 = c.take<float>(rows * fmax);
+    w.act8 = c.take<uint8_t>(rows * fmax);
+    w.act8s = c.take<float>(rows);
+  }
   return w;
 }
 
@@ -463,11 +488,16 @@ dg_status check_kv(const dg_model* m, const dg_kv* kv, bool need_room) {
   return DG_OK;
 }
 
+dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* next_gain,
+                  bool next_q8, float* trace_logits, int32_t* trace_idx, float* trace_gates,
+                  hipStream_t s);
+
 // One transformer layer on ws.h (the attention norm of this layer must already be in ws.u).
 // causal: encoder pass (causal canvas, writes K/V into the cache); next_gain: the norm of the
-// following consumer applied to the new h (NULL: none).  Optional router traces.
+// following consumer applied to the new h (NULL: none), with its e4m3 codes when next_q8.
+// Optional router traces.
 dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecWs& w,
-                    const uint16_t* next_gain, bool skip_ffn, float* trace_logits,
+                    const uint16_t* next_gain, bool next_q8, bool skip_ffn, float* trace_logits,
                     int32_t* trace_idx, float* trace_gates, hipStream_t s) {
   const dg_dims& d = m->dims;
   const dg_layer_w& lw = m->layers[l];
@@ -517,7 +547,19 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   DG_LAUNCH(PC_GEMM_O, s, dg::launch_dense_packed_f32(g, s));
   DG_LAUNCH(PC_RMSNORM, s, dg::launch_resid_norm(w.h, w.proj_part, kOProjSplit, T, d.d_model,
                                                  static_cast<const uint16_t*>(lw.ffn_norm), w.u,
-                                                 d.norm_eps, s));
+                                                 d.norm_eps, w.u8, w.u8s, s));
+  return run_ffn(m, l, T, w, next_gain, next_q8, trace_logits, trace_idx, trace_gates, s);
+}
+
+// The FFN half of a layer on ws.h, whose pre-FFN norm (and, for fp8, its e4m3 codes) is in ws.u:
+// router, top-k, permutation, routed + shared SwiGLU experts, combine (+ the next norm).
+dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* next_gain,
+                  bool next_q8, float* trace_logits, int32_t* trace_idx, float* trace_gates,
+                  hipStream_t s) {
+  const dg_dims& d = m->dims;
+  const dg_layer_w& lw = m->layers[l];
+  const bool fp8 = m->fp8();
+  dg::WGemmArgs g;
   // router
   memset(&g, 0, sizeof(g));
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_router);
@@ -542,7 +584,19 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   g.K = g.K_sh = d.d_model; g.N = d.ffn_inner; g.N_sh = d.shared_inner;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.act; g.ldo = fmax; g.ksplit = 1;
-  DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, s));
+  const long long rows = static_cast<long long>(T) * d.top_k + T;
+  if (fp8) {
+    // e4m3 codes of u (gathered through the permutation), fp32 SwiGLU output, then its codes
+    g.X = reinterpret_cast<const uint16_t*>(w.u8); g.x_scale = w.u8s;
+    g.w_scale = lw.s_gate_up; g.wsc_estride = 2LL * d.ffn_inner; g.w_scale_sh = lw.ss_gate_up;
+    g.out = w.act32;
+    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup_fp8(g, s));
+    DG_LAUNCH(PC_QUANT, s, dg::launch_quant_rows(w.act32, true, fmax, w.act8, fmax, w.act8s, rows,
+                                                 static_cast<long long>(T) * d.top_k,
+                                                 d.ffn_inner, d.shared_inner, s));
+  } else {
+    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, s));
+  }
   memset(&g, 0, sizeof(g));
   g.X = w.act; g.ldx = fmax; g.W = static_cast<const uint16_t*>(lw.w_down);
   g.w_estride = static_cast<long long>(d.d_model) * d.ffn_inner;
@@ -550,14 +604,41 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
   g.K = d.ffn_inner; g.K_sh = d.shared_inner; g.N = g.N_sh = d.d_model;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.y; g.ldo = d.d_model; g.ksplit = 1;
-  DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, s));
+  if (fp8) {
+    g.X = reinterpret_cast<const uint16_t*>(w.act8); g.x_scale = w.act8s;
+    g.w_scale = lw.s_down; g.wsc_estride = d.d_model; g.w_scale_sh = lw.ss_down;
+    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down_fp8(g, s));
+  } else {
+    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, s));
+  }
   DG_LAUNCH(PC_COMBINE, s, dg::launch_combine(w.h, w.y, w.inv, gates, T, d.top_k, d.d_model,
-                                              next_gain, w.u, d.norm_eps, s));
+                                              next_gain, w.u, d.norm_eps,
+                                              next_q8 ? w.u8 : nullptr,
+                                              next_q8 ? w.u8s : nullptr, s));
   return DG_OK;
 }
 
 dg_status check_model(const dg_model* m) {
   if (!m) return fail(DG_ERR_NULL, "model is NULL");
+  return DG_OK;
+}
+
+// LM head over the final norm in ws.u (fp8: its e4m3 codes in ws.u8) with the tempered
+// statistics epilogue; logits [T][V] bf16
+dg_status run_lm_head(const dg_model* m, int T, DecWs& w, uint16_t* logits, float inv_t_log2e,
+                      hipStream_t s) {
+  const dg_dims& d = m->dims;
+  dg::WGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(m->w_lm);
+  g.K = g.K_sh = d.d_model; g.N = g.N_sh = d.vocab; g.ntok = T; g.out = logits;
+  g.ldo = d.vocab; g.ksplit = 1; g.inv_t_log2e = inv_t_log2e; g.part = w.eb.part;
+  if (m->fp8()) {
+    g.X = reinterpret_cast<const uint16_t*>(w.u8); g.x_scale = w.u8s; g.w_scale = m->s_lm;
+    DG_LAUNCH(PC_LMHEAD, s, dg::launch_lmhead_packed_fp8(g, s));
+  } else {
+    DG_LAUNCH(PC_LMHEAD, s, dg::launch_lmhead_packed(g, s));
+  }
   return DG_OK;
 }
 
@@ -592,22 +673,18 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
 
   DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(st->canvas, m->embed, w.h, T, d.d_model, d.vocab, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
-                                               w.u, T, d.d_model, d.norm_eps, hs));
+                                               w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
   for (int l = 0; l < d.n_layers; ++l) {
-    const uint16_t* next = (l + 1 < d.n_layers)
-                               ? static_cast<const uint16_t*>(m->layers[l + 1].attn_norm)
-                               : m->final_norm;
-    if ((s = run_layer(m, kv, l, false, w, next, false, nullptr, nullptr, nullptr, hs)) != DG_OK)
+    const bool last = l + 1 == d.n_layers;
+    const uint16_t* next = !last ? static_cast<const uint16_t*>(m->layers[l + 1].attn_norm)
+                                 : m->final_norm;
+    if ((s = run_layer(m, kv, l, false, w, next, last && m->fp8(), false, nullptr, nullptr,
+                       nullptr, hs)) != DG_OK)
       return s;
   }
   // LM head with the tempered statistics, then the sampler
   dg::EbArgs a = eb_args(p, B, C, d.vocab, step, st, out, out->logits, w.eb);
-  dg::WGemmArgs g;
-  memset(&g, 0, sizeof(g));
-  g.X = w.u; g.ldx = d.d_model; g.W = m->w_lm; g.K = g.K_sh = d.d_model;
-  g.N = g.N_sh = d.vocab; g.ntok = T; g.out = out->logits; g.ldo = d.vocab; g.ksplit = 1;
-  g.inv_t_log2e = a.inv_t_log2e; g.part = w.eb.part;
-  DG_LAUNCH(PC_LMHEAD, hs, dg::launch_lmhead_packed(g, hs));
+  if ((s = run_lm_head(m, T, w, out->logits, a.inv_t_log2e, hs)) != DG_OK) return s;
   return run_sampler_tail(a, hs);
 }
 
@@ -626,11 +703,12 @@ dg_status dg_kv_append_canvas(const dg_model* m, dg_kv* kv, const int32_t* token
   DecWs w = carve_dec(c, d, B);
   DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(tokens, m->embed, w.h, T, d.d_model, d.vocab, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
-                                               w.u, T, d.d_model, d.norm_eps, hs));
+                                               w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
   for (int l = 0; l < d.n_layers; ++l) {
     const bool last = l + 1 == d.n_layers;  // its keys/values are all the last layer adds
     const uint16_t* next = last ? nullptr : static_cast<const uint16_t*>(m->layers[l + 1].attn_norm);
-    if ((s = run_layer(m, kv, l, true, w, next, last, nullptr, nullptr, nullptr, hs)) != DG_OK)
+    if ((s = run_layer(m, kv, l, true, w, next, false, last, nullptr, nullptr, nullptr, hs)) !=
+        DG_OK)
       return s;
   }
   for (int b = 0; b < B; ++b) kv->len[b] += C;
@@ -654,11 +732,85 @@ dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, in
   DecWs w = carve_dec(c, d, kv->batch);
   DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].attn_norm),
-                                               w.u, T, d.d_model, d.norm_eps, hs));
-  if ((s = run_layer(m, kv, layer, causal != 0, w, nullptr, false, router_logits, topk_idx, gates,
-                     hs)) != DG_OK)
+                                               w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
+  if ((s = run_layer(m, kv, layer, causal != 0, w, nullptr, false, false, router_logits, topk_idx,
+                     gates, hs)) != DG_OK)
     return s;
   DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  return DG_OK;
+}
+
+dg_status dg_ffn_forward(const dg_model* m, int32_t layer, int32_t batch, float* h,
+                         float* router_logits, int32_t* topk_idx, float* gates, void* ws,
+                         size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if (!h || !ws) return fail(DG_ERR_NULL, "h or workspace is NULL");
+  if (layer < 0 || layer >= m->dims.n_layers) return fail(DG_ERR_SHAPE, "layer out of range");
+  if (batch < 1 || batch > 64) return fail(DG_ERR_SHAPE, "batch must be in [1, 64]");
+  const size_t need = dg_workspace_bytes(m, batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const dg_dims& d = m->dims;
+  const int T = batch * d.canvas_len;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, batch);
+  DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].ffn_norm),
+                                               w.u, T, d.d_model, d.norm_eps, w.u8, w.u8s, hs));
+  if ((s = run_ffn(m, layer, T, w, nullptr, false, router_logits, topk_idx, gates, hs)) != DG_OK)
+    return s;
+  DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  return DG_OK;
+}
+
+dg_status dg_lm_head_forward(const dg_model* m, int32_t batch, const float* h, int32_t step,
+                             const dg_eb_params* p, dg_step_out* out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if (!h || !ws) return fail(DG_ERR_NULL, "h or workspace is NULL");
+  if ((s = check_params(p, step)) != DG_OK) return s;
+  if (!out || !out->entropy || !out->argmax || !out->logits)
+    return fail(DG_ERR_NULL, "out, out->entropy, out->argmax or out->logits is NULL");
+  if (batch < 1 || batch > 64) return fail(DG_ERR_SHAPE, "batch must be in [1, 64]");
+  const size_t need = dg_workspace_bytes(m, batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const dg_dims& d = m->dims;
+  const int T = batch * d.canvas_len;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, batch);
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(h, m->final_norm, w.u, T, d.d_model, d.norm_eps,
+                                               w.u8, w.u8s, hs));
+  dg_eb_state none;
+  memset(&none, 0, sizeof(none));
+  dg::EbArgs a = eb_args(p, batch, d.canvas_len, d.vocab, step, &none, out, out->logits, w.eb);
+  if ((s = run_lm_head(m, T, w, out->logits, a.inv_t_log2e, hs)) != DG_OK) return s;
+  DG_LAUNCH(PC_STATS_MERGE, hs, dg::launch_stats_merge(a, hs));
+  return DG_OK;
+}
+
+dg_status dg_quantize_rows_fp8(const void* src, int32_t src_is_f32, uint8_t* codes, float* scales,
+                               int64_t rows, int64_t cols, void* stream) {
+  if (!src || !codes || !scales) return fail(DG_ERR_NULL, "NULL pointer");
+  if (rows < 1 || cols < 4 || cols % 4 || rows > 0x7fffffffLL)
+    return fail(DG_ERR_SHAPE, "need rows >= 1 and cols a positive multiple of 4");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  DG_LAUNCH(PC_QUANT, hs, dg::launch_quant_rows(src, src_is_f32 != 0, cols, codes, cols, scales,
+                                                rows, rows, static_cast<int>(cols),
+                                                static_cast<int>(cols), hs));
+  return DG_OK;
+}
+
+dg_status dg_pack_weight_fp8(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t cols,
+                             void* stream) {
+  if (!src || !dst) return fail(DG_ERR_NULL, "NULL pointer");
+  if (rows < 16 || cols < 64 || rows % 16 || cols % 64)
+    return fail(DG_ERR_SHAPE, "rows must be a multiple of 16 and cols a multiple of 64");
+  if (src == dst) return fail(DG_ERR_SHAPE, "src and dst must not alias");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  DG_LAUNCH(PC_COPY, hs, dg::launch_pack_fp8(src, dst, rows, cols, hs));
   return DG_OK;
 }
 

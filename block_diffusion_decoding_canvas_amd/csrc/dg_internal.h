@@ -39,6 +39,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// two 16x16x32 OCP-e4m3 MFMAs over one 16-byte fragment pair: bytes 0-7 of every lane, then
+// bytes 8-15 (A and B take the same k mapping, so the k order inside the fragment is free)
+__device__ __forceinline__ f32x4 mfma_fp8_pair(u32x4 a, u32x4 b, f32x4 c) {
+  const long a0 = static_cast<long>((static_cast<uint64_t>(a.y) << 32) | a.x);
+  const long a1 = static_cast<long>((static_cast<uint64_t>(a.w) << 32) | a.z);
+  const long b0 = static_cast<long>((static_cast<uint64_t>(b.y) << 32) | b.x);
+  const long b1 = static_cast<long>((static_cast<uint64_t>(b.w) << 32) | b.z);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
+}
+
+// binary32 -> OCP e4m3 code: nearest, ties to even; magnitudes >= 448 saturate to 448 (0x7E);
+// NaN -> 0x7F.  Normals keep 3 mantissa bits (bias 7); below 2^-6 the quantum is 2^-9.
+__device__ __forceinline__ uint32_t f2e4m3(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (!(a == a)) return sign | 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // exponent and 3 mantissa bits
+  return sign | (r - (120u << 3));                                  // rebias 127 -> 7
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
@@ -158,6 +182,12 @@ struct WGemmArgs {
   // LM-head statistics epilogue
   float inv_t_log2e;      // log2(e) / T as fp32
   SoftStats* part;        // [rows][n_nblk]
+  // e4m3 operands: X holds e4m3 codes with one scale per X row, W packed e4m3 codes with one
+  // scale per weight row; output = accumulator * x_scale * w_scale
+  const float* x_scale;   // indexed like the X rows (through x_rows when gathered)
+  const float* w_scale;   // [experts][weight rows]
+  long long wsc_estride;  // scales between experts
+  const float* w_scale_sh;
 };
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
@@ -175,6 +205,16 @@ int moe_tile_rows();
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s);
+// e4m3 variants (X and W e4m3 codes, per-row scales); gate/up writes the fp32 SwiGLU output
+hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s);      // fp32 act
+hipError_t launch_moe_down_fp8(const WGemmArgs& a, hipStream_t s);        // Y rows bf16
+hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s);   // logits + stats
+hipError_t launch_pack_fp8(const void* src, void* dst, long long rows, long long cols,
+                           hipStream_t s);
+// per-row e4m3 quantisation: rows [0, rows_a) have cols_a columns, rows [rows_a, rows) cols_b
+hipError_t launch_quant_rows(const void* src, bool src_f32, long long ld_src, uint8_t* codes,
+                             long long ld_codes, float* scales, long long rows, long long rows_a,
+                             int cols_a, int cols_b, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* qkv;    // [B*C][(Hq+2Hkv)*dh]
@@ -197,18 +237,21 @@ int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys);
 // per-token kernels
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, int ntok, int d,
                         int vocab, hipStream_t s);
+// norms: u = bf16(RMSNorm(h) * gain); with q8 != NULL also the e4m3 codes of the fp32 normed
+// row and its scale (q8s)
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u, int ntok, int d,
-                          float eps, hipStream_t s);
+                          float eps, uint8_t* q8, float* q8s, hipStream_t s);
 hipError_t launch_topk(const float* logits, int ksplit, int ntok, int n_exp, int top_k,
                        int32_t* idx, float* gates, float* logits_out, hipStream_t s);
 hipError_t launch_resid_norm(float* h, const float* part, int ksplit, int ntok, int d,
-                             const uint16_t* gain, uint16_t* u, float eps, hipStream_t s);
+                             const uint16_t* gain, uint16_t* u, float eps, uint8_t* q8,
+                             float* q8s, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int ntok, int top_k, int n_exp, int tile_rows,
                           int32_t* perm, int32_t* inv, int32_t* chunks, int32_t* n_chunks,
                           int max_chunks, hipStream_t s);
 hipError_t launch_combine(float* h, const uint16_t* Y, const int32_t* inv, const float* gates,
                           int ntok, int top_k, int d, const uint16_t* next_gain,
-                          uint16_t* u_next, float eps, hipStream_t s);
+                          uint16_t* u_next, float eps, uint8_t* q8, float* q8s, hipStream_t s);
 hipError_t launch_kv_write(const uint16_t* qkv, uint16_t* kc, uint16_t* vc, int B, int C,
                            int Hq, int Hkv, int dh, int cap, const int* len, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t n, hipStream_t s);

@@ -21,7 +21,7 @@ namespace {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
-__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p) {
+__device__ __forceinline__ u32x4 ld_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
@@ -51,20 +51,27 @@ __device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
   return s;
 }
 
-// NTB: 16-token blocks per tile; SEG: k per staged token segment (a multiple of 32 PS); WAVES
-// per workgroup; PS: depth of the weight register ring in 32-k steps.  EPI_SWIGLU: gate/up pairs, 16 features per wave; otherwise 32 output rows per
-// wave.  EPI_BF16 stores bf16; EPI_F32 stores the fp32 partial of k-split ks in its own plane;
-// EPI_LMHEAD stores bf16 logits and, per (token, workgroup block of rows), the softmax
-// statistics of the rounded logits scaled by log2(e)/T.
-template <int EPI, int NTB, int SEG, int WAVES, int PS>
+// NTB: 16-token blocks per tile; SEG: k per staged token segment; WAVES per workgroup; PS: depth
+// of the weight register ring in steps; F8: e4m3 codes for X and W (with per-row scales)
+// instead of bf16.  A step is one 16-byte fragment load per lane and weight row tile: 32 k of
+// bf16 (one MFMA) or 64 k of e4m3 (two MFMAs).  EPI_SWIGLU: gate/up pairs, 16 features per
+// wave (bf16 output, fp32 with F8); otherwise 32 output rows per wave.  EPI_BF16 stores bf16;
+// EPI_F32 stores the fp32 partial of k-split ks in its own plane; EPI_LMHEAD stores bf16
+// logits and, per (token, workgroup block of rows), the softmax statistics of the rounded
+// logits scaled by log2(e)/T.
+template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false>
 __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   constexpr int NTHR = WAVES * 64;
+  constexpr int EB = F8 ? 1 : 2;                    // bytes per element
+  constexpr int KSTEP = F8 ? 64 : 32;               // k per step
   constexpr int MT = NTB * 16;                      // token rows per tile
-  constexpr int STRIDE = SEG + 8;                   // bf16 per staged row (conflict-free reads)
-  constexpr int XL = MT * (SEG / 8) / NTHR;         // 16-byte token loads per thread per segment
-  constexpr int SSTEPS = SEG / 32;
-  static_assert(SSTEPS % PS == 0 && XL >= 1, "segment must hold whole ring groups");
-  __shared__ __align__(16) uint16_t xs_lds[2][MT * STRIDE];
+  constexpr int SEGB = SEG * EB;                    // bytes of one staged row segment
+  constexpr int STRIDE = SEGB + 16;                 // bytes per staged row (conflict-free reads)
+  constexpr int XL = MT * (SEGB / 16) / NTHR;       // 16-byte token loads per thread per segment
+  constexpr int SSTEPS = SEG / KSTEP;
+  static_assert(SSTEPS % PS == 0 && XL >= 1 && MT * (SEGB / 16) % NTHR == 0,
+                "segment must hold whole ring groups");
+  __shared__ __align__(16) uint8_t xs_lds[2][MT * STRIDE];
 
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
   const int nb = slot % a.n_nblk;
@@ -83,7 +90,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     nrows = min(MT, a.ntok - row0);
   }
   const bool shared = a.chunks && expert == a.n_experts;
-  const uint16_t* W = shared ? a.W_sh : a.W + static_cast<long long>(expert) * a.w_estride;
+  // w_estride counts elements (EB bytes each)
+  const uint8_t* W = shared ? reinterpret_cast<const uint8_t*>(a.W_sh)
+                            : reinterpret_cast<const uint8_t*>(a.W) +
+                                  static_cast<long long>(expert) * a.w_estride * EB;
   const int N = shared ? a.N_sh : a.N;      // gate/up: F; otherwise output rows
   const int K = shared ? a.K_sh : a.K;
   constexpr bool GU = EPI == EPI_SWIGLU;
@@ -94,42 +104,43 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int ksteps = K / 32;
-  const int s_first = k_beg / 32, s_last = k_end / 32;   // this split's steps [s_first, s_last)
+  const int ksteps = K / KSTEP;
+  const int s_first = k_beg / KSTEP, s_last = k_end / KSTEP;   // this split's steps
 
   // the wave's two row tiles (fragment-major weights: tile rt, step s at (rt * ksteps + s) KiB)
   int feat[2];
-  const uint16_t* wfrag[2];
+  const uint8_t* wfrag[2];
   bool wave_live;
   if (GU) {
     const int f = n0 + wave * 16;
     wave_live = f < N;
     const int fc = wave_live ? f : N - 16;
     feat[0] = feat[1] = f;
-    wfrag[0] = W + (static_cast<long long>(fc / 16) * ksteps) * 512 + lane * 8;        // gate
-    wfrag[1] = W + (static_cast<long long>((N + fc) / 16) * ksteps) * 512 + lane * 8;  // up
+    wfrag[0] = W + (static_cast<long long>(fc / 16) * ksteps) * 1024 + lane * 16;        // gate
+    wfrag[1] = W + (static_cast<long long>((N + fc) / 16) * ksteps) * 1024 + lane * 16;  // up
   } else {
     const int r = n0 + wave * 32;
     wave_live = r < N;
     const int rc = wave_live ? r : N - 32;
     feat[0] = r;
     feat[1] = r + 16;
-    wfrag[0] = W + (static_cast<long long>(rc / 16) * ksteps) * 512 + lane * 8;
-    wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 512 + lane * 8;
+    wfrag[0] = W + (static_cast<long long>(rc / 16) * ksteps) * 1024 + lane * 16;
+    wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 1024 + lane * 16;
   }
 
   // token staging: thread loads XL 16-byte pieces of the MT x SEG segment
-  const uint16_t* xsrc[XL];
+  const uint8_t* X = reinterpret_cast<const uint8_t*>(a.X);
+  const uint8_t* xsrc[XL];
   int xdst[XL], xcol[XL];
 #pragma unroll
   for (int it = 0; it < XL; ++it) {
     const int idx = tid + it * NTHR;
-    const int r = idx / (SEG / 8), c16 = idx % (SEG / 8);
+    const int r = idx / (SEGB / 16), c16 = idx % (SEGB / 16);
     const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
     const int xr = a.x_rows ? a.x_rows[rr] : rr;
-    xsrc[it] = a.X + static_cast<long long>(xr) * a.ldx + c16 * 8;
-    xdst[it] = r * STRIDE + c16 * 8;
-    xcol[it] = c16 * 8;
+    xsrc[it] = X + (static_cast<long long>(xr) * a.ldx) * EB + c16 * 16;
+    xdst[it] = r * STRIDE + c16 * 16;
+    xcol[it] = c16 * (16 / EB);
   }
   const int nseg = (k_end - k_beg + SEG - 1) / SEG;
   u32x4 xr_[XL];
@@ -137,12 +148,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   // rows past the tile are zero-filled rather than loaded
   bool xrow_live[XL];
 #pragma unroll
-  for (int it = 0; it < XL; ++it) xrow_live[it] = (tid + it * NTHR) / (SEG / 8) < nrows;
+  for (int it = 0; it < XL; ++it) xrow_live[it] = (tid + it * NTHR) / (SEGB / 16) < nrows;
   auto load_seg = [&](int sg) __attribute__((always_inline)) {
     const int k0 = k_beg + sg * SEG;
 #pragma unroll
     for (int it = 0; it < XL; ++it)
-      xr_[it] = (xrow_live[it] && k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0) : zero4;
+      xr_[it] = (xrow_live[it] && k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0 * EB) : zero4;
   };
   auto store_seg = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -159,8 +170,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   u32x4 wst[PS][2];
   auto load_step = [&](int s, u32x4 (&w)[2]) __attribute__((always_inline)) {
     const int sc = min(s_first + s, max(s_last - 1, 0));  // past the end: reload (zeroed later)
-    w[0] = ld_nt(wfrag[0] + sc * 512);
-    w[1] = ld_nt(wfrag[1] + sc * 512);
+    w[0] = ld_nt(wfrag[0] + sc * 1024);
+    w[1] = ld_nt(wfrag[1] + sc * 1024);
   };
 
   if (nseg > 0) {
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   }
   const int nsteps = s_last - s_first;
   for (int sg = 0; sg < nseg; ++sg) {
-    const uint16_t* xb = xs_lds[sg & 1];
+    const uint8_t* xb = xs_lds[sg & 1];
     const int s_beg = sg * SSTEPS;
     // waves past the last output row skip the stream (they only join the barriers)
     const int s_end = wave_live ? min(nsteps, s_beg + SSTEPS) : s_beg;
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       for (int q = 0; q < PS; ++q) {
         const int s = s0 + q;                 // s0 is a multiple of PS: stage q holds step s
         const bool live = s < s_end;          // steps past the end: stale (finite) data, zero weights
-        const int kin = (s - s_beg) * 32 + g * 8;
+        const int kin = (s - s_beg) * 64 + g * 16;   // byte offset in the staged row
         u32x4 b[NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
@@ -193,8 +204,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
         const u32x4 w1 = live ? wst[q][1] : zero4;
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-          acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
-          acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
+          if constexpr (F8) {
+            acc[0][tb] = mfma_fp8_pair(w0, b[tb], acc[0][tb]);
+            acc[1][tb] = mfma_fp8_pair(w1, b[tb], acc[1][tb]);
+          } else {
+            acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
+            acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         load_step(s + PS, wst[q]);
@@ -208,11 +224,32 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (F8) {
+    // dequantise: accumulator * token-row scale * weight-row scale
+    const float* wsc = shared ? a.w_scale_sh : a.w_scale + static_cast<long long>(expert) * a.wsc_estride;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float sw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int wrow = (GU && rt == 1 ? N : 0) + feat[rt] + 4 * g + j;
+        sw[j] = wave_live ? wsc[wrow] : 0.f;
+      }
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int rr = row0 + min(tb * 16 + r16, nrows - 1);
+        const float sa = a.x_scale[a.x_rows ? a.x_rows[rr] : rr];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[rt][tb][j] = acc[rt][tb][j] * sa * sw[j];
+      }
+    }
+  }
   if constexpr (EPI == EPI_LMHEAD) {
     // bf16 logits; statistics of the rounded logits, merged over the 4 lanes of a token and then
     // over the waves through LDS (the staging buffers are free after this barrier)
     __syncthreads();
     SoftStats* red = reinterpret_cast<SoftStats*>(&xs_lds[0][0]);
+    static_assert(sizeof(SoftStats) * WAVES * MT <= sizeof(xs_lds), "LDS too small for stats");
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       const int t = tb * 16 + r16;
@@ -267,7 +304,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     const int t = tb * 16 + r16;
     if (t >= nrows) continue;
     const long long orow = row0 + t;
-    if constexpr (GU) {
+    if constexpr (GU && F8) {
+      float* o = static_cast<float*>(a.out) + orow * a.ldo;
+      const int f = feat[0] + 4 * g;
+      *reinterpret_cast<float4*>(o + f) =
+          make_float4(silu_f(acc[0][tb][0]) * acc[1][tb][0], silu_f(acc[0][tb][1]) * acc[1][tb][1],
+                      silu_f(acc[0][tb][2]) * acc[1][tb][2], silu_f(acc[0][tb][3]) * acc[1][tb][3]);
+    } else if constexpr (GU) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + orow * a.ldo;
       const int f = feat[0] + 4 * g;
       uint2 pk;
@@ -307,7 +350,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* src, uint16_t* dst
   st16(dst + i * 512 + lane * 8, ld16(src + n * cols + k));
 }
 
-template <int EPI, int NTB, int SEG, int WAVES, int PS>
+template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false>
 hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
   const int per = EPI == EPI_SWIGLU ? WAVES * 16 : WAVES * 32;
   a.n_nblk = (std::max(a.N, a.chunks ? a.N_sh : a.N) + per - 1) / per;
@@ -319,7 +362,8 @@ hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
   int grid = a.grid_tiles * a.ksplit * a.n_nblk;
   grid = (grid + 7) & ~7;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG, WAVES, PS>), dim3(grid), dim3(WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG, WAVES, PS, F8>), dim3(grid), dim3(WAVES * 64), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -342,6 +386,16 @@ hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
 }
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_LMHEAD, 16, 128, 8, 4>(a, s);
+}
+
+hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_SWIGLU, 2, 512, 4, 4, true>(a, s);
+}
+hipError_t launch_moe_down_fp8(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_BF16, 2, 512, 4, 4, true>(a, s);
+}
+hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s) {
+  return launch_stream<EPI_LMHEAD, 16, 256, 8, 4, true>(a, s);
 }
 
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {

@@ -1,6 +1,7 @@
 // Per-token kernels of the decoder step:
 //   embed     h[t] = E[token t] (row gather, fp32 residual stream)
-//   rmsnorm   u = bf16(h / sqrt(mean(h^2) + eps) * gain)
+//   rmsnorm   u = bf16(h / sqrt(mean(h^2) + eps) * gain); in the fp8 configuration also the
+//             row's e4m3 codes and scale (amax / 448), decided in binary32
 //   topk      router: top-k experts by logit (lowest id on ties, descending order), gates =
 //             softmax weights renormalised over the top-k
 //   permute   stable counting sort of the (token, slot) pairs by expert; emits the row order,
@@ -42,9 +43,54 @@ __device__ float block_sum(float v, float* red) {
   return s;
 }
 
+__device__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float m = 0.f;
+  for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) m = fmaxf(m, red[k]);
+  return m;
+}
+
+// four normed values x * rs * gain of row x at column c
+__device__ __forceinline__ float4 normed4(const float* x, float rs, const uint16_t* gain, int c) {
+  const float4 v = *reinterpret_cast<const float4*>(x + c);
+  const uint2 gg = *reinterpret_cast<const uint2*>(gain + c);
+  return make_float4(v.x * rs * __uint_as_float(gg.x << 16), v.y * rs * __uint_as_float(gg.x & 0xffff0000u),
+                     v.z * rs * __uint_as_float(gg.y << 16), v.w * rs * __uint_as_float(gg.y & 0xffff0000u));
+}
+
+// Writes u = bf16(x * rs * gain) for one row (the whole workgroup); with q8, also the e4m3
+// codes of the same fp32 values, quantised with the row scale amax / 448 (1 for an all-zero
+// row), and that scale.  The quantisation is decided in binary32.
+__device__ void norm_out(const float* x, float rs, const uint16_t* gain, uint16_t* o, int d,
+                         uint8_t* q8, float* q8s, float* red) {
+  float amax = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 y = normed4(x, rs, gain, c);
+    uint2 pk;
+    pk.x = pack_bf2(y.x, y.y);
+    pk.y = pack_bf2(y.z, y.w);
+    *reinterpret_cast<uint2*>(o + c) = pk;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
+  }
+  if (!q8) return;
+  amax = block_max(amax, red);
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 y = normed4(x, rs, gain, c);
+    *reinterpret_cast<uint32_t*>(q8 + c) = f2e4m3(y.x / sc) | (f2e4m3(y.y / sc) << 8) |
+                                           (f2e4m3(y.z / sc) << 16) | (f2e4m3(y.w / sc) << 24);
+  }
+  if (threadIdx.x == 0) *q8s = sc;
+}
+
 // one workgroup per token
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u,
-                                                 int d, float eps) {
+                                                 int d, float eps, uint8_t* q8, float* q8s) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float* x = h + static_cast<long long>(t) * d;
@@ -54,17 +100,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, const uint16_t*
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   const float rs = rsqrtf(block_sum(ss, red) / d + eps);
-  uint16_t* o = u + static_cast<long long>(t) * d;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const uint2 gw = *reinterpret_cast<const uint2*>(gain + c);
-    uint2 pk;
-    pk.x = pack_bf2(v.x * rs * __uint_as_float(gw.x << 16),
-                    v.y * rs * __uint_as_float(gw.x & 0xffff0000u));
-    pk.y = pack_bf2(v.z * rs * __uint_as_float(gw.y << 16),
-                    v.w * rs * __uint_as_float(gw.y & 0xffff0000u));
-    *reinterpret_cast<uint2*>(o + c) = pk;
-  }
+  norm_out(x, rs, gain, u + static_cast<long long>(t) * d, d,
+           q8 ? q8 + static_cast<long long>(t) * d : nullptr, q8 ? q8s + t : nullptr, red);
 }
 
 // one wave per token; n_exp <= 256, top_k <= 16.  The router logits arrive as ksplit fp32
@@ -243,7 +280,8 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* idx, int ntok, 
 // then u = RMSNorm(h[t]) with the given gain
 __global__ __launch_bounds__(256) void k_resid_norm(float* h, const float* part, int ksplit,
                                                     int ntok, int d, const uint16_t* gain,
-                                                    uint16_t* u, float eps) {
+                                                    uint16_t* u, float eps, uint8_t* q8,
+                                                    float* q8s) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   float* x = h + static_cast<long long>(t) * d;
@@ -262,24 +300,15 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, const float* part,
     ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
   }
   const float rs = rsqrtf(block_sum(ss, red) / d + eps);
-  uint16_t* o = u + static_cast<long long>(t) * d;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const uint2 gg = *reinterpret_cast<const uint2*>(gain + c);
-    uint2 pk;
-    pk.x = pack_bf2(v.x * rs * __uint_as_float(gg.x << 16),
-                    v.y * rs * __uint_as_float(gg.x & 0xffff0000u));
-    pk.y = pack_bf2(v.z * rs * __uint_as_float(gg.y << 16),
-                    v.w * rs * __uint_as_float(gg.y & 0xffff0000u));
-    *reinterpret_cast<uint2*>(o + c) = pk;
-  }
+  norm_out(x, rs, gain, u + static_cast<long long>(t) * d, d,
+           q8 ? q8 + static_cast<long long>(t) * d : nullptr, q8 ? q8s + t : nullptr, red);
 }
 
 // one workgroup per token
 __global__ __launch_bounds__(256) void k_combine(float* h, const uint16_t* Y, const int32_t* inv,
                                                  const float* gates, int ntok, int top_k, int d,
                                                  const uint16_t* next_gain, uint16_t* u_next,
-                                                 float eps) {
+                                                 float eps, uint8_t* q8, float* q8s) {
   __shared__ float red[4];
   __shared__ int rows[17];
   __shared__ float gw[16];
@@ -313,17 +342,8 @@ __global__ __launch_bounds__(256) void k_combine(float* h, const uint16_t* Y, co
   }
   if (!next_gain) return;
   const float rs = rsqrtf(block_sum(ss, red) / d + eps);
-  uint16_t* o = u_next + static_cast<long long>(t) * d;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const uint2 gg = *reinterpret_cast<const uint2*>(next_gain + c);
-    uint2 pk;
-    pk.x = pack_bf2(v.x * rs * __uint_as_float(gg.x << 16),
-                    v.y * rs * __uint_as_float(gg.x & 0xffff0000u));
-    pk.y = pack_bf2(v.z * rs * __uint_as_float(gg.y << 16),
-                    v.w * rs * __uint_as_float(gg.y & 0xffff0000u));
-    *reinterpret_cast<uint2*>(o + c) = pk;
-  }
+  norm_out(x, rs, next_gain, u_next + static_cast<long long>(t) * d, d,
+           q8 ? q8 + static_cast<long long>(t) * d : nullptr, q8 ? q8s + t : nullptr, red);
 }
 
 struct KvWriteArgs {
@@ -365,8 +385,8 @@ hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, 
 }
 
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u, int ntok, int d,
-                          float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(ntok), dim3(256), 0, s, h, gain, u, d, eps);
+                          float eps, uint8_t* q8, float* q8s, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(ntok), dim3(256), 0, s, h, gain, u, d, eps, q8, q8s);
   return hipGetLastError();
 }
 
@@ -378,9 +398,10 @@ hipError_t launch_topk(const float* logits, int ksplit, int ntok, int n_exp, int
 }
 
 hipError_t launch_resid_norm(float* h, const float* part, int ksplit, int ntok, int d,
-                             const uint16_t* gain, uint16_t* u, float eps, hipStream_t s) {
+                             const uint16_t* gain, uint16_t* u, float eps, uint8_t* q8,
+                             float* q8s, hipStream_t s) {
   hipLaunchKernelGGL(k_resid_norm, dim3(ntok), dim3(256), 0, s, h, part, ksplit, ntok, d, gain, u,
-                     eps);
+                     eps, q8, q8s);
   return hipGetLastError();
 }
 
@@ -395,9 +416,9 @@ hipError_t launch_permute(const int32_t* idx, int ntok, int top_k, int n_exp, in
 
 hipError_t launch_combine(float* h, const uint16_t* Y, const int32_t* inv, const float* gates,
                           int ntok, int top_k, int d, const uint16_t* next_gain,
-                          uint16_t* u_next, float eps, hipStream_t s) {
+                          uint16_t* u_next, float eps, uint8_t* q8, float* q8s, hipStream_t s) {
   hipLaunchKernelGGL(k_combine, dim3(ntok), dim3(256), 0, s, h, Y, inv, gates, ntok, top_k, d,
-                     next_gain, u_next, eps);
+                     next_gain, u_next, eps, q8, q8s);
   return hipGetLastError();
 }
 

@@ -99,9 +99,10 @@ def eb_sample(logits, step, params, state, out, ws=None, stream=None):
 
 
 def dims_struct(d):
+    wd = _lib.DG_FP8_E4M3 if d.get("wdtype", "bf16") in ("e4m3", "fp8") else _lib.DG_BF16
     return _lib.dg_dims(d["n_layers"], d["d"], d["hq"], d["hkv"], d["dh"], d["E"], d["top_k"],
                         d["F"], d["Fs"], d["V"], d["C"], d["window"], d["global_every"],
-                        _lib.DG_BF16, d["eps"])
+                        wd, d["eps"])
 
 
 class Model:
@@ -111,30 +112,47 @@ class Model:
     LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up", "w_down",
                   "ws_gate_up", "ws_down")
     PACKED_KEYS = ("w_qkv", "w_o", "w_gate_up", "w_down", "ws_gate_up", "ws_down")
+    FP8_KEYS = ("w_gate_up", "w_down", "ws_gate_up", "ws_down")
+    SCALE_KEYS = ("s_gate_up", "s_down", "ss_gate_up", "ss_down")
 
-    def __init__(self, weights, packed=False):
-        """weights: row-major device tensors; unless ``packed``, the expert matrices are
-        repacked in place (one layer's worth of scratch) into the fragment-major layout."""
+    def __init__(self, weights, packed=False, wdtype="bf16"):
+        """weights: row-major bf16 device tensors; unless ``packed``, the streamed matrices
+        are repacked in place into the fragment-major layout.  wdtype "e4m3": the expert and
+        LM-head matrices are first quantised per row to e4m3 codes (the bf16 masters are
+        released) and their fp32 row scales are kept as s_* entries."""
         lib = _lib.load()
         self.weights = weights
-        self.dims = dict(weights["dims"])
+        self.dims = dict(weights["dims"], wdtype=wdtype)
+        fp8 = wdtype in ("e4m3", "fp8")
+        if weights["w_lm"].data_ptr() == weights["embed"].data_ptr():
+            weights["w_lm"] = weights["w_lm"].clone()
         if not packed:
             for lw in weights["layers"]:
                 for k in self.PACKED_KEYS:
-                    pack_weight_(lw[k])
-            if weights["w_lm"].data_ptr() == weights["embed"].data_ptr():
-                weights["w_lm"] = weights["w_lm"].clone()
-            pack_weight_(weights["w_lm"])
+                    if fp8 and k in self.FP8_KEYS:
+                        lw[k], lw[self.SCALE_KEYS[self.FP8_KEYS.index(k)]] = quantize_pack_fp8(lw[k])
+                    else:
+                        pack_weight_(lw[k])
+            if fp8:
+                weights["w_lm"], weights["s_lm"] = quantize_pack_fp8(weights["w_lm"])
+            else:
+                pack_weight_(weights["w_lm"])
         n = self.dims["n_layers"]
         layers = (_lib.dg_layer_w * n)()
         for i, lw in enumerate(weights["layers"]):
             for k in self.LAYER_KEYS:
-                assert lw[k].dtype == torch.bfloat16 and lw[k].is_contiguous(), k
+                want = torch.uint8 if fp8 and k in self.FP8_KEYS else torch.bfloat16
+                assert lw[k].dtype == want and lw[k].is_contiguous(), k
                 setattr(layers[i], k, lw[k].data_ptr())
+            if fp8:
+                for k in self.SCALE_KEYS:
+                    assert lw[k].dtype == torch.float32 and lw[k].is_contiguous(), k
+                    setattr(layers[i], k, lw[k].data_ptr())
         self._dims = dims_struct(self.dims)
         h = ctypes.c_void_p()
         check(lib.dg_model_create(ctypes.byref(self._dims), layers, ptr(weights["embed"]),
                                   ptr(weights["final_norm"]), ptr(weights["w_lm"]),
+                                  ptr(weights.get("s_lm")) if fp8 else None,
                                   ctypes.byref(h)), "dg_model_create")
         self.handle = h
 
@@ -215,6 +233,50 @@ def pack_weight_(w, stream=None):
     tmp = torch.empty_like(w)
     pack_weight(w, tmp, stream)
     w.copy_(tmp)
+
+
+def ffn_forward(model, layer, batch, h, ws, router_logits=None, topk_idx=None, gates=None,
+                stream=None):
+    check(_lib.load().dg_ffn_forward(model.handle, layer, batch, ptr(h), ptr(router_logits),
+                                     ptr(topk_idx), ptr(gates), ptr(ws), ws.numel(),
+                                     stream_ptr(stream)), "dg_ffn_forward")
+
+
+def lm_head_forward(model, batch, h, step, params, out, ws, stream=None):
+    o = out.struct()
+    check(_lib.load().dg_lm_head_forward(model.handle, batch, ptr(h), step, ctypes.byref(params),
+                                         ctypes.byref(o), ptr(ws), ws.numel(), stream_ptr(stream)),
+          "dg_lm_head_forward")
+
+
+def quantize_rows_fp8(src, codes, scales, stream=None):
+    """e4m3 codes [rows, cols] (uint8) and fp32 row scales of a bf16 or fp32 matrix."""
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    assert src.dtype in (torch.bfloat16, torch.float32) and src.is_contiguous()
+    check(_lib.load().dg_quantize_rows_fp8(ptr(src), int(src.dtype == torch.float32), ptr(codes),
+                                           ptr(scales), rows, cols, stream_ptr(stream)),
+          "dg_quantize_rows_fp8")
+
+
+def pack_weight_fp8(src, dst, stream=None):
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    check(_lib.load().dg_pack_weight_fp8(ptr(src), ptr(dst), rows, cols, stream_ptr(stream)),
+          "dg_pack_weight_fp8")
+
+
+def quantize_pack_fp8(w, stream=None):
+    """(packed e4m3 codes with w's shape, fp32 row scales) of a bf16 matrix [..., N, K]."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=w.device)
+    quantize_rows_fp8(w, codes, scales, stream)
+    packed = torch.empty_like(codes)
+    pack_weight_fp8(codes, packed, stream)
+    del codes
+    return packed, scales
 
 
 def copy_bytes(dst, src, nbytes, stream=None):

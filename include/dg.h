@@ -55,10 +55,17 @@ typedef enum {
   DG_ERR_NONFINITE = 9     /* written to *dev_status when a logit row is not finite           */
 } dg_status;
 
-enum { DG_BF16 = 0 };
+/* Weight dtypes.  DG_FP8_E4M3 is the fp8 configuration: the model card quotes its speed on H100
+ * in FP8 without a scheme, so this library reads it as OCP e4m3 (bias 7, max 448, no infinities)
+ * for the routed and shared expert matrices and the LM head, each row (output channel) with an
+ * fp32 scale amax / 448, and their inputs quantised the same way per token row at run time
+ * (nearest even, saturating, decided in binary32); fp32 accumulation; output = accumulator *
+ * input scale * weight scale.  Attention, router, norms and embedding stay bf16. */
+enum { DG_BF16 = 0, DG_FP8_E4M3 = 1 };
 
 /* Model dimensions.  d_model, ffn_inner, shared_inner, (Hq + 2 Hkv) head_dim and Hq head_dim must
- * be multiples of 32; head_dim one of 16, 32, 64, 128, 256;
+ * be multiples of 32 (d_model, ffn_inner, shared_inner multiples of 64 with DG_FP8_E4M3);
+ * head_dim one of 16, 32, 64, 128, 256;
  * n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts <= 256; vocab a multiple of 256;
  * 1 <= canvas_len <= 1024; window == 0 (every layer global) or window >= canvas_len. */
 typedef struct {
@@ -66,11 +73,11 @@ typedef struct {
   int32_t n_experts, top_k, ffn_inner, shared_inner, vocab, canvas_len;
   int32_t window;        /* sliding window in tokens; 0 = every layer global                  */
   int32_t global_every;  /* layer l is global iff window == 0 || (l + 1) % global_every == 0   */
-  int32_t wdtype;        /* DG_BF16                                                           */
+  int32_t wdtype;        /* DG_BF16 or DG_FP8_E4M3 (expert and LM-head matrices)              */
   float norm_eps;        /* RMSNorm epsilon (1e-6)                                            */
 } dg_dims;
 
-/* One layer's weights (device, bf16).  Shapes with d = d_model, Hq, Hkv, dh, E, F, Fs:
+/* One layer's weights (device).  Shapes with d = d_model, Hq, Hkv, dh, E, F, Fs:
  *   attn_norm, ffn_norm [d]            RMSNorm gains
  *   w_qkv   [(Hq + 2 Hkv) dh, d]       rows: queries, keys, values; head-major     (PACKED)
  *   w_o     [d, Hq dh]                                                           (PACKED)
@@ -80,20 +87,26 @@ typedef struct {
  *   ws_gate_up[2Fs][d], ws_down [d][Fs]  the shared expert                          (PACKED)
  * PACKED matrices are stored fragment-major, as dg_pack_weight writes them: they are streamed
  * from HBM once per step, and this layout makes every wave load one contiguous KiB.
- * All other matrices are plain row-major [out, in]. */
+ * All other matrices are plain row-major [out, in], bf16.
+ * With DG_FP8_E4M3 the four expert matrices hold e4m3 codes packed by dg_pack_weight_fp8, and
+ * s_gate_up [E][2F], s_down [E][d], ss_gate_up [2Fs], ss_down [d] are their fp32 row scales
+ * (dg_quantize_rows_fp8); with DG_BF16 the scale pointers are ignored. */
 typedef struct {
   const void *attn_norm, *w_qkv, *w_o, *ffn_norm, *w_router;
   const void *w_gate_up, *w_down, *ws_gate_up, *ws_down;
+  const float *s_gate_up, *s_down, *ss_gate_up, *ss_down;
 } dg_layer_w;
 
 typedef struct dg_model dg_model;
 
 /* Build a model handle that BORROWS every pointer until dg_model_destroy.  The encoder and the
  * decoder share these weights (diffusers docs, "PEFT adapters": base weights are tied).
- * layers: host array [n_layers]; embed [V, d] row-major; final_norm [d]; w_lm [V, d] PACKED
- * (so w_lm cannot alias embed). */
+ * layers: host array [n_layers]; embed [V, d] row-major bf16; final_norm [d]; w_lm [V, d] PACKED
+ * (so w_lm cannot alias embed): bf16, or e4m3 codes with row scales s_lm [V] for DG_FP8_E4M3
+ * (s_lm is ignored for DG_BF16). */
 dg_status dg_model_create(const dg_dims* dims, const dg_layer_w* layers, const void* embed,
-                          const void* final_norm, const void* w_lm, dg_model** out);
+                          const void* final_norm, const void* w_lm, const float* s_lm,
+                          dg_model** out);
 void dg_model_destroy(dg_model* model);
 
 /* Static KV cache (diffusers docs, "Static cache and compilation").
@@ -178,6 +191,32 @@ dg_status dg_layer_forward(const dg_model* model, const dg_kv* kv, int32_t layer
  * read: element (n, k) moves to ((n/16 * cols/32 + k/32) * 64 + (k%32)/8 * 16 + n%16) * 8 + k%8.
  * src and dst are distinct device buffers of rows * cols bf16; asynchronous on `stream`. */
 dg_status dg_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* stream);
+
+/* One FFN half-layer (pre-FFN norm, router, routed + shared experts, residual) on h [B*C, d]
+ * fp32, updated in place; batch = B.  Trace outputs as for dg_layer_forward. */
+dg_status dg_ffn_forward(const dg_model* model, int32_t layer, int32_t batch, float* h,
+                         float* router_logits, int32_t* topk_idx, float* gates, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Final norm and LM head on h [B*C, d] fp32 (read only): writes out->logits (bf16 [B, C, V]),
+ * out->entropy (of softmax(logits / T_step), the schedule of params) and out->argmax, exactly as
+ * dg_decoder_step computes them; no sampler state is read or written. */
+dg_status dg_lm_head_forward(const dg_model* model, int32_t batch, const float* h, int32_t step,
+                             const dg_eb_params* params, dg_step_out* out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Per-row e4m3 quantisation of a row-major matrix src [rows][cols] (bf16, or fp32 when
+ * src_is_f32): scales[r] = max_c |src[r][c]| / 448 in fp32 (1 for an all-zero row) and
+ * codes[r][c] = e4m3(src[r][c] / scales[r]), binary32 division, nearest even, saturating.
+ * cols % 4 == 0; codes [rows][cols] uint8 and scales [rows] fp32 are device buffers. */
+dg_status dg_quantize_rows_fp8(const void* src, int32_t src_is_f32, uint8_t* codes, float* scales,
+                               int64_t rows, int64_t cols, void* stream);
+
+/* Packs e4m3 codes [rows][cols] (rows % 16 == 0, cols % 64 == 0) into the fragment-major layout
+ * the fp8 expert and LM-head kernels read: element (n, k) moves to
+ * ((n/16 * cols/64 + k/64) * 64 + (k%64)/16 * 16 + n%16) * 16 + k%16.  Distinct buffers. */
+dg_status dg_pack_weight_fp8(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t cols,
+                             void* stream);
 
 /* Plain device copy of n bytes (bandwidth / counter calibration). */
 dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream);

@@ -154,12 +154,11 @@ def split_qkv(qkv, dims):
     return q, k, v
 
 
-def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
-    """One transformer layer over a batch of canvases.
+def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
+    """First half of a layer: h + O-projection of the joint attention over RMSNorm(h).
 
-    h [B, C, d] residual stream; k_cache, v_cache [B, Hkv, cap, dh] (this layer);
-    cache_len [B].  Returns (new h, k [B, C, Hkv, dh], v, routing info).
-    """
+    h [B, C, d]; k_cache, v_cache [B, Hkv, cap, dh] (this layer); cache_len [B].
+    Returns (h after attention, k [B, C, Hkv, dh], v) -- k, v are the canvas keys/values."""
     eps = dims["eps"]
     bsz, clen, d = h.shape
     u = rms_norm(h, lw["attn_norm"], eps)
@@ -170,10 +169,25 @@ def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
         n = int(cache_len[b])
         mask = visible_cache_mask(n, clen, window)
         o[b] = attention(q[b], k_cache[b, :, :n], v_cache[b, :, :n], k[b], v[b], mask, causal)
-    h = h + o.reshape(bsz, clen, -1) @ lw["w_o"].T
-    u = rms_norm(h, lw["ffn_norm"], eps)
+    return h + o.reshape(bsz, clen, -1) @ lw["w_o"].T, k, v
+
+
+def ffn_block(h, lw, dims):
+    """Second half of a layer: h + MoE(RMSNorm(h)).  Returns (new h, routing info)."""
+    bsz, clen, d = h.shape
+    u = rms_norm(h, lw["ffn_norm"], dims["eps"])
     f, info = moe(u.reshape(bsz * clen, d), lw, dims["top_k"])
-    h = h + f.reshape(bsz, clen, d)
+    return h + f.reshape(bsz, clen, d), info
+
+
+def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
+    """One transformer layer over a batch of canvases.
+
+    h [B, C, d] residual stream; k_cache, v_cache [B, Hkv, cap, dh] (this layer);
+    cache_len [B].  Returns (new h, k [B, C, Hkv, dh], v, routing info).
+    """
+    h, k, v = attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal)
+    h, info = ffn_block(h, lw, dims)
     return h, k, v, info
 
 

@@ -168,7 +168,8 @@ def compare_eb_step(what, params, seed, ids, st_before, st_after, ref, gpu_state
     return exact
 
 
-def routing_certified(dims, mnp, model, kv, ws, cache64, tokens, causal=False, margin=4.0):
+def routing_certified(dims, mnp, model, kv, ws, cache64, tokens, causal=False, margin=4.0,
+                      ref_model=None, check_layers=False):
     """Per-position masks of canvas rows whose expert sets are certified in every layer so far.
 
     Each layer runs on the GPU (dg_layer_forward) from the oracle's own input to that layer
@@ -176,17 +177,21 @@ def routing_certified(dims, mnp, model, kv, ws, cache64, tokens, causal=False, m
     and (k+1)-th router logit exceeds `margin` times the largest router-logit error the GPU
     shows on that layer.  Returns a list: entry l is the mask of rows certified in layers < l
     (entry 0 is all True), for l = 0 .. n_layers.  causal: run the encoder layers (these write
-    the rows' keys and values at [len, len + C) of the cache)."""
+    the rows' keys and values at [len, len + C) of the cache).  ref_model: the oracle's model
+    when it differs from `mnp` (the e4m3-quantised model of the fp8 configuration).
+    check_layers: also compare each layer's increment (output - input) with the oracle's on the
+    rows certified in that layer, at the stated tolerance."""
     import torch
     from block_diffusion_decoding_canvas_amd import driver
     from oracle import model as om
     tokens = np.asarray(tokens)
     B, C = tokens.shape
     T, k = B * C, dims["top_k"]
-    h = mnp["embed"][tokens].astype(np.float64)
+    src = ref_model if ref_model is not None else mnp
+    h = src["embed"][tokens].astype(np.float64)
     masks = [np.ones(T, dtype=bool)]
     for layer in range(dims["n_layers"]):
-        h_next, _, _, info = om.layer_forward(h, mnp["layers"][layer], dims, layer,
+        h_next, _, _, info = om.layer_forward(h, src["layers"][layer], dims, layer,
                                               cache64["k"][layer], cache64["v"][layer],
                                               cache64["len"], causal=causal)
         hg = torch.from_numpy(h.reshape(T, -1).astype(np.float32)).to("cuda")
@@ -196,6 +201,13 @@ def routing_certified(dims, mnp, model, kv, ws, cache64, tokens, causal=False, m
         r_ref = info["router_logits"]
         rerr = np.abs(rl.cpu().numpy() - r_ref).max()
         srt = -np.sort(-r_ref, axis=1)
-        masks.append(masks[-1] & ((srt[:, k - 1] - srt[:, k]) > margin * rerr + 1e-7))
+        layer_cert = (srt[:, k - 1] - srt[:, k]) > margin * rerr + 1e-7
+        if check_layers:
+            h_in = h.reshape(T, -1).astype(np.float32).astype(np.float64)
+            hout = hg.cpu().numpy().astype(np.float64)
+            assert_close_rel(hout[layer_cert] - h_in[layer_cert],
+                             h_next.reshape(T, -1)[layer_cert] - h_in[layer_cert],
+                             what=f"layer {layer} increment (certified routing)")
+        masks.append(masks[-1] & layer_cert)
         h = h_next
     return masks

@@ -34,7 +34,7 @@ def _tiny_dims(**kw):
     return driver.dims_struct(d)
 
 
-def _create(dims, null_layer=False):
+def _create(dims, null_layer=False, scales=True, s_lm=True):
     lib = _lib.load()
     n = dims.n_layers
     layers = (_lib.dg_layer_w * n)()
@@ -42,11 +42,15 @@ def _create(dims, null_layer=False):
     for i in range(n):
         for k in driver.Model.LAYER_KEYS:
             setattr(layers[i], k, fake)
+        if scales:
+            for k in driver.Model.SCALE_KEYS:
+                setattr(layers[i], k, fake)
     if null_layer:
         layers[n - 1].w_down = None
     h = ctypes.c_void_p()
     st = lib.dg_model_create(ctypes.byref(dims), layers, ctypes.c_void_p(fake),
-                             ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.byref(h))
+                             ctypes.c_void_p(fake), ctypes.c_void_p(fake),
+                             ctypes.c_void_p(fake) if s_lm else None, ctypes.byref(h))
     return st, h
 
 
@@ -68,6 +72,56 @@ def test_model_create_validation():
     d.wdtype = 7
     st, _ = _create(d)
     assert st == 3                               # DG_ERR_DTYPE
+    # the bf16 configuration ignores the scale pointers
+    st, h = _create(_tiny_dims(), scales=False, s_lm=False)
+    assert st == 0
+    lib.dg_model_destroy(h)
+
+
+def test_fp8_model_create_validation():
+    lib = _lib.load()
+    fp8 = dict(wdtype="e4m3")
+    st, h = _create(_tiny_dims(**fp8))
+    assert st == 0
+    # the fp8 workspace holds the e4m3 activation buffers on top of the bf16 one
+    st2, hb = _create(_tiny_dims())
+    assert lib.dg_workspace_bytes(h, 1) > lib.dg_workspace_bytes(hb, 1)
+    lib.dg_model_destroy(h)
+    lib.dg_model_destroy(hb)
+    assert _create(_tiny_dims(d=96, **fp8))[0] == 2        # d_model % 64
+    assert _create(_tiny_dims(F=96, **fp8))[0] == 2        # ffn_inner % 64
+    assert _create(_tiny_dims(**fp8), scales=False)[0] == 1
+    assert _create(_tiny_dims(**fp8), s_lm=False)[0] == 1
+
+
+def test_quantize_and_pack_fp8_validation():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dg_quantize_rows_fp8(fake, 0, fake, fake, 4, 6, None) == 2
+    assert lib.dg_quantize_rows_fp8(fake, 0, fake, fake, 0, 8, None) == 2
+    assert lib.dg_quantize_rows_fp8(None, 0, fake, fake, 4, 8, None) == 1
+    assert lib.dg_pack_weight_fp8(fake, ctypes.c_void_p(0x2000), 16, 32, None) == 2
+    assert lib.dg_pack_weight_fp8(fake, ctypes.c_void_p(0x2000), 8, 64, None) == 2
+    assert lib.dg_pack_weight_fp8(fake, fake, 16, 64, None) == 2   # aliasing
+    assert lib.dg_pack_weight_fp8(None, fake, 16, 64, None) == 1
+
+
+def test_stage_calls_validate():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    ws = lib.dg_workspace_bytes(h, 2)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dg_ffn_forward(h, 2, 1, fake, None, None, None, fake, ws, None) == 2   # layer
+    assert lib.dg_ffn_forward(h, 0, 2, fake, None, None, None, fake, ws - 1, None) == 5
+    assert lib.dg_ffn_forward(h, 0, 0, fake, None, None, None, fake, ws, None) == 2
+    p = driver.eb_params(max_steps=8)
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0x1000)
+    assert lib.dg_lm_head_forward(h, 2, fake, 8, ctypes.byref(p), ctypes.byref(out), fake, ws,
+                                  None) == 6
+    out.logits = None
+    assert lib.dg_lm_head_forward(h, 2, fake, 0, ctypes.byref(p), ctypes.byref(out), fake, ws,
+                                  None) == 1
+    lib.dg_model_destroy(h)
 
 
 def test_eb_sample_validation_before_launch():

@@ -157,6 +157,10 @@ def test_full_width_layer(causal):
     cert = np.array([np.sort(r_ref[t])[::-1][k - 1] - np.sort(r_ref[t])[::-1][k] >
                      2 * rerr[t] + 1e-7 for t in range(T)])
     assert_close_rel(hout[cert], h_ref[cert], what="layer output (certified routing)")
+    # the layer's increment on its own (the residual input passes through unchanged)
+    h_in = h.reshape(T, -1).astype(np.float64)
+    assert_close_rel(hout[cert] - h_in[cert], h_ref[cert] - h_in[cert],
+                     what="layer increment (certified routing)")
     if causal:
         kgpu = kv.k[0].float().cpu().numpy()[0, :, 2048:2048 + T]
         vgpu = kv.v[0].float().cpu().numpy()[0, :, 2048:2048 + T]

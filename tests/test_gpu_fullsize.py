@@ -60,9 +60,11 @@ def _layers_on_oracle_inputs(dims, mnp, model, kv, ws, c64, canvas):
         tig = ti.cpu().numpy()
         for t in np.nonzero(layer_cert)[0]:
             assert set(tig[t]) == set(info["topk_idx"][t]), f"layer {layer} token {t} experts"
-        hout = hg.cpu().numpy()
-        assert_close_rel(hout[layer_cert], h_next.reshape(T, -1)[layer_cert],
-                         what=f"layer {layer} output (certified routing)")
+        hout = hg.cpu().numpy().astype(np.float64)
+        h_in = h.reshape(T, -1).astype(np.float32).astype(np.float64)
+        assert_close_rel(hout[layer_cert] - h_in[layer_cert],
+                         h_next.reshape(T, -1)[layer_cert] - h_in[layer_cert],
+                         what=f"layer {layer} increment (certified routing)")
         print(f"layer {layer}: router err {rerr:.2e}, certified {layer_cert.sum()}/{T}")
         cert &= layer_cert
         h = h_next

@@ -64,7 +64,8 @@ def test_ragged_windowed_batch_steps_with_frozen_canvas():
         torch.cuda.synchronize()
         zr, z64, _ = om.decoder_forward(st["canvas"], m64, c64)
         zg = out.logits.float().cpu().numpy()
-        cert = routing_certified(dims, mnp, model, kv, ws, c64, st["canvas"])[-1]
+        cert = routing_certified(dims, mnp, model, kv, ws, c64, st["canvas"],
+                                 check_layers=True)[-1]
         cert = cert.reshape(B, dims["C"])
         assert cert.sum() >= cert.size // 4
         assert_close_rel(zg[cert], zr[cert], what=f"logits s={s} (certified rows)")
