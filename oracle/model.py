@@ -68,19 +68,21 @@ def visible_cache_mask(cache_len, canvas_len, window):
     return (cache_len + i) - j < window
 
 
-def attention(q, k_cache, v_cache, k_new, v_new, cache_mask, causal):
+def attention(q, k_cache, v_cache, k_new, v_new, cache_mask, causal, q_pos=None):
     """Joint softmax attention for one canvas.
 
-    q [C, Hq, dh]; k_cache, v_cache [Hkv, L, dh]; k_new, v_new [C, Hkv, dh];
-    cache_mask [C, L] bool; causal: canvas query i sees canvas key j only if j <= i.
-    Returns [C, Hq, dh].
+    q [R, Hq, dh] for the canvas positions q_pos (default: all C positions, R = C);
+    k_cache, v_cache [Hkv, L, dh]; k_new, v_new [C, Hkv, dh]; cache_mask [R, L] bool;
+    causal: canvas query i sees canvas key j only if j <= i.  Returns [R, Hq, dh].
     """
-    clen, hq, dh = q.shape
+    rows, hq, dh = q.shape
+    clen = k_new.shape[0]
     hkv = k_new.shape[1]
+    q_pos = np.arange(clen) if q_pos is None else np.asarray(q_pos)
     out = np.zeros_like(q)
-    canvas_mask = (np.tril(np.ones((clen, clen), dtype=bool)) if causal
-                   else np.ones((clen, clen), dtype=bool))
-    mask = np.concatenate([cache_mask, canvas_mask], axis=1)          # [C, L + C]
+    j = np.arange(clen)[None, :]
+    canvas_mask = (j <= q_pos[:, None]) if causal else np.ones((rows, clen), dtype=bool)
+    mask = np.concatenate([cache_mask, canvas_mask], axis=1)          # [R, L + C]
     for h in range(hq):
         g = (h * hkv) // hq
         keys = np.concatenate([k_cache[g], k_new[:, g, :]], axis=0)   # [L + C, dh]
@@ -239,12 +241,17 @@ def quantize_model_e4m3(model):
     norms and embedding stay in bf16.  Returns a new model dict (float64 arrays)."""
     out = dict(dims=dict(model["dims"], wdtype="e4m3"), layers=[])
     for lw in model["layers"]:
-        q = dict(lw)
-        for key, skey in (("w_gate_up", "s_gate_up"), ("w_down", "s_down"),
-                          ("ws_gate_up", "ss_gate_up"), ("ws_down", "ss_down")):
-            q[key], q[skey] = quantize_rows_e4m3(lw[key])
-        out["layers"].append(q)
+        out["layers"].append(quantize_layer_e4m3(lw))
     for key in ("embed", "final_norm"):
         out[key] = model[key]
     out["w_lm"], out["s_lm"] = quantize_rows_e4m3(model["w_lm"])
     return out
+
+
+def quantize_layer_e4m3(lw):
+    """One layer of the fp8 configuration (see quantize_model_e4m3)."""
+    q = dict(lw)
+    for key, skey in (("w_gate_up", "s_gate_up"), ("w_down", "s_down"),
+                      ("ws_gate_up", "ss_gate_up"), ("ws_down", "ss_down")):
+        q[key], q[skey] = quantize_rows_e4m3(lw[key])
+    return q

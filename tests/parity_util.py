@@ -9,6 +9,14 @@ import numpy as np
 
 # tolerances for hidden states, logits and entropies: bf16 inputs, fp32 accumulation
 REL_TOL = 2e-2
+# End-to-end bound for chained e4m3 stages (the stages themselves are held to REL_TOL from
+# identical inputs).  An e4m3 quantiser (relative step D <= 2^-3) fed two inputs that differ by
+# a relative d flips a code with probability ~ d / D, so its outputs differ by ~ sqrt(d D) in
+# RMS: more than d whenever d < D.  Chained through the layers, the two sides' differences
+# therefore grow towards the step D itself and no further (each side is within D / 2 of its own
+# unquantised values): per row 2 D, over the whole array D.
+FP8_CHAIN_TOL = 0.25
+FP8_CHAIN_ARRAY_TOL = 0.125
 
 
 def assert_close_rel(gpu, ref, rel=REL_TOL, what=""):

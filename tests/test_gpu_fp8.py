@@ -15,19 +15,12 @@ from block_diffusion_decoding_canvas_amd import driver, synth
 from oracle import model as om
 from oracle import sampler as osamp
 from oracle.numerics import e4m3_code, quantize_rows_e4m3, round_bf16
-from tests.parity_util import (argmax_certified, assert_close_rel, assert_entropy_close,
-                               compare_eb_step, entropy_sensitivity, entropy_tolerance,
-                               routing_certified)
+from tests.parity_util import (FP8_CHAIN_ARRAY_TOL, FP8_CHAIN_TOL, argmax_certified,
+                               assert_close_rel, assert_entropy_close, compare_eb_step,
+                               entropy_sensitivity, entropy_tolerance, routing_certified)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-# End-to-end bound for chained e4m3 stages.  An e4m3 quantiser (relative step D between 2^-4
-# and 2^-3) fed two inputs that differ by a relative d flips a code with probability ~ d / D,
-# so the quantised vectors differ by ~ sqrt(d D) in RMS.  With d = 2e-2 (the bf16 bar) that is
-# 5e-2 per quantised product; a layer chains two (expert input, SwiGLU output) and the LM head
-# one more, and the residual stream adds rather than multiplies them: 3 x 5e-2 per row.
-FP8_CHAIN_TOL = 0.15
-FP8_CHAIN_ARRAY_TOL = 0.08
 
 
 def _ffn_stages_on_oracle_states(dims, m64, c64, model, ws, canvas):

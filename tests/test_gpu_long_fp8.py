@@ -1,0 +1,281 @@
+"""Long-context batched fp8 configuration at full size, compared on sampled canvas rows.
+
+Model: the full-width layers (d 2816, 16/8 heads of 256, 128 experts top-8 + shared, inner 704)
+with e4m3 expert and LM-head weights, a 262,144-entry vocabulary, one sliding-window (1,024)
+layer followed by one global layer; 4 canvases of 256 tokens with N(0,1) caches of 131,072 /
+131,072 / 130,001 / 100,003 tokens.
+
+The oracle cannot take the global layer over every canvas row in seconds, so:
+  * every row goes through the windowed layer (its output makes the global layer's canvas keys);
+    a windowed query hides every cache position older than len - window + 1, and hidden keys add
+    exactly zero, so the oracle gets only the last window - 1 cache positions;
+  * sampled rows go through the global layer, the final norm and the LM head (rows are
+    independent given the keys and values).
+Stages from the oracle's own inputs are held to the stated tolerance (both FFNs and the LM head
+in fp8; the global layer in bf16, which isolates the 131K-key attention from e4m3 code flips);
+the chained fp8 step to the fp8 chain bound; integers exactly (renoised canvas, finalised
+argmax where certified).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_decoding_canvas_amd import driver, synth
+from oracle import model as om
+from oracle import sampler as osamp
+from oracle.numerics import quantize_rows_e4m3, round_bf16
+from tests.parity_util import (FP8_CHAIN_ARRAY_TOL, FP8_CHAIN_TOL, argmax_certified,
+                               assert_close_rel, assert_entropy_close, entropy_sensitivity,
+                               entropy_tolerance)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+LENS = (131072, 131072, 130001, 100003)
+ROWS = np.array([0, 1, 37, 100, 127, 128, 200, 255])      # sampled canvas positions
+SEED = 8
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def case():
+    dims = synth.dims_full(n_layers=2)
+    dims.update(window=1024, global_every=2)                 # layer 0 windowed, layer 1 global
+    B, C = len(LENS), dims["C"]
+    cap = max(LENS) + C
+    w = synth.make_model_device(dims, DEV, seed=5)
+    ids = list(range(B))
+    canvas = osamp.init_canvas(SEED, ids, C, dims["V"])
+    # host copies for the oracle (the same seeded values), before the model quantises in place
+    host = [{k: v.float().cpu().numpy() for k, v in lw.items()} for lw in w["layers"]]
+    emb = w["embed"][torch.from_numpy(canvas).to(DEV)].float().cpu().numpy().astype(np.float64)
+    w_lm = w["w_lm"].float().cpu().numpy()
+    fnorm = w["final_norm"].float().cpu().numpy().astype(np.float64)
+    wb = dict(dims=dict(dims), layers=[{k: v.clone() for k, v in lw.items()} for lw in w["layers"]],
+              embed=w["embed"], final_norm=w["final_norm"], w_lm=w["w_lm"].clone())
+    k, v = synth.make_cache_device(dims, B, cap, max(LENS), DEV, seed=6)
+    for b, n in enumerate(LENS):
+        k[:, b, :, n:] = 0
+        v[:, b, :, n:] = 0
+    kv = driver.KVCache(dims, B, cap, DEV, k, v, LENS)
+    log("device model and cache ready; quantising on the device")
+    model = driver.Model(w, wdtype="e4m3")
+    model_bf16 = driver.Model(wb)
+    ws = driver.workspace(max(model.workspace_bytes(B), model_bf16.workspace_bytes(B)))
+    torch.cuda.synchronize()
+    # the oracle's weights: e4m3 expert matrices (and the bf16 ones of layer 1), e4m3 LM head
+    f64 = [{kk: vv.astype(np.float64) for kk, vv in lw.items()} for lw in host]
+    del host
+    q_layers = [om.quantize_layer_e4m3(lw) for lw in f64]
+    w_lm_q, s_lm = quantize_rows_e4m3(w_lm)
+    del w_lm
+    log("oracle weights quantised")
+    win = dims["window"]                                     # layer 0: last window-1 positions
+    kc0 = np.zeros((B, dims["hkv"], win - 1, dims["dh"]), dtype=np.float32)
+    vc0 = np.zeros_like(kc0)
+    for b, n in enumerate(LENS):
+        kc0[b] = kv.k[0, b, :, n - win + 1:n].float().cpu().numpy()
+        vc0[b] = kv.v[0, b, :, n - win + 1:n].float().cpu().numpy()
+    kc1 = kv.k[1].float().cpu().numpy()
+    vc1 = kv.v[1].float().cpu().numpy()
+    return dict(dims=dims, B=B, C=C, cap=cap, canvas=canvas, ids=ids, emb=emb, fnorm=fnorm,
+                model=model, model_bf16=model_bf16, ws=ws, kv=kv, f64=f64, q=q_layers,
+                w_lm_q=w_lm_q, s_lm=s_lm, kc0=kc0, vc0=vc0, kc1=kc1, vc1=vc1)
+
+
+def _layer0_all_rows(c, layer_w, causal=False):
+    """Windowed layer 0 over every row: (state after attention, output, routing info, k, v)."""
+    d = c["dims"]
+    lens0 = np.array([d["window"] - 1] * c["B"])
+    h_mid, k, v = om.attention_block(c["emb"], layer_w, d, 0, c["kc0"], c["vc0"], lens0, causal)
+    h_out, info = om.ffn_block(h_mid, layer_w, d)
+    return h_mid, h_out, info, k, v
+
+
+def _layer1_rows(c, h1, layer_w):
+    """Global layer 1 for the sampled rows of every canvas: (state after attention, output)."""
+    d = c["dims"]
+    B, R = c["B"], len(ROWS)
+    u = om.rms_norm(h1, layer_w["attn_norm"], d["eps"])
+    q, k, v = om.split_qkv(u @ layer_w["w_qkv"].T, d)
+    h_mid = np.zeros((B, R, d["d"]))
+    for b, n in enumerate(LENS):
+        mask = om.visible_cache_mask(n, c["C"], 0)[ROWS]
+        o = om.attention(q[b, ROWS], c["kc1"][b, :, :n], c["vc1"][b, :, :n], k[b], v[b], mask,
+                         False, q_pos=ROWS)
+        h_mid[b] = h1[b, ROWS] + o.reshape(R, -1) @ layer_w["w_o"].T
+    h_out, info = om.ffn_block(h_mid, layer_w, d)
+    return h_mid, h_out, info
+
+
+def _gpu_ffn(c, layer, h_full_rows):
+    """GPU FFN (fp8 model) on a [B*C, d] fp32 state; returns (new state, router logits)."""
+    d = c["dims"]
+    T = c["B"] * c["C"]
+    hg = torch.from_numpy(h_full_rows.reshape(T, -1).astype(np.float32)).to(DEV)
+    rl = torch.zeros((T, d["E"]), dtype=torch.float32, device=DEV)
+    driver.ffn_forward(c["model"], layer, c["B"], hg, c["ws"], rl)
+    torch.cuda.synchronize()
+    return hg.cpu().numpy().astype(np.float64), rl.cpu().numpy()
+
+
+def _certified(r_ref, r_gpu, k):
+    rerr = np.abs(r_gpu - r_ref).max()
+    srt = -np.sort(-r_ref, axis=1)
+    return (srt[:, k - 1] - srt[:, k]) > 4 * rerr + 1e-7
+
+
+def _sel(x):
+    """[B, C, ...] -> the sampled rows [B * R, ...]."""
+    return x[:, ROWS].reshape((-1,) + x.shape[2:])
+
+
+@pytest.fixture(scope="module")
+def oracle_fwd(case):
+    c = case
+    log("oracle: windowed layer over all rows")
+    h0m, h1, info0, _, _ = _layer0_all_rows(c, c["q"][0])
+    log("oracle: global layer over sampled rows")
+    h1m, h2, info1 = _layer1_rows(c, h1, c["q"][1])
+    z64 = om.linear(om.rms_norm(h2, c["fnorm"], c["dims"]["eps"]), c["w_lm_q"], c["s_lm"])
+    return dict(h0m=h0m, h1=h1, h1m=h1m, h2=h2, z64=z64.reshape(-1, z64.shape[-1]),
+                info0=info0, info1=info1)
+
+
+def test_long_fp8_stages(case, oracle_fwd):
+    c, o = case, oracle_fwd
+    d, k = c["dims"], c["dims"]["top_k"]
+    T = c["B"] * c["C"]
+    # fp8 FFN of the windowed layer, every row, from the oracle's post-attention state
+    hg, rl = _gpu_ffn(c, 0, o["h0m"])
+    cert = _certified(o["info0"]["router_logits"], rl, k)
+    assert cert.sum() >= T // 4
+    h_in = o["h0m"].reshape(T, -1).astype(np.float32).astype(np.float64)
+    assert_close_rel((hg - h_in)[cert], (o["h1"] - o["h0m"]).reshape(T, -1)[cert],
+                     what="fp8 FFN layer 0")
+    log(f"layer 0 FFN: certified {cert.sum()}/{T}")
+    # fp8 FFN of the global layer at the sampled rows (other rows: the layer's input)
+    h_fill = o["h1"].copy()
+    h_fill[:, ROWS] = o["h1m"]
+    hg, rl = _gpu_ffn(c, 1, h_fill)
+    hg = hg.reshape(c["B"], c["C"], -1)[:, ROWS].reshape(-1, d["d"])
+    rl = rl.reshape(c["B"], c["C"], -1)[:, ROWS].reshape(-1, d["E"])
+    cert = _certified(o["info1"]["router_logits"], rl, k)
+    h_in = o["h1m"].reshape(-1, d["d"]).astype(np.float32).astype(np.float64)
+    assert_close_rel((hg - h_in)[cert], (o["h2"] - o["h1m"]).reshape(-1, d["d"])[cert],
+                     what="fp8 FFN layer 1 (sampled rows)")
+    log(f"layer 1 FFN: certified {cert.sum()}/{len(cert)}")
+    # the global layer over the 131K-key caches in bf16, from the oracle's bf16 layer input
+    h0m_b, h1_b, _, _, _ = _layer0_all_rows(c, c["f64"][0])
+    h1m_b, h2_b, info_b = _layer1_rows(c, h1_b, c["f64"][1])
+    hg = torch.from_numpy(h1_b.reshape(T, -1).astype(np.float32)).to(DEV)
+    rl = torch.zeros((T, d["E"]), dtype=torch.float32, device=DEV)
+    driver.layer_forward(c["model_bf16"], c["kv"], 1, 0, hg, c["ws"], rl)
+    torch.cuda.synchronize()
+    hg = hg.cpu().numpy().astype(np.float64).reshape(c["B"], c["C"], -1)[:, ROWS].reshape(-1, d["d"])
+    rl = rl.cpu().numpy().reshape(c["B"], c["C"], -1)[:, ROWS].reshape(-1, d["E"])
+    cert = _certified(info_b["router_logits"], rl, k)
+    h_in = _sel(h1_b).astype(np.float32).astype(np.float64)
+    assert_close_rel((hg - h_in)[cert], (h2_b.reshape(-1, d["d"]) - _sel(h1_b))[cert],
+                     what="bf16 global layer over 131K-key caches (sampled rows)")
+    log(f"bf16 global layer: certified {cert.sum()}/{len(cert)}")
+    # fp8 LM head from the oracle's final state (other rows: zeros)
+    h_fin = np.zeros((c["B"], c["C"], d["d"]))
+    h_fin[:, ROWS] = o["h2"]
+    out = driver.StepOut(c["B"], c["C"], d["V"], DEV)
+    p = driver.eb_params(seed=SEED)
+    driver.lm_head_forward(c["model"], c["B"], torch.from_numpy(
+        h_fin.reshape(T, -1).astype(np.float32)).to(DEV), 47, p, out, c["ws"])
+    torch.cuda.synchronize()
+    zg = _sel(out.logits.float().cpu().numpy())
+    assert_close_rel(zg, round_bf16(o["z64"]), what="fp8 LM head (sampled rows)")
+    log("LM head stage ok")
+
+
+def test_long_fp8_decoder_steps(case, oracle_fwd):
+    c, o = case, oracle_fwd
+    d = c["dims"]
+    params = osamp.default_params()
+    p = driver.eb_params_from_dict(params, SEED)
+    zr = round_bf16(o["z64"])
+    logits = {}
+    for step in (47, 0):
+        gs = driver.SamplerState(c["B"], c["C"], DEV, canvas_ids=c["ids"])
+        gs.load_host(osamp.new_state(c["canvas"]))
+        out = driver.StepOut(c["B"], c["C"], d["V"], DEV)
+        driver.decoder_step(c["model"], c["kv"], step, p, gs, out, c["ws"])
+        torch.cuda.synchronize()
+        logits[step] = out.logits.clone()
+        zg = _sel(out.logits.float().cpu().numpy())
+        rel = np.linalg.norm(zg - zr, axis=1) / np.linalg.norm(zr, axis=1)
+        log(f"step {step}: sampled logits worst row rel err {rel.max():.2e}, "
+            f"median {np.median(rel):.2e}")
+        assert_close_rel(zg, zr, rel=FP8_CHAIN_TOL, what=f"fp8 logits step {step}")
+        assert np.linalg.norm(zg - zr) <= FP8_CHAIN_ARRAY_TOL * np.linalg.norm(zr)
+        inv_t = osamp.inv_temperature_f32(step, params["max_steps"])
+        h_ref, a_ref = osamp.entropy_argmax(zr, inv_t)
+        dz = np.abs(zg - o["z64"]).max(axis=1)
+        tol = entropy_tolerance(h_ref, dz * float(inv_t), entropy_sensitivity(o["z64"], inv_t))
+        h_all = out.entropy.cpu().numpy()
+        assert_entropy_close(_sel(h_all), h_ref, f"entropy step {step}", tol)
+        a_all = out.argmax.cpu().numpy()
+        for i, (ag, ar) in enumerate(zip(_sel(a_all), a_ref)):
+            if ag != ar:
+                assert not argmax_certified(o["z64"][i], dz[i]), f"argmax row {i}"
+        g = gs.host()
+        if step == 47:
+            # last step: every position is finalised to its argmax; every canvas is done
+            assert g["done"].all() and g["committed"].all()
+            assert np.array_equal(g["canvas"], a_all)
+        else:
+            # random weights: every entropy is far above the bound, so nothing commits and every
+            # position is renoised from Philox with step tag 0
+            assert h_all.min() > params["entropy_bound"]
+            assert not out.commit_now.cpu().numpy().any()
+            want = np.stack([osamp.uniform_tokens(SEED, cid, 0, np.arange(c["C"]), d["V"])
+                             for cid in c["ids"]])
+            assert np.array_equal(g["canvas"], want)
+    # the logits do not depend on the step: bitwise equal across the two runs
+    assert torch.equal(logits[47], logits[0])
+
+
+def test_long_fp8_append(case, oracle_fwd):
+    c = case
+    d, kv = c["dims"], c["kv"]
+    B, C = c["B"], c["C"]
+    T = B * C
+    tokens = c["canvas"]
+    # layer 1's appended keys/values from the oracle's own encoder input, at the stated tolerance
+    _, h1_enc, _, k0, v0 = _layer0_all_rows(c, c["q"][0], causal=True)
+    hg = torch.from_numpy(h1_enc.reshape(T, -1).astype(np.float32)).to(DEV)
+    driver.layer_forward(c["model"], kv, 1, 1, hg, c["ws"])
+    torch.cuda.synchronize()
+    u = om.rms_norm(h1_enc, c["q"][1]["attn_norm"], d["eps"])
+    _, k1, v1 = om.split_qkv(u @ c["q"][1]["w_qkv"].T, d)
+    for b, n in enumerate(LENS):
+        assert_close_rel(kv.k[1, b, :, n:n + C].float().cpu().numpy(), k1[b].transpose(1, 0, 2),
+                         what=f"layer 1 K from the oracle's encoder state, canvas {b}")
+        assert_close_rel(kv.v[1, b, :, n:n + C].float().cpu().numpy(), v1[b].transpose(1, 0, 2),
+                         what=f"layer 1 V, canvas {b}")
+    # the chained append: layer 0 at the stated tolerance (its input is the embedding), layer 1
+    # at the fp8 chain bound; entries before len untouched; len advanced
+    before = kv.k[1, :, :, LENS[3] - 5:LENS[3]].clone()
+    driver.kv_append_canvas(c["model"], kv, torch.from_numpy(tokens.astype(np.int32)).to(DEV),
+                            c["ws"])
+    torch.cuda.synchronize()
+    try:
+        assert kv.lengths() == [n + C for n in LENS]
+        for b, n in enumerate(LENS):
+            assert_close_rel(kv.k[0, b, :, n:n + C].float().cpu().numpy(),
+                             k0[b].transpose(1, 0, 2), what=f"appended layer 0 K, canvas {b}")
+            assert_close_rel(kv.v[0, b, :, n:n + C].float().cpu().numpy(),
+                             v0[b].transpose(1, 0, 2), what=f"appended layer 0 V, canvas {b}")
+            assert_close_rel(kv.k[1, b, :, n:n + C].float().cpu().numpy(),
+                             k1[b].transpose(1, 0, 2), rel=FP8_CHAIN_TOL,
+                             what=f"appended layer 1 K, canvas {b}")
+        assert torch.equal(before, kv.k[1, :, :, LENS[3] - 5:LENS[3]])
+    finally:
+        for b, n in enumerate(LENS):
+            kv.len[b] = n

@@ -244,3 +244,19 @@ def test_window_mask_brute_force():
         for i in range(c):
             for j in range(n):
                 assert m[i, j] == (abs((n + i) - j) < w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_query_subset_equals_full_rows(causal):
+    """Attention of a subset of canvas queries (given their positions) equals those rows of the
+    full result: rows are independent given the keys and values."""
+    rng = np.random.default_rng(9)
+    C, L, hq, hkv, dh = 12, 20, 4, 2, 8
+    q = rng.standard_normal((C, hq, dh))
+    kc, vc = rng.standard_normal((hkv, L, dh)), rng.standard_normal((hkv, L, dh))
+    kn, vn = rng.standard_normal((C, hkv, dh)), rng.standard_normal((C, hkv, dh))
+    mask = om.visible_cache_mask(L, C, 16)
+    full = om.attention(q, kc, vc, kn, vn, mask, causal)
+    rows = np.array([0, 3, 7, 11])
+    sub = om.attention(q[rows], kc, vc, kn, vn, mask[rows], causal, q_pos=rows)
+    assert np.array_equal(sub, full[rows])
