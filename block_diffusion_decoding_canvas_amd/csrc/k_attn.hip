@@ -96,20 +96,50 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
   const int win_lo = len + qi - a.window + 1;  // first visible cache position (windowed layers)
 
+  // wave-uniform range of this wave's canvas positions (tiles that no query of the wave sees
+  // partially are processed without per-element masks)
+  int qi_lo = qi, qi_hi = qi;
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    qi_lo = min(qi_lo, __shfl_xor(qi_lo, o2, 64));
+    qi_hi = max(qi_hi, __shfl_xor(qi_hi, o2, 64));
+  }
+  qi_lo = __builtin_amdgcn_readfirstlane(qi_lo);
+  qi_hi = __builtin_amdgcn_readfirstlane(qi_hi);
+
   // staging items: (key pair p, dh chunk c): two keys' rows of K, and of V written transposed;
   // the next tile's rows are prefetched into registers while the current one is computed
+  constexpr int ITEMS_ALL = (KT / 2) * (DH / 8);
   u32x4 pk0[IT], pk1[IT], pv0[IT], pv1[IT];
   auto key_ptr = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
     return kk < nc ? cache + static_cast<long long>(c_lo + kk) * DH
                    : canvas + static_cast<long long>(kk - nc) * ldqkv;
   };
   auto fetch = [&](int tt) __attribute__((always_inline)) {
+    const int kt0 = tt * KT;
+    if (kt0 + KT <= nc) {
+      // every key of the tile is a cache row: two consecutive rows per item
+      const long long base = static_cast<long long>(c_lo + kt0) * DH;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int idx = tid + it * NTHR;
+        const int pp = idx % (KT / 2), c = idx / (KT / 2);
+        const long long off = base + static_cast<long long>(2 * pp) * DH + c * 8;
+        if (idx < ITEMS_ALL) {
+          pk0[it] = ld16(kcache + off);
+          pk1[it] = ld16(kcache + off + DH);
+          pv0[it] = ld16(vcache + off);
+          pv1[it] = ld16(vcache + off + DH);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = tid + it * NTHR;
-      const bool on = idx < (KT / 2) * (DH / 8);
-      const int p = idx % (KT / 2), c = idx / (KT / 2);
-      const int k0 = tt * KT + 2 * p;
+      const bool on = idx < ITEMS_ALL;
+      const int pp = idx % (KT / 2), c = idx / (KT / 2);
+      const int k0 = kt0 + 2 * pp;
       pk0[it] = pk1[it] = pv0[it] = pv1[it] = zero4;
       if (on && k0 < nk) {
         pk0[it] = ld16(key_ptr(k0, kcache, kcanvas) + c * 8);
@@ -125,22 +155,23 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = tid + it * NTHR;
-      if (idx >= (KT / 2) * (DH / 8)) continue;
-      const int p = idx % (KT / 2), c = idx / (KT / 2);
-      st16(ks + (2 * p) * C::KS_STRIDE + c * 8, pk0[it]);
-      st16(ks + (2 * p + 1) * C::KS_STRIDE + c * 8, pk1[it]);
+      if (idx >= ITEMS_ALL) continue;
+      const int pp = idx % (KT / 2), c = idx / (KT / 2);
+      st16(ks + (2 * pp) * C::KS_STRIDE + c * 8, pk0[it]);
+      st16(ks + (2 * pp + 1) * C::KS_STRIDE + c * 8, pk1[it]);
       // V^T[dh][key]: each 32-bit store holds keys 2p and 2p+1 of one dh
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t a0 = pv0[it][e], a1 = pv1[it][e];
-        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e) * C::VT_STRIDE) + p;
-        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + p;
-        *row0 = (a0 & 0xffffu) | (a1 << 16);
-        *row1 = (a0 >> 16) | (a1 & 0xffff0000u);
+        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e) * C::VT_STRIDE) + pp;
+        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + pp;
+        *row0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // low halves: key 2p, key 2p+1
+        *row1 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // high halves
       }
     }
   };
 
+  const float sc = a.scale_log2e;
   // the next tile's K/V rows are fetched into registers while the current tile is computed
   if (t_beg < t_end) fetch(t_beg);
   for (int tt = t_beg; tt < t_end; ++tt) {
@@ -150,7 +181,7 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
     __syncthreads();
     if (tt + 1 < t_end) fetch(tt + 1);
 
-  // S^T[key][q] for 4 sub-tiles of 16 keys
+    // S^T[key][q] for 4 sub-tiles of 16 keys (raw dot products)
     f32x4 s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -162,45 +193,60 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
         s[nt] = mfma16x16x32(kf, qf[ks_], s[nt]);
       }
     }
-    // scale, mask, running max (lane's query = r16; its keys: nt*16 + 4 lg + j)
+    // visibility: a tile inside the canvas or inside the cache that every query of this wave
+    // sees entirely needs no per-element mask (the lane's keys: nt*16 + 4 lg + j)
+    const bool in_cache = kbase + KT <= nc;
+    const bool full =
+        kbase + KT <= nk &&
+        (in_cache ? (a.window == 0 || c_lo + kbase >= len + qi_hi - a.window + 1)
+                  : (kbase >= nc && (!a.causal || kbase + KT - 1 - nc <= qi_lo)));
     float tmax = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 4; ++nt)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = kbase + nt * 16 + 4 * lg + j;
-        bool vis = kk < nk;
-        if (kk < nc) {
-          if (a.window > 0) vis = vis && (c_lo + kk >= win_lo);
-        } else if (a.causal) {
-          vis = vis && (kk - nc <= qi);
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kk = kbase + nt * 16 + 4 * lg + j;
+          bool vis = kk < nk;
+          if (kk < nc) {
+            if (a.window > 0) vis = vis && (c_lo + kk >= win_lo);
+          } else if (a.causal) {
+            vis = vis && (kk - nc <= qi);
+          }
+          s[nt][j] = vis ? s[nt][j] : -INFINITY;
+          tmax = fmaxf(tmax, s[nt][j]);
         }
-        const float v = vis ? s[nt][j] * a.scale_log2e : -INFINITY;
-        s[nt][j] = v;
-        tmax = fmaxf(tmax, v);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    // running max in scaled (log2) units; the scale is > 0, so it commutes with the max
+    const float m_new = fmaxf(m_run, tmax * sc);
+    const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run + neg_m);   // m_run = -inf: 0
     m_run = m_new;
-    l_run *= alpha;
+    // rescale only when some lane's maximum moved (a wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+    }
     u32x4 pb[2];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
-      float p[8];
+      f32x4 lo, hi;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = (m_new == -INFINITY) ? 0.f : exp2f(s[2 * kp][j] - m_new);
-        p[4 + j] = (m_new == -INFINITY) ? 0.f : exp2f(s[2 * kp + 1][j] - m_new);
+        lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kp][j], sc, neg_m));
+        hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kp + 1][j], sc, neg_m));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) l_run += p[j];
-      pb[kp] = u32x4{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
-                     pack_bf2(p[6], p[7])};
+      l_run += (lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]);
+      pb[kp] = u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
+                     cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])};
     }
     // O^T[dh][q] += V^T[dh][keys] P^T[keys][q]; the B operand's 8 keys per lane are
     // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}; the A operand reads the same keys
