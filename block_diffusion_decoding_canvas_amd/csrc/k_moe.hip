@@ -73,12 +73,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
                 "segment must hold whole ring groups");
   __shared__ __align__(16) uint8_t xs_lds[2][MT * STRIDE];
 
+  // logical slot -> (token tile, k split, row block).  Consecutive slots run on one XCD (one L2):
+  // grouped products put a tile's row blocks together (its gathered token rows are shared);
+  // dense products put the token tiles of one row block together, so every weight band is
+  // fetched from HBM into one L2 and reused there by all token tiles
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
-  const int nb = slot % a.n_nblk;
-  const int tk = slot / a.n_nblk;
-  const int ks = tk % a.ksplit;
-  const int tile = tk / a.ksplit;
-  if (tile >= a.grid_tiles) return;
+  int nb, ks, tile;
+  if (a.chunks) {
+    nb = slot % a.n_nblk;
+    const int tk = slot / a.n_nblk;
+    ks = tk % a.ksplit;
+    tile = tk / a.ksplit;
+  } else {
+    tile = slot % a.grid_tiles;
+    const int rest = slot / a.grid_tiles;
+    ks = rest % a.ksplit;
+    nb = rest / a.ksplit;
+  }
+  if (tile >= a.grid_tiles || nb >= a.n_nblk) return;
   int expert = 0, row0, nrows;
   if (a.chunks) {
     if (tile >= *a.n_chunks) return;
