@@ -77,7 +77,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   // grouped products put a tile's row blocks together (its gathered token rows are shared);
   // dense products put the token tiles of one row block together, so every weight band is
   // fetched from HBM into one L2 and reused there by all token tiles
-  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  int slot;
+  if (a.chunks) {
+    // the grid is sized for the most tiles a routing can produce; the active slots (known only
+    // on the device) are spread evenly over the 8 XCDs, a contiguous run on each
+    const int n_active = *a.n_chunks * a.ksplit * a.n_nblk;
+    const int per = (n_active + 7) >> 3;
+    const int j = blockIdx.x >> 3;
+    slot = (blockIdx.x & 7) * per + j;
+    if (j >= per || slot >= n_active) return;
+  } else {
+    slot = xcd_remap(blockIdx.x, gridDim.x);
+  }
   int nb, ks, tile;
   if (a.chunks) {
     nb = slot % a.n_nblk;
@@ -140,36 +151,42 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 1024 + lane * 16;
   }
 
-  // token staging: thread loads XL 16-byte pieces of the MT x SEG segment
+  // token staging: thread loads XL 16-byte pieces of the MT x SEG segment.  Every load is issued
+  // unconditionally from an in-range address (rows past the tile read its last row, k past the
+  // range reads the range's last piece) and masked afterwards: conditional loads would make the
+  // compiler wait for every outstanding load (the weight ring included) before the LDS store.
   const uint8_t* X = reinterpret_cast<const uint8_t*>(a.X);
   const uint8_t* xsrc[XL];
   int xdst[XL], xcol[XL];
+  uint32_t xrow_mask[XL];
 #pragma unroll
   for (int it = 0; it < XL; ++it) {
     const int idx = tid + it * NTHR;
     const int r = idx / (SEGB / 16), c16 = idx % (SEGB / 16);
     const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
     const int xr = a.x_rows ? a.x_rows[rr] : rr;
-    xsrc[it] = X + (static_cast<long long>(xr) * a.ldx) * EB + c16 * 16;
+    xsrc[it] = X + (static_cast<long long>(xr) * a.ldx) * EB;
     xdst[it] = r * STRIDE + c16 * 16;
     xcol[it] = c16 * (16 / EB);
+    xrow_mask[it] = r < nrows ? 0xffffffffu : 0u;   // rows past the tile are zero-filled
   }
   const int nseg = (k_end - k_beg + SEG - 1) / SEG;
   u32x4 xr_[XL];
+  uint32_t xm_[XL];                          // mask of the pieces in flight, applied at the store
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // rows past the tile are zero-filled rather than loaded
-  bool xrow_live[XL];
-#pragma unroll
-  for (int it = 0; it < XL; ++it) xrow_live[it] = (tid + it * NTHR) / (SEGB / 16) < nrows;
   auto load_seg = [&](int sg) __attribute__((always_inline)) {
     const int k0 = k_beg + sg * SEG;
 #pragma unroll
-    for (int it = 0; it < XL; ++it)
-      xr_[it] = (xrow_live[it] && k0 + xcol[it] < k_end) ? ld16(xsrc[it] + k0 * EB) : zero4;
+    for (int it = 0; it < XL; ++it) {
+      const int k = k0 + xcol[it];
+      const int kc = min(k, k_end - 16 / EB);
+      xr_[it] = ld16(xsrc[it] + static_cast<long long>(kc) * EB);
+      xm_[it] = k < k_end ? xrow_mask[it] : 0u;
+    }
   };
   auto store_seg = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it]);
+    for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it] & xm_[it]);
   };
 
   f32x4 acc[2][NTB];
@@ -198,40 +215,57 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   const int nsteps = s_last - s_first;
+  // one step: the token fragments of step s from LDS, the MFMAs with ring stage q (zero weights
+  // when the step is past the end), then the ring stage refilled with step s + PS
+  auto step = [&](const uint8_t* xb, int s, int s_beg, int q, bool live)
+      __attribute__((always_inline)) {
+    const int kin = (s - s_beg) * 64 + g * 16;   // byte offset in the staged row
+    u32x4 b[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
+    const u32x4 w0 = live ? wst[q][0] : zero4;
+    const u32x4 w1 = live ? wst[q][1] : zero4;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      if constexpr (F8) {
+        acc[0][tb] = mfma_fp8_pair(w0, b[tb], acc[0][tb]);
+        acc[1][tb] = mfma_fp8_pair(w1, b[tb], acc[1][tb]);
+      } else {
+        acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
+        acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(s + PS, wst[q]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   for (int sg = 0; sg < nseg; ++sg) {
     const uint8_t* xb = xs_lds[sg & 1];
     const int s_beg = sg * SSTEPS;
-    // waves past the last output row skip the stream (they only join the barriers)
-    const int s_end = wave_live ? min(nsteps, s_beg + SSTEPS) : s_beg;
-    for (int s0 = s_beg; s0 < s_end; s0 += PS) {
+    if (wave_live && s_beg + SSTEPS <= nsteps) {
+      // a full segment as straight-line code: the only loop-carried loads are then the token
+      // pieces issued at the end of the previous segment, which are older than this segment's
+      // weight loads, so the store below waits for them alone and the ring stays in flight
 #pragma unroll
-      for (int q = 0; q < PS; ++q) {
-        const int s = s0 + q;                 // s0 is a multiple of PS: stage q holds step s
-        const bool live = s < s_end;          // steps past the end: stale (finite) data, zero weights
-        const int kin = (s - s_beg) * 64 + g * 16;   // byte offset in the staged row
-        u32x4 b[NTB];
+      for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
+      if (sg + 1 < nseg) {
+        store_seg((sg + 1) & 1);
+        if (sg + 2 < nseg) load_seg(sg + 2);
+      }
+    } else {
+      // the last, partial segment (or a wave past the last output row, which only joins the
+      // barriers)
+      const int s_end = wave_live ? min(nsteps, s_beg + SSTEPS) : s_beg;
+      for (int s0 = s_beg; s0 < s_end; s0 += PS) {
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
-        const u32x4 w0 = live ? wst[q][0] : zero4;
-        const u32x4 w1 = live ? wst[q][1] : zero4;
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          if constexpr (F8) {
-            acc[0][tb] = mfma_fp8_pair(w0, b[tb], acc[0][tb]);
-            acc[1][tb] = mfma_fp8_pair(w1, b[tb], acc[1][tb]);
-          } else {
-            acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
-            acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        load_step(s + PS, wst[q]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < PS; ++q) step(xb, s0 + q, s_beg, q, s0 + q < s_end);
+      }
+      if (sg + 1 < nseg) {
+        store_seg((sg + 1) & 1);
+        if (sg + 2 < nseg) load_seg(sg + 2);
       }
     }
     if (sg + 1 < nseg) {
-      store_seg((sg + 1) & 1);
-      if (sg + 2 < nseg) load_seg(sg + 2);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
