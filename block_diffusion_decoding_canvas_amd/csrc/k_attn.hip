@@ -306,15 +306,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int sp = 0; sp < a.n_split; ++sp) mmax = fmaxf(mmax, a.ml_part[(sp * stride + row) * 2]);
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < a.n_split; ++sp) {
-    const float m = a.ml_part[(sp * stride + row) * 2];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mmax);
-    l += w * a.ml_part[(sp * stride + row) * 2 + 1];
-    const float4 v = *reinterpret_cast<const float4*>(a.o_part + (sp * stride + row) * DH + c4);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  // splits merged in split order; each group of 8 is loaded together (clamped split index,
+  // zero weight past the last split)
+  for (int sp0 = 0; sp0 < a.n_split; sp0 += 8) {
+    float2 ml[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const long long r2 = static_cast<long long>(min(sp0 + u, a.n_split - 1)) * stride + row;
+      ml[u] = *reinterpret_cast<const float2*>(a.ml_part + r2 * 2);
+      v[u] = *reinterpret_cast<const float4*>(a.o_part + r2 * DH + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (sp0 + u < a.n_split) {  // uniform; the loads above are already in flight
+        const float m = ml[u].x;
+        const float w = (m == -INFINITY) ? 0.f : exp2f(m - mmax);
+        l += w * ml[u].y;
+        acc.x += w * v[u].x;
+        acc.y += w * v[u].y;
+        acc.z += w * v[u].z;
+        acc.w += w * v[u].w;
+      }
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int r = static_cast<int>(row % R);

@@ -441,7 +441,7 @@ hipError_t launch_moe_down_fp8(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_BF16, 2, 512, 4, 4, true>(a, s);
 }
 hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_LMHEAD, 16, 256, 8, 4, true>(a, s);
+  return launch_stream<EPI_LMHEAD, 8, 256, 8, 4, true>(a, s);
 }
 
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {

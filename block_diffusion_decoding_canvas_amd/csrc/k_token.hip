@@ -118,9 +118,17 @@ __global__ __launch_bounds__(256) void k_topk(const float* logits, int ksplit, i
     const int e = lane + 64 * k;
     float x = -INFINITY;
     if (e < n_exp) {
+      // the k-split partial planes, summed in plane order; groups of 8 loads are issued
+      // together (clamped plane index, zero weight past the last plane)
       x = 0.f;
-      for (int sp = 0; sp < ksplit; ++sp)
-        x += logits[(static_cast<long long>(sp) * ntok + t) * n_exp + e];
+      for (int sp0 = 0; sp0 < ksplit; sp0 += 8) {
+        float part[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          part[u] = logits[(static_cast<long long>(min(sp0 + u, ksplit - 1)) * ntok + t) * n_exp + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x += (sp0 + u < ksplit) ? part[u] : 0.f;
+      }
       if (logits_out) logits_out[static_cast<long long>(t) * n_exp + e] = x;
     }
     v[k] = x;
@@ -289,12 +297,23 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* h, const float* part,
   float ss = 0.f;
   for (int c = threadIdx.x * 4; c < d; c += 1024) {
     float4 acc = *reinterpret_cast<const float4*>(x + c);
-    for (int sp = 0; sp < ksplit; ++sp) {
-      const float4 p = *reinterpret_cast<const float4*>(part + sp * plane + static_cast<long long>(t) * d + c);
-      acc.x += p.x;
-      acc.y += p.y;
-      acc.z += p.z;
-      acc.w += p.w;
+    // the k-split partial planes, added in plane order; each group of 4 loads is issued
+    // together (clamped plane index, zero weight past the last plane)
+    for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
+      float4 p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        p[u] = *reinterpret_cast<const float4*>(part + min(sp0 + u, ksplit - 1) * plane +
+                                                static_cast<long long>(t) * d + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (sp0 + u < ksplit) {   // uniform; the loads above are already in flight
+          acc.x += p[u].x;
+          acc.y += p[u].y;
+          acc.z += p[u].z;
+          acc.w += p[u].w;
+        }
+      }
     }
     *reinterpret_cast<float4*>(x + c) = acc;
     ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
