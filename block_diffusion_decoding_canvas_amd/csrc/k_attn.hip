@@ -363,7 +363,7 @@ int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys) {
   const int R = (Hq / Hkv) * C;
   const int base = B * Hkv * ((R + QB - 1) / QB);
   const int ntiles = (max_keys + KT - 1) / KT;
-  int n = (512 + base - 1) / base;
+  int n = (256 + base - 1) / base;
   n = std::min(n, std::max(1, ntiles / 2));
   n = std::min(n, std::max(1, 1024 / base));
   return std::max(1, n);
