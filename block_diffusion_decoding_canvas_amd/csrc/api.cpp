@@ -420,6 +420,7 @@ struct DecWs {
   float* act32;       // [T k + T][max(F, Fs)] fp32 SwiGLU output
   uint8_t* act8;      // its e4m3 codes
   float* act8s;       // [T k + T] row scales
+  uint8_t* hot;       // 1 KiB read by the streaming kernels' past-the-end loads (never used)
 };
 
 int attn_base_blocks(const dg_dims& d, int B) {
@@ -455,6 +456,7 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
   w.act = c.take<uint16_t>(rows * fmax);
   w.y = c.take<uint16_t>(rows * d.d_model);
   w.eb = carve_eb(c, static_cast<int>(T), d.vocab / dg::gemm_lmhead_rows_per_block(), d.vocab);
+  w.hot = c.take<uint8_t>(1024);
   w.u8 = nullptr; w.u8s = nullptr; w.act32 = nullptr; w.act8 = nullptr; w.act8s = nullptr;
   if (d.wdtype == DG_FP8_E4M3) {
     w.u8 = c.take<uint8_t>(T * d.d_model);
@@ -509,6 +511,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
 
   dg::WGemmArgs g;
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   // QKV projection
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_qkv);
   g.K = g.K_sh = d.d_model; g.N = g.N_sh = dq; g.ntok = T; g.out = w.qkv; g.ldo = dq; g.ksplit = 1;
@@ -540,6 +543,7 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecW
 
   // output projection (k-split partials) + residual + pre-FFN norm
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   g.X = w.attn; g.ldx = d.n_q_heads * d.head_dim; g.W = static_cast<const uint16_t*>(lw.w_o);
   g.K = g.K_sh = d.n_q_heads * d.head_dim; g.N = g.N_sh = d.d_model; g.ntok = T;
   g.out = w.proj_part; g.ldo = d.d_model; g.ksplit = kOProjSplit;
@@ -562,6 +566,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   dg::WGemmArgs g;
   // router
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(lw.w_router);
   g.K = g.K_sh = d.d_model; g.N = g.N_sh = d.n_experts; g.ntok = T;
   g.out = w.router_part; g.ldo = d.n_experts; g.ksplit = kRouterSplit;
@@ -577,6 +582,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   // routed + shared experts: gate/up with SwiGLU, then down
   const int fmax = std::max(d.ffn_inner, d.shared_inner);
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   g.X = w.u; g.ldx = d.d_model; g.x_rows = w.perm;
   g.W = static_cast<const uint16_t*>(lw.w_gate_up);
   g.w_estride = 2LL * d.ffn_inner * d.d_model;
@@ -598,6 +604,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
     DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, s));
   }
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   g.X = w.act; g.ldx = fmax; g.W = static_cast<const uint16_t*>(lw.w_down);
   g.w_estride = static_cast<long long>(d.d_model) * d.ffn_inner;
   g.W_sh = static_cast<const uint16_t*>(lw.ws_down);
@@ -630,6 +637,7 @@ dg_status run_lm_head(const dg_model* m, int T, DecWs& w, uint16_t* logits, floa
   const dg_dims& d = m->dims;
   dg::WGemmArgs g;
   memset(&g, 0, sizeof(g));
+  g.hot = w.hot;
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(m->w_lm);
   g.K = g.K_sh = d.d_model; g.N = g.N_sh = d.vocab; g.ntok = T; g.out = logits;
   g.ldo = d.vocab; g.ksplit = 1; g.inv_t_log2e = inv_t_log2e; g.part = w.eb.part;

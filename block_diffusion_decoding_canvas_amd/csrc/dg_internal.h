@@ -195,6 +195,9 @@ struct WGemmArgs {
   const float* w_scale;   // [experts][weight rows]
   long long wsc_estride;  // scales between experts
   const float* w_scale_sh;
+  // 1 KiB of readable device memory (workspace) that the weight ring's past-the-end loads read
+  // instead of weights; its contents are never used
+  const uint8_t* hot;
 };
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };

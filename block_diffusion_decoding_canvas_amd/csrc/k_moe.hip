@@ -195,20 +195,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) acc[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight ring: local step s (global step s_first + s) lives in stage s % PS
+  // weight ring: local step s (global step s_first + s) lives in stage s % PS.  Steps past the
+  // end (the ring's last refills) still issue their loads, so that the loads stay straight-line,
+  // but from a 1 KiB block that stays L2-resident instead of re-reading a weight fragment from
+  // HBM; their data is replaced by zeros when used
   u32x4 wst[PS][2];
+  const uint8_t* hot = a.hot ? a.hot + lane * 16
+                            : wfrag[0] + static_cast<long long>(max(s_last - 1, 0)) * 1024;
   auto load_step = [&](int s, u32x4 (&w)[2]) __attribute__((always_inline)) {
-    const int sc = min(s_first + s, max(s_last - 1, 0));  // past the end: reload (zeroed later)
-    w[0] = ld_nt(wfrag[0] + sc * 1024);
-    w[1] = ld_nt(wfrag[1] + sc * 1024);
+    const bool in = s_first + s < s_last;
+    const long long off = static_cast<long long>(s_first + s) * 1024;
+    w[0] = ld_nt(in ? wfrag[0] + off : hot);
+    w[1] = ld_nt(in ? wfrag[1] + off : hot);
   };
 
   if (nseg > 0) {
-    load_seg(0);
+    // the weight ring first: it depends only on the tile's expert, while the token pieces may
+    // wait for the gathered row indices
     if (wave_live) {
 #pragma unroll
       for (int q = 0; q < PS; ++q) load_step(q, wst[q]);
     }
+    load_seg(0);
     store_seg(0);
     if (nseg > 1) load_seg(1);
     __syncthreads();
