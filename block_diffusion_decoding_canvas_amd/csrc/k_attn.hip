@@ -181,18 +181,37 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
     __syncthreads();
     if (tt + 1 < t_end) fetch(tt + 1);
 
-    // S^T[key][q] for 4 sub-tiles of 16 keys (raw dot products)
+    // S^T[key][q] for 4 sub-tiles of 16 keys (raw dot products).  The 4 NKS MFMAs run ks-major
+    // (consecutive MFMAs update different accumulators) with a 4-deep ring of K fragments read
+    // from LDS ahead of use, pinned by scheduling barriers so each MFMA waits only for its own
+    constexpr int NS = 4 * C::NKS;
+    auto kfrag = [&](int i) -> u32x4 {
+      const int d0 = (i / 4) * 32 + lg * 8;
+      return (d0 < DH) ? ld16(ks + ((i % 4) * 16 + r16) * C::KS_STRIDE + d0) : zero4;
+    };
     f32x4 s[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 kr[4];
 #pragma unroll
-      for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
-        const int d0 = ks_ * 32 + lg * 8;
-        const u32x4 kf = (d0 < DH) ? ld16(ks + (nt * 16 + r16) * C::KS_STRIDE + d0) : zero4;
-        s[nt] = mfma16x16x32(kf, qf[ks_], s[nt]);
-      }
+    for (int i = 0; i < 4; ++i) kr[i] = kfrag(i);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      s[i % 4] = mfma16x16x32(kr[i % 4], qf[i / 4], s[i % 4]);
+      if (i + 4 < NS) kr[i % 4] = kfrag(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments of the P V product, read while the softmax below runs
+    constexpr int NP = 2 * C::NDT;
+    auto vfrag = [&](int i) -> u32x4 {
+      const uint16_t* vrow = vt + ((i % C::NDT) * 16 + r16) * C::VT_STRIDE + (i / C::NDT) * 32 + 4 * lg;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
+    u32x4 vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = vfrag(i);
     // visibility: a tile inside the canvas or inside the cache that every query of this wave
     // sees entirely needs no per-element mask (the lane's keys: nt*16 + 4 lg + j)
     const bool in_cache = kbase + KT <= nc;
@@ -249,16 +268,13 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
                      cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])};
     }
     // O^T[dh][q] += V^T[dh][keys] P^T[keys][q]; the B operand's 8 keys per lane are
-    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}; the A operand reads the same keys
+    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}; the A operand reads the same keys.
+    // kp-major (consecutive MFMAs update different accumulators), 4-deep V^T fragment ring.
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const uint16_t* vrow = vt + (dt * 16 + r16) * C::VT_STRIDE + kp * 32 + 4 * lg;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        o[dt] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[kp], o[dt]);
-      }
+    for (int i = 0; i < NP; ++i) {
+      o[i % C::NDT] = mfma16x16x32(vr[i % 4], pb[i / C::NDT], o[i % C::NDT]);
+      if (i + 4 < NP) vr[i % 4] = vfrag(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
