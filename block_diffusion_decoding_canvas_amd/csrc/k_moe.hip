@@ -59,8 +59,10 @@ __device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
 // EPI_F32 stores the fp32 partial of k-split ks in its own plane; EPI_LMHEAD stores bf16
 // logits and, per (token, workgroup block of rows), the softmax statistics of the rounded
 // logits scaled by log2(e)/T.
-template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false>
+template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false, int RT = 2>
 __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
+  static_assert(RT == 2 || (EPI != EPI_SWIGLU && EPI != EPI_LMHEAD), "gate/up pairs and the LM-head "
+                "statistics take two row tiles per wave");
   constexpr int NTHR = WAVES * 64;
   constexpr int EB = F8 ? 1 : 2;                    // bytes per element
   constexpr int KSTEP = F8 ? 64 : 32;               // k per step
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   const int N = shared ? a.N_sh : a.N;      // gate/up: F; otherwise output rows
   const int K = shared ? a.K_sh : a.K;
   constexpr bool GU = EPI == EPI_SWIGLU;
-  const int n0 = nb * (GU ? WAVES * 16 : WAVES * 32);  // first output feature of the workgroup
+  const int n0 = nb * (GU ? WAVES * 16 : WAVES * 16 * RT);  // first output feature of the workgroup
   if (n0 >= N) return;                      // uniform across the workgroup
   const int k_beg = min(K, ks * a.k_per_split);   // a multiple of SEG
   const int k_end = min(K, k_beg + a.k_per_split);
@@ -130,9 +132,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   const int ksteps = K / KSTEP;
   const int s_first = k_beg / KSTEP, s_last = k_end / KSTEP;   // this split's steps
 
-  // the wave's two row tiles (fragment-major weights: tile rt, step s at (rt * ksteps + s) KiB)
-  int feat[2];
-  const uint8_t* wfrag[2];
+  // the wave's RT row tiles (fragment-major weights: tile rt, step s at (rt * ksteps + s) KiB)
+  int feat[RT];
+  const uint8_t* wfrag[RT];
   bool wave_live;
   if (GU) {
     const int f = n0 + wave * 16;
@@ -142,13 +144,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     wfrag[0] = W + (static_cast<long long>(fc / 16) * ksteps) * 1024 + lane * 16;        // gate
     wfrag[1] = W + (static_cast<long long>((N + fc) / 16) * ksteps) * 1024 + lane * 16;  // up
   } else {
-    const int r = n0 + wave * 32;
+    const int r = n0 + wave * 16 * RT;
     wave_live = r < N;
-    const int rc = wave_live ? r : N - 32;
-    feat[0] = r;
-    feat[1] = r + 16;
-    wfrag[0] = W + (static_cast<long long>(rc / 16) * ksteps) * 1024 + lane * 16;
-    wfrag[1] = W + (static_cast<long long>(rc / 16 + 1) * ksteps) * 1024 + lane * 16;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      feat[rt] = r + 16 * rt;
+      const int rc = min(feat[rt], N - 16);     // tiles past the last row read a valid tile
+      wfrag[rt] = W + (static_cast<long long>(rc / 16) * ksteps) * 1024 + lane * 16;
+    }
   }
 
   // token staging: thread loads XL 16-byte pieces of the MT x SEG segment.  Every load is issued
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it] & xm_[it]);
   };
 
-  f32x4 acc[2][NTB];
+  f32x4 acc[RT][NTB];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) acc[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -199,14 +202,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   // end (the ring's last refills) still issue their loads, so that the loads stay straight-line,
   // but from a 1 KiB block that stays L2-resident instead of re-reading a weight fragment from
   // HBM; their data is replaced by zeros when used
-  u32x4 wst[PS][2];
+  u32x4 wst[PS][RT];
   const uint8_t* hot = a.hot ? a.hot + lane * 16
                             : wfrag[0] + static_cast<long long>(max(s_last - 1, 0)) * 1024;
-  auto load_step = [&](int s, u32x4 (&w)[2]) __attribute__((always_inline)) {
+  auto load_step = [&](int s, u32x4 (&w)[RT]) __attribute__((always_inline)) {
     const bool in = s_first + s < s_last;
     const long long off = static_cast<long long>(s_first + s) * 1024;
-    w[0] = ld_nt(in ? wfrag[0] + off : hot);
-    w[1] = ld_nt(in ? wfrag[1] + off : hot);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) w[rt] = ld_nt(in ? wfrag[rt] + off : hot);
   };
 
   if (nseg > 0) {
@@ -231,16 +234,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     u32x4 b[NTB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
-    const u32x4 w0 = live ? wst[q][0] : zero4;
-    const u32x4 w1 = live ? wst[q][1] : zero4;
+    u32x4 wv[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) wv[rt] = live ? wst[q][rt] : zero4;
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-      if constexpr (F8) {
-        acc[0][tb] = mfma_fp8_pair(w0, b[tb], acc[0][tb]);
-        acc[1][tb] = mfma_fp8_pair(w1, b[tb], acc[1][tb]);
-      } else {
-        acc[0][tb] = mfma16x16x32(w0, b[tb], acc[0][tb]);
-        acc[1][tb] = mfma16x16x32(w1, b[tb], acc[1][tb]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (F8)
+          acc[rt][tb] = mfma_fp8_pair(wv[rt], b[tb], acc[rt][tb]);
+        else
+          acc[rt][tb] = mfma16x16x32(wv[rt], b[tb], acc[rt][tb]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -282,12 +286,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     // dequantise: accumulator * token-row scale * weight-row scale
     const float* wsc = shared ? a.w_scale_sh : a.w_scale + static_cast<long long>(expert) * a.wsc_estride;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       float sw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int wrow = (GU && rt == 1 ? N : 0) + feat[rt] + 4 * g + j;
-        sw[j] = wave_live ? wsc[wrow] : 0.f;
+        sw[j] = (wave_live && feat[rt] < N) ? wsc[wrow] : 0.f;
       }
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -374,7 +378,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     } else if constexpr (EPI == EPI_BF16) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + orow * a.ldo;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
+        if (feat[rt] >= N) continue;
         uint2 pk;
         pk.x = pack_bf2(acc[rt][tb][0], acc[rt][tb][1]);
         pk.y = pack_bf2(acc[rt][tb][2], acc[rt][tb][3]);
@@ -384,8 +389,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       float* o = static_cast<float*>(a.out) + static_cast<long long>(ks) * a.split_stride +
                  orow * a.ldo;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        *reinterpret_cast<float4*>(o + feat[rt] + 4 * g) =
+      for (int rt = 0; rt < RT; ++rt)
+        if (feat[rt] < N)
+          *reinterpret_cast<float4*>(o + feat[rt] + 4 * g) =
             make_float4(acc[rt][tb][0], acc[rt][tb][1], acc[rt][tb][2], acc[rt][tb][3]);
     }
   }
@@ -404,9 +410,9 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* src, uint16_t* dst
   st16(dst + i * 512 + lane * 8, ld16(src + n * cols + k));
 }
 
-template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false>
+template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false, int RT = 2>
 hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
-  const int per = EPI == EPI_SWIGLU ? WAVES * 16 : WAVES * 32;
+  const int per = EPI == EPI_SWIGLU ? WAVES * 16 : WAVES * 16 * RT;
   a.n_nblk = (std::max(a.N, a.chunks ? a.N_sh : a.N) + per - 1) / per;
   if (!a.chunks) a.grid_tiles = (a.ntok + NTB * 16 - 1) / (NTB * 16);
   if (a.ksplit < 1) a.ksplit = 1;
@@ -416,8 +422,8 @@ hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
   int grid = a.grid_tiles * a.ksplit * a.n_nblk;
   grid = (grid + 7) & ~7;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG, WAVES, PS, F8>), dim3(grid), dim3(WAVES * 64), 0, s,
-                     a);
+  hipLaunchKernelGGL((k_stream<EPI, NTB, SEG, WAVES, PS, F8, RT>), dim3(grid), dim3(WAVES * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -430,7 +436,7 @@ hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_SWIGLU, 2, 256, 4, 4>(a, s);
 }
 hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_BF16, 2, 256, 4, 4>(a, s);
+  return launch_stream<EPI_BF16, 2, 256, 4, 4, false, 4>(a, s);
 }
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_BF16, 4, 256, 4, 8>(a, s);
