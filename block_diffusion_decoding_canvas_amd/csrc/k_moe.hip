@@ -231,25 +231,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   auto step = [&](const uint8_t* xb, int s, int s_beg, int q, bool live)
       __attribute__((always_inline)) {
     const int kin = (s - s_beg) * 64 + g * 16;   // byte offset in the staged row
-    u32x4 b[NTB];
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
     u32x4 wv[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) wv[rt] = live ? wst[q][rt] : zero4;
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
+    auto mma = [&](const u32x4& bt, int tb) __attribute__((always_inline)) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         if constexpr (F8)
-          acc[rt][tb] = mfma_fp8_pair(wv[rt], b[tb], acc[rt][tb]);
+          acc[rt][tb] = mfma_fp8_pair(wv[rt], bt, acc[rt][tb]);
         else
-          acc[rt][tb] = mfma16x16x32(wv[rt], b[tb], acc[rt][tb]);
+          acc[rt][tb] = mfma16x16x32(wv[rt], bt, acc[rt][tb]);
+      }
+    };
+    if constexpr (NTB <= 4) {
+      u32x4 b[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) b[tb] = ld16(xb + (tb * 16 + r16) * STRIDE + kin);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) mma(b[tb], tb);
+    } else {
+      // many token blocks: their fragments flow through a 4-deep register ring, each read
+      // issued four blocks ahead of its MFMAs (pinned), so LDS latency overlaps the MFMAs
+      u32x4 br[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) br[i] = ld16(xb + (i * 16 + r16) * STRIDE + kin);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        mma(br[tb % 4], tb);
+        if (tb + 4 < NTB) br[tb % 4] = ld16(xb + ((tb + 4) * 16 + r16) * STRIDE + kin);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_step(s + PS, wst[q]);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // the next segment's pieces go to the other LDS buffer, then the one after is loaded
+  auto next_seg = [&](int sg) __attribute__((always_inline)) {
+    if (sg + 1 < nseg) {
+      store_seg((sg + 1) & 1);
+      if (sg + 2 < nseg) load_seg(sg + 2);
+    }
   };
   for (int sg = 0; sg < nseg; ++sg) {
     const uint8_t* xb = xs_lds[sg & 1];
@@ -257,13 +279,44 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     if (wave_live && s_beg + SSTEPS <= nsteps) {
       // a full segment as straight-line code: the only loop-carried loads are then the token
       // pieces issued at the end of the previous segment, which are older than this segment's
-      // weight loads, so the store below waits for them alone and the ring stays in flight
+      // weight loads, so the store below waits for them alone and the ring stays in flight.
+      // With 4 or more token blocks (the dense products, run at one or two waves per SIMD) the
+      // token fragments of the whole segment (fragment f = step u * NTB + block tb) stream
+      // through a D-deep register ring, each LDS read issued D fragments ahead of its MFMAs, so
+      // the LDS latency hides under independent MFMAs; the grouped expert products (2 token
+      // blocks, several waves per SIMD) keep their registers for occupancy instead
+      if constexpr (NTB < 4) {
 #pragma unroll
-      for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
-      if (sg + 1 < nseg) {
-        store_seg((sg + 1) & 1);
-        if (sg + 2 < nseg) load_seg(sg + 2);
+        for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
+      } else {
+        constexpr int NF = SSTEPS * NTB;
+        constexpr int D = NF < (NTB == 4 ? 8 : 4) ? NF : (NTB == 4 ? 8 : 4);
+        const uint8_t* xf = xb + r16 * STRIDE + g * 16;
+        u32x4 br[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) br[i] = ld16(xf + (i % NTB) * 16 * STRIDE + (i / NTB) * 64);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int u = f / NTB, tb = f % NTB;
+          const u32x4 bt = br[f % D];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            if constexpr (F8)
+              acc[rt][tb] = mfma_fp8_pair(wst[u % PS][rt], bt, acc[rt][tb]);
+            else
+              acc[rt][tb] = mfma16x16x32(wst[u % PS][rt], bt, acc[rt][tb]);
+          }
+          if (f + D < NF)
+            br[f % D] = ld16(xf + ((f + D) % NTB) * 16 * STRIDE + ((f + D) / NTB) * 64);
+          __builtin_amdgcn_sched_barrier(0);
+          if (tb == NTB - 1) {
+            // the step's last MFMAs have read its ring stage: refill it with step s + PS
+            load_step(s_beg + u + PS, wst[u % PS]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
+      next_seg(sg);
     } else {
       // the last, partial segment (or a wave past the last output row, which only joins the
       // barriers)
@@ -272,10 +325,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
 #pragma unroll
         for (int q = 0; q < PS; ++q) step(xb, s0 + q, s_beg, q, s0 + q < s_end);
       }
-      if (sg + 1 < nseg) {
-        store_seg((sg + 1) & 1);
-        if (sg + 2 < nseg) load_seg(sg + 2);
-      }
+      next_seg(sg);
     }
     if (sg + 1 < nseg) {
       __syncthreads();
@@ -442,10 +492,10 @@ hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_BF16, 4, 256, 4, 8>(a, s);
 }
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_F32, 4, 256, 4, 8>(a, s);
+  return launch_stream<EPI_F32, 8, 256, 4, 4>(a, s);
 }
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_LMHEAD, 16, 128, 8, 4>(a, s);
+  return launch_stream<EPI_LMHEAD, 16, 128, 8, 2>(a, s);
 }
 
 hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s) {
