@@ -256,6 +256,7 @@ dg_status dg_model_create(const dg_dims* d, const dg_layer_w* layers, const void
     return fail(DG_ERR_SHAPE, "non-positive or too small dimension");
   if (d->d_model % 32 || d->ffn_inner % 32 || d->shared_inner % 32)
     return fail(DG_ERR_SHAPE, "d_model, ffn_inner and shared_inner must be multiples of 32");
+  if (d->d_model > 8192) return fail(DG_ERR_SHAPE, "d_model must be <= 8192");
   if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128 &&
       d->head_dim != 256)
     return fail(DG_ERR_SHAPE, "head_dim must be one of 16, 32, 64, 128, 256");

@@ -65,6 +65,7 @@ enum { DG_BF16 = 0, DG_FP8_E4M3 = 1 };
 
 /* Model dimensions.  d_model, ffn_inner, shared_inner, (Hq + 2 Hkv) head_dim and Hq head_dim must
  * be multiples of 32 (d_model, ffn_inner, shared_inner multiples of 64 with DG_FP8_E4M3);
+ * d_model <= 8192 (a token row is held in the registers of one workgroup);
  * head_dim one of 16, 32, 64, 128, 256;
  * n_q_heads a multiple of n_kv_heads; 1 <= top_k <= n_experts <= 256; vocab a multiple of 256;
  * 1 <= canvas_len <= 1024; window == 0 (every layer global) or window >= canvas_len. */

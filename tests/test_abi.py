@@ -61,11 +61,14 @@ def test_model_create_validation():
     assert lib.dg_workspace_bytes(h, 1) > 0
     lib.dg_model_destroy(h)
     bad = [dict(hq=6, hkv=4), dict(top_k=9), dict(d=48), dict(F=100), dict(V=500),
-           dict(C=0), dict(C=2000), dict(window=8), dict(dh=8)]
+           dict(C=0), dict(C=2000), dict(window=8), dict(dh=8), dict(d=8224)]
     for kw in bad:
         st, _ = _create(_tiny_dims(**kw))
         assert st == 2, kw                       # DG_ERR_SHAPE
         assert lib.dg_last_error()
+    st, h = _create(_tiny_dims(d=8192))            # the largest row a workgroup holds
+    assert st == 0
+    lib.dg_model_destroy(h)
     st, _ = _create(_tiny_dims(), null_layer=True)
     assert st == 1                               # DG_ERR_NULL
     d = _tiny_dims()

@@ -143,3 +143,93 @@ def test_capacity_and_state_errors_enqueue_nothing():
     out = driver.StepOut(B, dims["C"], dims["V"], DEV)
     with pytest.raises(driver._lib.DgError, match="STATE"):
         driver.decoder_step(model, kv, 6, driver.eb_params(max_steps=6), gs, out, ws)
+
+
+@pytest.mark.parametrize("d,top_k", [(1056, 10), (3072, 8)])
+def test_layer_row_shapes(d, top_k):
+    """One decoder layer over 2 canvases at model widths whose token rows end in a partial
+    1024-column chunk (d 1056) or fill three chunks exactly (d 3072), with up to 10 routed
+    experts per token: the per-token row kernels (residual + norm, combine + next norm) and the
+    routing against the oracle on rows whose expert set is certified."""
+    dims = dict(n_layers=1, d=d, hq=4, hkv=2, dh=64, E=16, top_k=top_k, F=128, Fs=64, V=256,
+                C=40, window=0, global_every=1, eps=1e-6)
+    rng = np.random.default_rng(11)
+    mnp = dict(dims=dims, layers=[synth.make_layer(dims, rng, norm_gain_std=0.1)],
+               embed=np.zeros((256, d), np.float32), final_norm=np.ones(d, np.float32),
+               w_lm=np.zeros((256, d), np.float32))
+    B, cap, n = 2, 120, 70
+    cache = synth.make_cache(dims, B, cap, n, seed=12)
+    T = B * dims["C"]
+    h = synth.hidden_states(T, d, seed=13)
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    kv = driver.KVCache.from_host(dims, cache, cap, DEV)
+    ws = driver.workspace(model.workspace_bytes(B))
+    hg = torch.from_numpy(h.astype(np.float32)).to(DEV)
+    rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device=DEV)
+    ti = torch.zeros((T, top_k), dtype=torch.int32, device=DEV)
+    gt = torch.zeros((T, top_k), dtype=torch.float32, device=DEV)
+    driver.layer_forward(model, kv, 0, 0, hg, ws, rl, ti, gt)
+    torch.cuda.synchronize()
+    lw = synth.model_to_f64(mnp)["layers"][0]
+    k64 = cache["k"][0].astype(np.float64)
+    v64 = cache["v"][0].astype(np.float64)
+    h_ref, _, _, info = om.layer_forward(h.astype(np.float64).reshape(B, dims["C"], d), lw, dims,
+                                         0, k64, v64, np.array(cache["len"]), causal=False)
+    h_ref = h_ref.reshape(T, d)
+    rg = rl.cpu().numpy()
+    r_ref = info["router_logits"].reshape(T, -1)
+    assert_close_rel(rg, r_ref, what="router logits")
+    rerr = np.abs(rg - r_ref).max(axis=1)
+    srt = -np.sort(-r_ref, axis=1)
+    cert = srt[:, top_k - 1] - srt[:, top_k] > 2 * rerr + 1e-7
+    assert cert.sum() >= T // 2
+    for t in np.nonzero(cert)[0]:
+        assert set(ti.cpu().numpy()[t]) == set(info["topk_idx"].reshape(T, -1)[t])
+    hout = hg.cpu().numpy()
+    assert_close_rel(hout[cert] - h[cert], h_ref[cert] - h[cert],
+                     what=f"layer increment d={d} top_k={top_k} (certified routing)")
+
+
+def test_router_exact_ties_lowest_id_first():
+    """Duplicated router rows give bit-identical logits (same products, same order): the top-k
+    keeps the lower expert id ahead of its twin, and picks it alone when only one fits."""
+    dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=16, E=8, top_k=3, F=64, Fs=64, V=256, C=40,
+                window=0, global_every=1, eps=1e-6)
+    rng = np.random.default_rng(21)
+    lw = synth.make_layer(dims, rng, norm_gain_std=0.1)
+    twins = [(2, 5), (1, 7)]
+    for lo, hi in twins:
+        lw["w_router"][hi] = lw["w_router"][lo]
+    mnp = dict(dims=dims, layers=[lw], embed=np.zeros((256, 64), np.float32),
+               final_norm=np.ones(64, np.float32), w_lm=np.zeros((256, 64), np.float32))
+    cache = synth.make_cache(dims, 1, 80, 30, seed=22)
+    T = dims["C"]
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    kv = driver.KVCache.from_host(dims, cache, 80, DEV)
+    ws = driver.workspace(model.workspace_bytes(1))
+    hg = torch.from_numpy(synth.hidden_states(T, 64, seed=23).astype(np.float32)).to(DEV)
+    rl = torch.zeros((T, 8), dtype=torch.float32, device=DEV)
+    ti = torch.zeros((T, 3), dtype=torch.int32, device=DEV)
+    gt = torch.zeros((T, 3), dtype=torch.float32, device=DEV)
+    driver.layer_forward(model, kv, 0, 0, hg, ws, rl, ti, gt)
+    torch.cuda.synchronize()
+    r = rl.cpu().numpy()
+    sel = ti.cpu().numpy()
+    seen_both = seen_one = 0
+    for lo, hi in twins:
+        assert np.array_equal(r[:, lo], r[:, hi])
+    for t in range(T):
+        # the selection is the rank order of (logit desc, id asc) over the GPU's own logits
+        order = sorted(range(8), key=lambda e: (-r[t, e], e))[:3]
+        assert list(sel[t]) == order, t
+        for lo, hi in twins:
+            if lo in sel[t] and hi in sel[t]:
+                i = list(sel[t]).index(lo)
+                assert sel[t][i + 1] == hi
+                seen_both += 1
+            elif hi in sel[t]:
+                raise AssertionError(f"token {t}: expert {hi} chosen without its lower twin {lo}")
+            elif lo in sel[t]:
+                seen_one += 1
+    print(f"twin pairs selected together {seen_both}, lower twin alone {seen_one}")
+    assert seen_both + seen_one > 0
