@@ -6,39 +6,59 @@
 // only if (len + i) - j < window (model card dimension table: 1,024-token window).
 //
 // Layout of the work: one workgroup = (canvas b, KV head g, 128 query rows, one split of the
-// key range).  The query rows of a KV head are its Hq/Hkv query heads times the canvas
-// positions, so the K/V tiles staged in LDS serve every query head that reads them.  Keys are
-// processed in tiles of 64 (K tile [key][dh] and V tile transposed [dh][key] in LDS).  Each wave
-// holds 16 query rows and computes S^T = K Q^T, so the probabilities come out of the MFMA in the
+// key range).  The query rows of a KV head are its Hq/Hkv query heads
+// times the canvas positions, so the K/V tiles staged in LDS serve every query head that reads
+// them.  Keys are processed in tiles of 64 (K tile [key][dh] and V tile transposed [dh][key] in
+// LDS, double buffered: tile t + 1 is staged while tile t is computed, one barrier per tile).
+// Up to head_dim 128 there are 4 waves (one per SIMD), each holding 32 query rows as two 16-row
+// MFMA tiles, so every K and V^T fragment read from LDS feeds two MFMAs; at head_dim 256 the
+// registers hold one 16-row tile per wave and there are 8 waves.  Each wave computes S^T = K Q^T, so the probabilities come out of the MFMA in the
 // lane layout that the P V product takes as its B operand (O^T = V^T P^T) with no shuffle.
-// Splits of the key range write unnormalised partial outputs with their running max and sum,
-// merged afterwards by log-sum-exp.
+// LDS rows are padded to strides whose 16-byte fragment reads run at the full LDS rate, and the
+// keys of each 32-key group of V^T are stored in the order the B operand holds them, so one
+// 16-byte read gives a lane its 8 keys.  Splits of the key range write unnormalised partial
+// outputs with their running max and sum, merged afterwards by log-sum-exp.
 #include "dg_internal.h"
 
 namespace dg {
 namespace {
 
-constexpr int KT = 64;        // keys per tile
-constexpr int NWAVE = 8;      // waves per workgroup
-constexpr int QB = NWAVE * 16; // query rows per workgroup
-constexpr int NTHR = NWAVE * 64;
+constexpr int KT = 64;               // keys per tile
+constexpr int QB = 128;              // query rows per workgroup
 
 template <int DH>
 struct AttnCfg {
-  static constexpr int KS_STRIDE = DH + 8;   // bf16 per K row in LDS
-  static constexpr int VT_STRIDE = KT + 8;   // bf16 per transposed V row in LDS
+  static constexpr int QT = DH >= 256 ? 1 : 2;  // 16-row query tiles per wave
+  static constexpr int NWAVE = QB / (16 * QT);  // waves per workgroup
+  static constexpr int NTHR = NWAVE * 64;
+  static constexpr int KS_STRIDE = DH + 16;  // bf16 per K row in LDS
+  static constexpr int VT_STRIDE = KT + 16;  // bf16 per transposed V row in LDS
   static constexpr int NKS = (DH + 31) / 32; // 32-wide dh steps of QK^T
   static constexpr int NDT = DH / 16;        // 16-row dh tiles of O^T
-  static constexpr int LDS_BYTES = (KT * KS_STRIDE + DH * VT_STRIDE) * 2;
+  static constexpr int KBUF = KT * KS_STRIDE;
+  static constexpr int VBUF = DH * VT_STRIDE;
+  static constexpr int KCH = DH / 8;                          // 16-byte chunks per key row
+  // staging: thread t holds key t % KT of the tile (K) and key pair t % (KT / 2) (V), with the
+  // chunks t / KT + j * KSTEP, j < KIT (K) and t / (KT / 2) + j * VSTEP, j < VIT (V)
+  static constexpr int KSTEP = NTHR / KT, VSTEP = NTHR / (KT / 2);
+  static constexpr int KIT = (KCH + KSTEP - 1) / KSTEP;
+  static constexpr int VIT = (KCH + VSTEP - 1) / VSTEP;
+  static constexpr int RING = 8 / QT;  // fragment ring depth: 8 MFMAs of cover
 };
 
+// position of key k of a tile in a V^T row: inside each 32-key group, key 16 h + 4 l + j goes to
+// 8 l + 4 h + j, the order in which lane group l of the P V product's B operand holds its keys
+__device__ __forceinline__ int vt_pos(int k) {
+  const int q = k & 31;
+  return (k & ~31) + 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3);
+}
+
 template <int DH>
-__global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   using C = AttnCfg<DH>;
-  constexpr int ITEMS = (KT / 2) * (DH / 8) / NTHR;  // (key pair, 8-dh chunk) items per thread
-  constexpr int IT = ITEMS >= 1 ? ITEMS : 1;
-  __shared__ __align__(16) uint16_t ks[KT * C::KS_STRIDE];
-  __shared__ __align__(16) uint16_t vt[DH * C::VT_STRIDE];
+  constexpr int QT = C::QT, NTHR = C::NTHR;
+  __shared__ __align__(16) uint16_t ks[2][C::KBUF];
+  __shared__ __align__(16) uint16_t vt[2][C::VBUF];
 
   // logical block -> (canvas, KV head, key split, query block); the query blocks that share a
   // KV head and split are consecutive, so they run on one XCD and share its L2 for K/V tiles
@@ -66,39 +86,58 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   const int t_beg = split * per;
   const int t_end = min(ntiles, t_beg + per);
 
-  // this lane's query row (B operand column)
-  const int r = qblk * QB + wave * 16 + r16;
-  const bool r_ok = r < R;
-  const int rr = r_ok ? r : R - 1;
-  const int hl = rr / a.C, qi = rr % a.C;
-  const int h = g * hpg + hl;
-  const long long qrow = static_cast<long long>(b) * a.C + qi;
-
+  // this lane's query rows (B operand columns), one per query tile
+  int r[QT], qi[QT], h[QT], win_lo[QT];
+  bool r_ok[QT];
+  long long qrow[QT];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 qf[C::NKS];
-  {
-    const uint16_t* qp = a.qkv + qrow * ldqkv + h * DH;
+  u32x4 qf[C::NKS][QT];
+#pragma unroll
+  for (int q = 0; q < QT; ++q) {
+    r[q] = qblk * QB + wave * 16 * QT + q * 16 + r16;
+    r_ok[q] = r[q] < R;
+    const int rr = r_ok[q] ? r[q] : R - 1;
+    const int hl = rr / a.C;
+    qi[q] = rr % a.C;
+    h[q] = g * hpg + hl;
+    qrow[q] = static_cast<long long>(b) * a.C + qi[q];
+    win_lo[q] = len + qi[q] - a.window + 1;   // first visible cache position (windowed layers)
+    const uint16_t* qp = a.qkv + qrow[q] * ldqkv + h[q] * DH;
 #pragma unroll
     for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
       const int d0 = ks_ * 32 + lg * 8;
-      qf[ks_] = (d0 < DH) ? ld16(qp + d0) : zero4;
+      qf[ks_][q] = (d0 < DH) ? ld16(qp + d0) : zero4;
+      // opaque to the compiler: the fragments stay in registers for the whole key range
+      // instead of being re-loaded (behind the tile prefetches) in every tile
+      asm volatile("" : "+v"(qf[ks_][q]));
     }
   }
 
-  f32x4 o[C::NDT];
+  f32x4 o[C::NDT][QT];
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int q = 0; q < QT; ++q) o[dt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int q = 0; q < QT; ++q) {
+    m_run[q] = -INFINITY;
+    l_run[q] = 0.f;
+  }
 
   const uint16_t* kcache = a.kc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
   const uint16_t* vcache = a.vc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
   const uint16_t* kcanvas = a.qkv + static_cast<long long>(b) * a.C * ldqkv + (a.Hq + g) * DH;
   const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
-  const int win_lo = len + qi - a.window + 1;  // first visible cache position (windowed layers)
 
   // wave-uniform range of this wave's canvas positions (tiles that no query of the wave sees
   // partially are processed without per-element masks)
-  int qi_lo = qi, qi_hi = qi;
+  int qi_lo = qi[0], qi_hi = qi[0];
+#pragma unroll
+  for (int q = 1; q < QT; ++q) {
+    qi_lo = min(qi_lo, qi[q]);
+    qi_hi = max(qi_hi, qi[q]);
+  }
 #pragma unroll
   for (int o2 = 1; o2 < 64; o2 <<= 1) {
     qi_lo = min(qi_lo, __shfl_xor(qi_lo, o2, 64));
@@ -107,64 +146,67 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   qi_lo = __builtin_amdgcn_readfirstlane(qi_lo);
   qi_hi = __builtin_amdgcn_readfirstlane(qi_hi);
 
-  // staging items: (key pair p, dh chunk c): two keys' rows of K, and of V written transposed;
-  // the next tile's rows are prefetched into registers while the current one is computed
-  constexpr int ITEMS_ALL = (KT / 2) * (DH / 8);
-  u32x4 pk0[IT], pk1[IT], pv0[IT], pv1[IT];
-  auto key_ptr = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
-    return kk < nc ? cache + static_cast<long long>(c_lo + kk) * DH
-                   : canvas + static_cast<long long>(kk - nc) * ldqkv;
+  // staging.  K pieces: (key kk, 16-byte chunk c), consecutive threads on consecutive keys; V
+  // items: (key pair p, chunk c), the two keys' rows written transposed.  K of the next tile is
+  // fetched before this tile's S^T and stored after it; V of the next tile is fetched then and
+  // stored after the P V product.
+  // every load is unconditional: a key past the range reads the last key of the range (finite
+  // data whose scores are masked to -inf, so its probability is 0), and the cache or canvas row
+  // is chosen by bit arithmetic on both (clamped) addresses, so no branch makes the compiler
+  // wait for loads in flight
+  auto kv_row = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
+    const int kc = min(kk, nk - 1);
+    const uintptr_t pc = reinterpret_cast<uintptr_t>(
+        cache + static_cast<long long>(c_lo + max(min(kc, nc - 1), 0)) * DH);
+    const uintptr_t pn = reinterpret_cast<uintptr_t>(
+        canvas + static_cast<long long>(max(kc - nc, 0)) * ldqkv);
+    const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
+    return reinterpret_cast<const uint16_t*>((pc & m) | (pn & ~m));
   };
-  auto fetch = [&](int tt) __attribute__((always_inline)) {
-    const int kt0 = tt * KT;
-    if (kt0 + KT <= nc) {
-      // every key of the tile is a cache row: two consecutive rows per item
-      const long long base = static_cast<long long>(c_lo + kt0) * DH;
+  constexpr bool KFULL = C::KCH % C::KSTEP == 0;   // every thread has all its K pieces
+  constexpr bool VFULL = C::KCH % C::VSTEP == 0;   // and V items
+  const int k_key = tid % KT, k_c0 = tid / KT;             // this thread's K key and first chunk
+  const int v_pair = tid % (KT / 2), v_c0 = tid / (KT / 2);  // its V key pair and first chunk
+  u32x4 pk[C::KIT], pv0[C::VIT], pv1[C::VIT];
+  auto fetch_k = [&](int tt) __attribute__((always_inline)) {
+    const uint16_t* row = kv_row(tt * KT + k_key, kcache, kcanvas);
 #pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int idx = tid + it * NTHR;
-        const int pp = idx % (KT / 2), c = idx / (KT / 2);
-        const long long off = base + static_cast<long long>(2 * pp) * DH + c * 8;
-        if (idx < ITEMS_ALL) {
-          pk0[it] = ld16(kcache + off);
-          pk1[it] = ld16(kcache + off + DH);
-          pv0[it] = ld16(vcache + off);
-          pv1[it] = ld16(vcache + off + DH);
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + it * NTHR;
-      const bool on = idx < ITEMS_ALL;
-      const int pp = idx % (KT / 2), c = idx / (KT / 2);
-      const int k0 = kt0 + 2 * pp;
-      pk0[it] = pk1[it] = pv0[it] = pv1[it] = zero4;
-      if (on && k0 < nk) {
-        pk0[it] = ld16(key_ptr(k0, kcache, kcanvas) + c * 8);
-        pv0[it] = ld16(key_ptr(k0, vcache, vcanvas) + c * 8);
-      }
-      if (on && k0 + 1 < nk) {
-        pk1[it] = ld16(key_ptr(k0 + 1, kcache, kcanvas) + c * 8);
-        pv1[it] = ld16(key_ptr(k0 + 1, vcache, vcanvas) + c * 8);
-      }
+    for (int it = 0; it < C::KIT; ++it) {
+      const int c = min(k_c0 + it * C::KSTEP, C::KCH - 1);
+      pk[it] = ld16(row + c * 8);
     }
   };
-  auto stage = [&]() __attribute__((always_inline)) {
+  auto stage_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + it * NTHR;
-      if (idx >= ITEMS_ALL) continue;
-      const int pp = idx % (KT / 2), c = idx / (KT / 2);
-      st16(ks + (2 * pp) * C::KS_STRIDE + c * 8, pk0[it]);
-      st16(ks + (2 * pp + 1) * C::KS_STRIDE + c * 8, pk1[it]);
+    for (int it = 0; it < C::KIT; ++it) {
+      const int c = k_c0 + it * C::KSTEP;
+      if (!KFULL && c >= C::KCH) continue;
+      st16(ks[buf] + k_key * C::KS_STRIDE + c * 8, pk[it]);
+    }
+  };
+  auto fetch_v = [&](int tt) __attribute__((always_inline)) {
+    const int k0 = tt * KT + 2 * v_pair;
+    const uint16_t* row0 = kv_row(k0, vcache, vcanvas);
+    const uint16_t* row1 = kv_row(k0 + 1, vcache, vcanvas);
+#pragma unroll
+    for (int it = 0; it < C::VIT; ++it) {
+      const int c = min(v_c0 + it * C::VSTEP, C::KCH - 1);
+      pv0[it] = ld16(row0 + c * 8);
+      pv1[it] = ld16(row1 + c * 8);
+    }
+  };
+  auto stage_v = [&](int buf) __attribute__((always_inline)) {
+    const int w0 = vt_pos(2 * v_pair) >> 1;   // keys 2p, 2p+1 stay adjacent: one 32-bit word
+#pragma unroll
+    for (int it = 0; it < C::VIT; ++it) {
+      const int c = v_c0 + it * C::VSTEP;
+      if (!VFULL && c >= C::KCH) continue;
       // V^T[dh][key]: each 32-bit store holds keys 2p and 2p+1 of one dh
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t a0 = pv0[it][e], a1 = pv1[it][e];
-        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e) * C::VT_STRIDE) + pp;
-        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + pp;
+        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt[buf] + (c * 8 + 2 * e) * C::VT_STRIDE) + w0;
+        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt[buf] + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + w0;
         *row0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // low halves: key 2p, key 2p+1
         *row1 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // high halves
       }
@@ -172,46 +214,58 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
   };
 
   const float sc = a.scale_log2e;
-  // the next tile's K/V rows are fetched into registers while the current tile is computed
-  if (t_beg < t_end) fetch(t_beg);
+  if (t_beg < t_end) {
+    fetch_k(t_beg);
+    fetch_v(t_beg);
+    stage_k(0);
+    stage_v(0);
+  }
+  __syncthreads();
   for (int tt = t_beg; tt < t_end; ++tt) {
     const int kbase = tt * KT;
-    __syncthreads();  // previous tile fully consumed
-    stage();
-    __syncthreads();
-    if (tt + 1 < t_end) fetch(tt + 1);
+    const int cur = (tt - t_beg) & 1;
+    const bool more = tt + 1 < t_end;
+    const uint16_t* ksb = ks[cur];
+    const uint16_t* vtb = vt[cur];
+    if (more) fetch_k(tt + 1);
 
-    // S^T[key][q] for 4 sub-tiles of 16 keys (raw dot products).  The 4 NKS MFMAs run ks-major
-    // (consecutive MFMAs update different accumulators) with a 4-deep ring of K fragments read
-    // from LDS ahead of use, pinned by scheduling barriers so each MFMA waits only for its own
+    // S^T[key][q] for 4 sub-tiles of 16 keys and the wave's query tiles (raw dot products).  The
+    // K fragments run ks-major through a ring read from LDS RING fragments ahead of use (pinned
+    // by scheduling barriers); each fragment feeds the MFMAs of every query tile
     constexpr int NS = 4 * C::NKS;
     auto kfrag = [&](int i) -> u32x4 {
       const int d0 = (i / 4) * 32 + lg * 8;
-      return (d0 < DH) ? ld16(ks + ((i % 4) * 16 + r16) * C::KS_STRIDE + d0) : zero4;
+      return (d0 < DH) ? ld16(ksb + ((i % 4) * 16 + r16) * C::KS_STRIDE + d0) : zero4;
     };
-    f32x4 s[4];
+    f32x4 s[QT][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 kr[4];
+    for (int q = 0; q < QT; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kr[i] = kfrag(i);
+      for (int nt = 0; nt < 4; ++nt) s[q][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KR = C::RING < NS ? C::RING : NS;
+    u32x4 kr[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) kr[i] = kfrag(i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      s[i % 4] = mfma16x16x32(kr[i % 4], qf[i / 4], s[i % 4]);
-      if (i + 4 < NS) kr[i % 4] = kfrag(i + 4);
+#pragma unroll
+      for (int q = 0; q < QT; ++q) s[q][i % 4] = mfma16x16x32(kr[i % KR], qf[i / 4][q], s[q][i % 4]);
+      if (i + KR < NS) kr[i % KR] = kfrag(i + KR);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      stage_k(cur ^ 1);   // the other buffer was last read before the previous barrier
+      fetch_v(tt + 1);
     }
     // the first V^T fragments of the P V product, read while the softmax below runs
     constexpr int NP = 2 * C::NDT;
     auto vfrag = [&](int i) -> u32x4 {
-      const uint16_t* vrow = vt + ((i % C::NDT) * 16 + r16) * C::VT_STRIDE + (i / C::NDT) * 32 + 4 * lg;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-      return u32x4{lo.x, lo.y, hi.x, hi.y};
+      return ld16(vtb + ((i % C::NDT) * 16 + r16) * C::VT_STRIDE + (i / C::NDT) * 32 + 8 * lg);
     };
-    u32x4 vr[4];
+    constexpr int VR = C::RING < NP ? C::RING : NP;
+    u32x4 vr[VR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = vfrag(i);
+    for (int i = 0; i < VR; ++i) vr[i] = vfrag(i);
     // visibility: a tile inside the canvas or inside the cache that every query of this wave
     // sees entirely needs no per-element mask (the lane's keys: nt*16 + 4 lg + j)
     const bool in_cache = kbase + KT <= nc;
@@ -219,89 +273,100 @@ __global__ __launch_bounds__(NTHR) void k_attn(AttnArgs a) {
         kbase + KT <= nk &&
         (in_cache ? (a.window == 0 || c_lo + kbase >= len + qi_hi - a.window + 1)
                   : (kbase >= nc && (!a.causal || kbase + KT - 1 - nc <= qi_lo)));
-    float tmax = -INFINITY;
-    if (full) {
+    u32x4 pb[QT][2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
-    } else {
+    for (int q = 0; q < QT; ++q) {
+      float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 4; ++nt)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(s[q][nt][0], s[q][nt][1]), fmaxf(s[q][nt][2], s[q][nt][3])));
+      } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kk = kbase + nt * 16 + 4 * lg + j;
-          bool vis = kk < nk;
-          if (kk < nc) {
-            if (a.window > 0) vis = vis && (c_lo + kk >= win_lo);
-          } else if (a.causal) {
-            vis = vis && (kk - nc <= qi);
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kk = kbase + nt * 16 + 4 * lg + j;
+            bool vis = kk < nk;
+            if (kk < nc) {
+              if (a.window > 0) vis = vis && (c_lo + kk >= win_lo[q]);
+            } else if (a.causal) {
+              vis = vis && (kk - nc <= qi[q]);
+            }
+            s[q][nt][j] = vis ? s[q][nt][j] : -INFINITY;
+            tmax = fmaxf(tmax, s[q][nt][j]);
           }
-          s[nt][j] = vis ? s[nt][j] : -INFINITY;
-          tmax = fmaxf(tmax, s[nt][j]);
         }
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // running max in scaled (log2) units; the scale is > 0, so it commutes with the max
-    const float m_new = fmaxf(m_run, tmax * sc);
-    const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run + neg_m);   // m_run = -inf: 0
-    m_run = m_new;
-    // rescale only when some lane's maximum moved (a wave-uniform branch)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      l_run *= alpha;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // running max in scaled (log2) units; the scale is > 0, so it commutes with the max
+      const float m_new = fmaxf(m_run[q], tmax * sc);
+      const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[q] + neg_m);   // m_run = -inf: 0
+      m_run[q] = m_new;
+      // rescale only when some lane's maximum moved (a wave-uniform branch)
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        l_run[q] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
-    }
-    u32x4 pb[2];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      f32x4 lo, hi;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kp][j], sc, neg_m));
-        hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kp + 1][j], sc, neg_m));
+        for (int dt = 0; dt < C::NDT; ++dt) o[dt][q] *= alpha;
       }
-      l_run += (lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]);
-      pb[kp] = u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
-                     cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])};
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp][j], sc, neg_m));
+          hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp + 1][j], sc, neg_m));
+        }
+        l_run[q] += (lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]);
+        pb[q][kp] = u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
+                          cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])};
+      }
     }
     // O^T[dh][q] += V^T[dh][keys] P^T[keys][q]; the B operand's 8 keys per lane are
-    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}; the A operand reads the same keys.
-    // kp-major (consecutive MFMAs update different accumulators), 4-deep V^T fragment ring.
+    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}, the 16 bytes at V^T column 32 kp + 8 lg.
+    // kp-major V^T fragment ring; each fragment feeds every query tile
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      o[i % C::NDT] = mfma16x16x32(vr[i % 4], pb[i / C::NDT], o[i % C::NDT]);
-      if (i + 4 < NP) vr[i % 4] = vfrag(i + 4);
+#pragma unroll
+      for (int q = 0; q < QT; ++q)
+        o[i % C::NDT][q] = mfma16x16x32(vr[i % VR], pb[q][i / C::NDT], o[i % C::NDT][q]);
+      if (i + VR < NP) vr[i % VR] = vfrag(i + VR);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (more) stage_v(cur ^ 1);
+    __syncthreads();
   }
 
-  // row sum over the 4 lanes that share this query
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!r_ok) return;
-  if (a.n_split == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = a.out + qrow * (a.Hq * DH) + h * DH;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      uint2 pk;
-      pk.x = pack_bf2(o[dt][0] * inv, o[dt][1] * inv);
-      pk.y = pack_bf2(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<uint2*>(op + dt * 16 + 4 * lg) = pk;
-    }
-  } else {
-    const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + r;
-    float* op = a.o_part + prow * DH;
+  for (int q = 0; q < QT; ++q) {
+    // row sum over the 4 lanes that share this query
+    float l = l_run[q];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!r_ok[q]) continue;
+    if (a.n_split == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* op = a.out + qrow[q] * (a.Hq * DH) + h[q] * DH;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-      *reinterpret_cast<float4*>(op + dt * 16 + 4 * lg) =
-          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (lg == 0) {
-      a.ml_part[prow * 2] = m_run;
-      a.ml_part[prow * 2 + 1] = l_run;
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        uint2 pk2;
+        pk2.x = pack_bf2(o[dt][q][0] * inv, o[dt][q][1] * inv);
+        pk2.y = pack_bf2(o[dt][q][2] * inv, o[dt][q][3] * inv);
+        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * lg) = pk2;
+      }
+    } else {
+      const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + r[q];
+      float* op = a.o_part + prow * DH;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+        *reinterpret_cast<float4*>(op + dt * 16 + 4 * lg) =
+            make_float4(o[dt][q][0], o[dt][q][1], o[dt][q][2], o[dt][q][3]);
+      if (lg == 0) {
+        a.ml_part[prow * 2] = m_run[q];
+        a.ml_part[prow * 2 + 1] = l;
+      }
     }
   }
 }
@@ -364,7 +429,7 @@ hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   const int R = (a.Hq / a.Hkv) * a.C;
   int grid = ((R + QB - 1) / QB) * a.Hkv * a.B * a.n_split;
   grid = (grid + 7) & ~7;
-  hipLaunchKernelGGL(k_attn<DH>, dim3(grid), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(k_attn<DH>, dim3(grid), dim3(AttnCfg<DH>::NTHR), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const long long n = static_cast<long long>(a.B) * a.Hkv * R * (DH / 4);
