@@ -9,7 +9,11 @@ the same on the 8,448-token cache and is appended.  Inputs are resident in HBM b
 
 Reported: denoising steps/s (value), tokens/s, the HBM roofline fraction of the MoE gate/up
 kernel (the dominant kernel) from HIP events recorded around its launches in the timed region,
-and the plain CPU oracle timed on a bounded sample of the same step on the host cores.
+and the plain CPU oracle timed on a bounded sample of the same step on the host cores.  Besides,
+from HIP events in an untimed pass: the MFMA fraction of the LM head and of attention (algorithmic
+flops), the HBM fraction of the MoE down product, and the HBM fraction of the standalone EB
+sampler's statistics kernel on the standalone sampler workload (bf16 logits [256 x 262144]:
+30% peaked rows with one logit 12 over N(0,1), 40% N(0,2) rows, 30% N(0,0.1) rows).
 """
 import argparse
 import json
@@ -27,6 +31,7 @@ METRIC = "canvas denoise steps/s + tokens/s (256-tok canvas, 1 GPU), % of roofli
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
 
 
 def parse():
@@ -67,6 +72,65 @@ def moe_gateup_bytes(dims, n_touched):
     weights = (n_touched * 2 * f * d + 2 * fs * d) * 2
     acts = t * d * 2 + (t * k * f + t * fs) * 2
     return weights + acts
+
+
+def moe_down_bytes(dims, n_touched):
+    """Algorithmic HBM bytes of one down launch: each touched expert's [d, F] weights and the
+    shared expert's once, the SwiGLU activations read once, the expert outputs written once."""
+    d, f, fs, k, t = dims["d"], dims["F"], dims["Fs"], dims["top_k"], dims["C"]
+    weights = (n_touched * d * f + d * fs) * 2
+    acts = (t * k * f + t * fs) * 2 + (t * k + t) * d * 2
+    return weights + acts
+
+
+def attention_flops(dims, cache_len, causal):
+    """Algorithmic flops of one layer's canvas attention: QK^T and PV over the visible keys (the
+    cache, then the canvas: all of it for the decoder, the causal prefix for the encoder)."""
+    c, hq, dh = dims["C"], dims["hq"], dims["dh"]
+    keys = cache_len + ((c + 1) / 2 if causal else c)
+    return 4.0 * hq * c * keys * dh
+
+
+def sampler_roofline(driver, timer, dev, vocab, steps=8):
+    """The standalone EB sampler (dg_eb_sample) on the standalone sampler workload: HBM rate of
+    its statistics kernel (one read of the logits) and the time of the whole call."""
+    import torch
+    rows = 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    cls = torch.randperm(rows, generator=g, device=dev)
+    z = torch.randn((rows, vocab), generator=g, device=dev)
+    peaked, moderate = cls[:77], cls[77:77 + 102]
+    z[moderate] *= 2.0 ** 0.5
+    flat = cls[179:]
+    z[flat] *= 0.1 ** 0.5
+    pos = torch.randint(0, vocab, (77,), generator=g, device=dev)
+    z[peaked, pos] = 12.0
+    logits = z.to(torch.bfloat16).view(1, rows, vocab)
+    del z
+    params = driver.eb_params()
+    state = driver.SamplerState(1, rows, dev)
+    out = driver.StepOut(1, rows, vocab, dev)
+    driver.canvas_init(params, state, vocab)
+    ws = driver.eb_sample(logits, 0, params, state, out)
+    torch.cuda.synchronize()
+    names = ["logit_stats", "stats_merge", "eb_commit", "candidates", "cand_apply"]
+    timer.reset()
+    timer.enable(names)
+    for s in range(steps):
+        driver.eb_sample(logits, s, params, state, out, ws)
+    torch.cuda.synchronize()
+    timer.enable([])
+    ms = {n: timer.read(n) for n in names}
+    t_stats = ms["logit_stats"][0] / max(ms["logit_stats"][1], 1) * 1e-3
+    total = sum(v[0] for v in ms.values()) / steps * 1e-3
+    nbytes = rows * vocab * 2
+    gbs = nbytes / t_stats / 1e9
+    return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), kernel="logit_stats",
+                bytes_per_launch=nbytes, avg_launch_us=round(t_stats * 1e6, 2),
+                sampler_call_us=round(total * 1e6, 2),
+                workload="bf16 logits [256 x 262144]: 30% peaked, 40% N(0,2), 30% N(0,0.1) rows")
 
 
 def measured_traffic():
@@ -160,17 +224,22 @@ def main():
     timer = driver.KernelTimer()
     torch.cuda.synchronize()
 
-    def one_pass():
-        """Generate `canvases` canvases back to back; returns decoder steps run."""
+    def one_pass(per_canvas=None):
+        """Generate `canvases` canvases back to back; returns decoder steps run (and appends the
+        steps of each canvas to `per_canvas`)."""
         kv.len[0] = args.cache
         steps = 0
         for _ in range(args.canvases):
             driver.canvas_init(params, state, dims["V"])
+            n = 0
             for s in range(params.max_steps):
                 driver.decoder_step(model, kv, s, params, state, out, ws)
-                steps += 1
+                n += 1
                 if bool(state.done.all()):
                     break
+            steps += n
+            if per_canvas is not None:
+                per_canvas.append(n)
             driver.kv_append_canvas(model, kv, state.canvas, ws)
         return steps
 
@@ -194,7 +263,8 @@ def main():
     # per-kernel breakdown from one more (untimed) pass with every class timed
     timer.reset()
     timer.enable()
-    one_pass()
+    per_canvas = []
+    one_pass(per_canvas)
     torch.cuda.synchronize()
     timer.enable([])
     per_class = {n: timer.read(n) for n in timer.names}
@@ -218,6 +288,39 @@ def main():
                     experts_touched=n_touched)
     kernel_ms = {n: round(v[0], 3) for n, v in per_class.items() if v[1]}
 
+    # the other kernels the path is judged on, from the per-class pass (HIP events per launch)
+    def rate(name):
+        ms, n = per_class[name]
+        return ms / max(n, 1) * 1e-3, n
+    t_lm, n_lm = rate("lmhead")
+    lm_flops = 2.0 * B * C * dims["V"] * dims["d"]
+    t_at, n_at = rate("attention")
+    at_flops = 0.0
+    for i, n in enumerate(per_canvas):
+        length = args.cache + i * C
+        at_flops += args.layers * (n * attention_flops(dims, length, False) +
+                                   attention_flops(dims, length, True))
+    t_dn, n_dn = rate("moe_down")
+    dn_bytes = moe_down_bytes(dims, n_touched)
+
+    def mfma_line(flops, t, n, kernel):
+        tf = flops / t / 1e12
+        return dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                    frac=round(tf / MFMA_BF16_PEAK_TFS, 4), kernel=kernel,
+                    avg_launch_us=round(t * 1e6, 2), launches=n)
+    rooflines = dict(
+        moe_gateup=roofline,
+        moe_down=dict(bound="hbm", achieved=round(dn_bytes / t_dn / 1e9, 1), peak=HBM_PEAK_GBS,
+                      unit="GB/s", frac=round(dn_bytes / t_dn / 1e9 / HBM_PEAK_GBS, 4),
+                      kernel="moe_down", bytes_per_launch=dn_bytes,
+                      avg_launch_us=round(t_dn * 1e6, 2), launches=n_dn),
+        lmhead=mfma_line(lm_flops, t_lm, n_lm, "lmhead (bf16 GEMM + tempered softmax statistics)"),
+        attention=dict(mfma_line(at_flops / max(n_at, 1), t_at, n_at,
+                                 "attention (+ split merge), averaged over the pass"),
+                       flops_per_launch=round(at_flops / max(n_at, 1))))
+    log("timing the standalone EB sampler")
+    rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -238,7 +341,8 @@ def main():
                     canvases_per_step=args.canvases, decoder_steps=total_steps),
         tokens_per_s=round(tokens / elapsed, 2),
         decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
-        roofline=roofline, cpu_baseline=cpu, kernel_ms_per_bench_step=kernel_ms)
+        roofline=roofline, cpu_baseline=cpu, rooflines=rooflines,
+        kernel_ms_per_bench_step=kernel_ms)
     print(json.dumps(line))
 
 

@@ -108,7 +108,7 @@ __device__ __forceinline__ SoftStats stats_merge(SoftStats x, SoftStats y) {
   SoftStats l = y_wins ? x : y;
   if (l.m == -INFINITY) return w;
   const float d = l.m - w.m;  // <= 0
-  const float s = exp2f(d);
+  const float s = __builtin_amdgcn_exp2f(d);
   w.r = w.r + (1.0f + l.r) * s;
   w.a = w.a + (l.a + d * (1.0f + l.r)) * s;
   return w;

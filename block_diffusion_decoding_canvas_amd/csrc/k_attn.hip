@@ -371,7 +371,10 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   }
 }
 
-// merge of split partials: one thread per (query row, 4 dh values)
+// merge of split partials: one thread per (query row, 4 dh values).  Splits are merged in split
+// order, 8 at a time: each group's running maxima, sums and partial rows are loaded together
+// (clamped split index, zero weight past the last split), so up to 8 splits cost one memory
+// round trip; the result so far is rescaled when a later group raises the maximum.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int hpg = a.Hq / a.Hkv;
@@ -383,12 +386,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const long long row = idx / per_row;  // (b, g, r)
   const int c4 = static_cast<int>(idx % per_row) * 4;
   const long long stride = rows;        // rows per split
-  float mmax = -INFINITY;
-  for (int sp = 0; sp < a.n_split; ++sp) mmax = fmaxf(mmax, a.ml_part[(sp * stride + row) * 2]);
-  float l = 0.f;
+  float mmax = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // splits merged in split order; each group of 8 is loaded together (clamped split index,
-  // zero weight past the last split)
   for (int sp0 = 0; sp0 < a.n_split; sp0 += 8) {
     float2 ml[8];
     float4 v[8];
@@ -397,6 +396,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
       const long long r2 = static_cast<long long>(min(sp0 + u, a.n_split - 1)) * stride + row;
       ml[u] = *reinterpret_cast<const float2*>(a.ml_part + r2 * 2);
       v[u] = *reinterpret_cast<const float4*>(a.o_part + r2 * DH + c4);
+    }
+    float gmax = mmax;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (sp0 + u < a.n_split) gmax = fmaxf(gmax, ml[u].x);
+    if (gmax != mmax) {   // a later group raised the maximum: rescale what is merged so far
+      const float r = (mmax == -INFINITY) ? 0.f : exp2f(mmax - gmax);
+      l *= r;
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+      mmax = gmax;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {

@@ -25,28 +25,28 @@ __device__ __forceinline__ u32x4 ld_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// statistics of 8 scaled logits given in increasing vocabulary order (4 at n_a.., 4 at n_b..)
+// statistics of 8 scaled logits given in increasing vocabulary order (4 at n_a.., 4 at n_b..):
+// the maximum from a max tree, its first position (lowest index on ties) from a reverse scan,
+// 2^(y - m) with the hardware exp2 (arguments <= 0).  Non-finite inputs leave r or a NaN (+inf
+// through inf - inf, NaN directly, -inf through -inf * 0), which the caller turns into the flag.
 __device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
-  float m = y[0];
-  int k_best = 0;
+  const float m = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                        fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+  int k_best = 7;
 #pragma unroll
-  for (int k = 1; k < 8; ++k)
-    if (y[k] > m) {
-      m = y[k];
-      k_best = k;
-    }
+  for (int k = 6; k >= 0; --k) k_best = (y[k] == m) ? k : k_best;
   float r = 0.f, acc = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float d = y[k] - m;
-    const float e = (k == k_best) ? 0.f : exp2f(d);
+    const float e = (k == k_best) ? 0.f : __builtin_amdgcn_exp2f(d);
     r += e;
-    acc += d * e;
+    acc = __builtin_fmaf(d, e, acc);
   }
   SoftStats s;
   s.m = m;
   s.idx = k_best < 4 ? n_a + k_best : n_b + (k_best - 4);
-  s.r = r;
+  s.r = (r != r || acc != acc) ? NAN : r;
   s.a = acc;
   return s;
 }
@@ -353,11 +353,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     }
   }
   if constexpr (EPI == EPI_LMHEAD) {
-    // bf16 logits; statistics of the rounded logits, merged over the 4 lanes of a token and then
-    // over the waves through LDS (the staging buffers are free after this barrier)
+    // bf16 logits; each lane's statistics of the rounded, scaled logits it holds for a token
+    // (8 rows) go to LDS as one of the token's WAVES * 4 partials (the staging buffers are free
+    // after this barrier), then TPT threads per token merge them in a fixed order
     __syncthreads();
+    constexpr int NP = WAVES * 4;          // partials per token: (wave, lane group)
+    constexpr int TPT = NTHR / MT;         // merging threads per token
+    static_assert(TPT >= 1 && (TPT & (TPT - 1)) == 0 && NP % TPT == 0 && TPT <= 64,
+                  "token partials must split evenly over a power-of-two thread group");
+    static_assert(sizeof(SoftStats) * NP * MT <= sizeof(xs_lds), "LDS too small for stats");
     SoftStats* red = reinterpret_cast<SoftStats*>(&xs_lds[0][0]);
-    static_assert(sizeof(SoftStats) * WAVES * MT <= sizeof(xs_lds), "LDS too small for stats");
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       const int t = tb * 16 + r16;
@@ -376,31 +381,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
         y[rt * 4 + 3] = __uint_as_float(pk.y & 0xffff0000u) * a.inv_t_log2e;
       }
       SoftStats st = stats8(y, feat[0] + 4 * g, feat[1] + 4 * g);
-      bool bad = false;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) bad |= !(fabsf(y[k]) <= 3.402823466e38f);
-      if (bad) st.r = NAN;
-#pragma unroll
-      for (int o2 = 16; o2 <= 32; o2 <<= 1) {
-        const SoftStats u = stats_shfl_xor(st, o2);
-        const bool nan = isnan(st.r) || isnan(u.r);
-        st = stats_merge(st, u);
-        if (nan) st.r = NAN;
-      }
-      if (g == 0) red[wave * MT + t] = st;
+      if (!wave_live) st = SoftStats{-INFINITY, 0x7fffffff, 0.f, 0.f};   // rows past N: neutral
+      red[(wave * 4 + g) * MT + t] = st;
     }
     __syncthreads();
-    for (int t = tid; t < nrows; t += NTHR) {
-      SoftStats st = red[t];
+    {
+      // thread -> (token tid / TPT, partials (tid % TPT) * NP / TPT ...); then the group's
+      // threads (consecutive lanes) combine by xor shuffles
+      const int t = tid / TPT, part0 = (tid % TPT) * (NP / TPT);
+      SoftStats st = red[part0 * MT + t];
       bool nan = isnan(st.r);
-      for (int w = 1; w < WAVES; ++w) {
-        if (n0 + w * 32 >= N) break;
-        const SoftStats u = red[w * MT + t];
+#pragma unroll
+      for (int p = 1; p < NP / TPT; ++p) {
+        const SoftStats u = red[(part0 + p) * MT + t];
+        nan |= isnan(u.r);
+        st = stats_merge(st, u);
+      }
+#pragma unroll
+      for (int o2 = 1; o2 < TPT; o2 <<= 1) {
+        const SoftStats u = stats_shfl_xor(st, o2);
         nan |= isnan(u.r);
         st = stats_merge(st, u);
       }
       if (nan) st.r = NAN;
-      a.part[static_cast<long long>(row0 + t) * a.n_nblk + nb] = st;
+      if (tid % TPT == 0 && t < nrows) a.part[static_cast<long long>(row0 + t) * a.n_nblk + nb] = st;
     }
     return;
   }

@@ -17,32 +17,31 @@ namespace dg {
 namespace {
 
 constexpr int kStatsThreads = 256;
-constexpr int kStatsChunk = 16384;   // vocabulary entries per statistics workgroup
+constexpr int kStatsChunk = 32768;   // vocabulary entries per statistics workgroup
 constexpr int kCandThreads = 256;
 constexpr int kCandChunk = 4096;     // vocabulary entries per candidate workgroup
 
-// Fold a group of 8 consecutive logits (indices base .. base+7) into running statistics.
-// The group is visited in index order, so the lowest index wins ties.
-__device__ __forceinline__ void stats_fold8(SoftStats& s, bool& bad, const uint4 raw, int base,
-                                            float c) {
-  float y[8];
+// Fold a group of 8 consecutive logits (indices base .. base+7) into running statistics of
+// y = z c (c = log2(e) / T > 0, so the maximum and its position are those of z).  The group's
+// maximum comes from a max tree and its first position from a reverse scan, so the lowest index
+// wins ties; y - m is one fma.  Non-finite inputs need no separate test: +inf makes d = inf -
+// inf, a NaN propagates, and -inf gives d * e = -inf * 0, so r or a ends NaN (checked once per
+// thread).  2^d uses the hardware exp2 (d <= 0; results below 2^-126 flush to 0, nothing at the
+// scale of the sums, which hold the maximum's 1 implicitly).
+__device__ __forceinline__ void stats_fold8(SoftStats& s, const uint4 raw, int base, float c) {
+  float z[8];
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    y[2 * k] = __uint_as_float(w[k] << 16) * c;
-    y[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * c;
+    z[2 * k] = __uint_as_float(w[k] << 16);
+    z[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
   }
-  float gm = y[0];
-  int gi = 0;
+  const float gz = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  const float gm = gz * c;
+  int gi = 7;
 #pragma unroll
-  for (int k = 1; k < 8; ++k) {
-    if (y[k] > gm) {
-      gm = y[k];
-      gi = k;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) bad |= !(fabsf(y[k]) <= FLT_MAX);
+  for (int k = 6; k >= 0; --k) gi = (z[k] == gz) ? k : gi;
   int skip = -1;
   if (gm > s.m) {
     if (s.m == -INFINITY) {
@@ -50,7 +49,7 @@ __device__ __forceinline__ void stats_fold8(SoftStats& s, bool& bad, const uint4
       s.a = 0.f;
     } else {
       const float d = s.m - gm;
-      const float sc = exp2f(d);
+      const float sc = __builtin_amdgcn_exp2f(d);
       s.a = (s.a + d * (1.0f + s.r)) * sc;
       s.r = (1.0f + s.r) * sc;
     }
@@ -58,12 +57,13 @@ __device__ __forceinline__ void stats_fold8(SoftStats& s, bool& bad, const uint4
     s.idx = base + gi;
     skip = gi;
   }
+  const float neg_m = -s.m;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float d = y[k] - s.m;
-    const float e = (k == skip) ? 0.f : exp2f(d);
+    const float d = __builtin_fmaf(z[k], c, neg_m);
+    const float e = (k == skip) ? 0.f : __builtin_amdgcn_exp2f(d);
     s.r += e;
-    s.a += d * e;
+    s.a = __builtin_fmaf(d, e, s.a);
   }
 }
 
@@ -97,12 +97,22 @@ __global__ __launch_bounds__(kStatsThreads) void k_logit_stats(EbArgs a) {
   const int v1 = min(a.V, v0 + kStatsChunk);
   const uint16_t* z = a.logits + static_cast<size_t>(row) * a.V;
   SoftStats s = stats_empty();
-  bool bad = false;
-  for (int v = v0 + threadIdx.x * 8; v < v1; v += kStatsThreads * 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(z + v);
-    stats_fold8(s, bad, raw, v, a.inv_t_log2e);
+  // the thread's groups of 8 are loaded NG at a time, then folded in index order
+  constexpr int NG = 8;
+  for (int v00 = v0 + threadIdx.x * 8; v00 < v1; v00 += NG * kStatsThreads * 8) {
+    uint4 raw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int v = min(v00 + g * kStatsThreads * 8, v1 - 8);
+      raw[g] = *reinterpret_cast<const uint4*>(z + v);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int v = v00 + g * kStatsThreads * 8;
+      if (v < v1) stats_fold8(s, raw[g], v, a.inv_t_log2e);
+    }
   }
-  if (bad) s.r = NAN;
+  if (isnan(s.r) || isnan(s.a)) s.r = NAN;
   s = stats_block_reduce(s);
   if (threadIdx.x == 0) a.part[static_cast<size_t>(row) * a.n_part + chunk] = s;
 }
