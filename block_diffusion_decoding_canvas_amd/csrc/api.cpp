@@ -591,6 +591,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   g.K = g.K_sh = d.d_model; g.N = d.ffn_inner; g.N_sh = d.shared_inner;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.act; g.ldo = fmax; g.ksplit = 1;
+  g.sh_tiles = (T + dg::moe_tile_rows() - 1) / dg::moe_tile_rows();
   const long long rows = static_cast<long long>(T) * d.top_k + T;
   if (fp8) {
     // e4m3 codes of u (gathered through the permutation), fp32 SwiGLU output, then its codes
@@ -612,6 +613,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   g.K = d.ffn_inner; g.K_sh = d.shared_inner; g.N = g.N_sh = d.d_model;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.y; g.ldo = d.d_model; g.ksplit = 1;
+  g.sh_tiles = (T + dg::moe_tile_rows() - 1) / dg::moe_tile_rows();
   if (fp8) {
     g.X = reinterpret_cast<const uint16_t*>(w.act8); g.x_scale = w.act8s;
     g.w_scale = lw.s_down; g.wsc_estride = d.d_model; g.w_scale_sh = lw.ss_down;

@@ -198,6 +198,9 @@ struct WGemmArgs {
   // 1 KiB of readable device memory (workspace) that the weight ring's past-the-end loads read
   // instead of weights; its contents are never used
   const uint8_t* hot;
+  // grouped products: the shared expert's tiles (the last sh_tiles of the tile list; 0 = none)
+  // are ordered token tile fastest, so its weights are read into one L2 per row block
+  int sh_tiles;
 };
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };

@@ -79,11 +79,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   // grouped products put a tile's row blocks together (its gathered token rows are shared);
   // dense products put the token tiles of one row block together, so every weight band is
   // fetched from HBM into one L2 and reused there by all token tiles
-  int slot;
+  int slot, n_ch = 0;
   if (a.chunks) {
     // the grid is sized for the most tiles a routing can produce; the active slots (known only
     // on the device) are spread evenly over the 8 XCDs, a contiguous run on each
-    const int n_active = *a.n_chunks * a.ksplit * a.n_nblk;
+    n_ch = *a.n_chunks;
+    const int n_active = n_ch * a.ksplit * a.n_nblk;
     const int per = (n_active + 7) >> 3;
     const int j = blockIdx.x >> 3;
     slot = (blockIdx.x & 7) * per + j;
@@ -93,10 +94,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   }
   int nb, ks, tile;
   if (a.chunks) {
-    nb = slot % a.n_nblk;
-    const int tk = slot / a.n_nblk;
-    ks = tk % a.ksplit;
-    tile = tk / a.ksplit;
+    const int sh_first = n_ch - a.sh_tiles;   // the shared expert's tiles close the list
+    if (a.sh_tiles > 0 && a.ksplit == 1 && slot >= sh_first * a.n_nblk) {
+      // the shared expert's tiles of one row block in consecutive slots (one XCD, one L2)
+      const int j = slot - sh_first * a.n_nblk;
+      nb = j / a.sh_tiles;
+      tile = sh_first + j % a.sh_tiles;
+      ks = 0;
+    } else {
+      nb = slot % a.n_nblk;
+      const int tk = slot / a.n_nblk;
+      ks = tk % a.ksplit;
+      tile = tk / a.ksplit;
+    }
   } else {
     tile = slot % a.grid_tiles;
     const int rest = slot / a.grid_tiles;
