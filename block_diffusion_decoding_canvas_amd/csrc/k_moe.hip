@@ -25,19 +25,27 @@ __device__ __forceinline__ u32x4 ld_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// statistics of 8 scaled logits given in increasing vocabulary order (4 at n_a.., 4 at n_b..):
-// the maximum from a max tree, its first position (lowest index on ties) from a reverse scan,
-// 2^(y - m) with the hardware exp2 (arguments <= 0).  Non-finite inputs leave r or a NaN (+inf
-// through inf - inf, NaN directly, -inf through -inf * 0), which the caller turns into the flag.
-__device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
-  const float m = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
-                        fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-  int k_best = 7;
+// statistics of NV scaled logits in increasing vocabulary order, y[k] the logit of vocabulary
+// row n0 + (k / 4) * 16 + k % 4 (4 rows of each of NV / 4 16-row tiles): the maximum from a max
+// tree, its first position (lowest index on ties) from a reverse scan, 2^(y - m) with the
+// hardware exp2 (arguments <= 0).  Non-finite inputs leave r or a NaN (+inf through inf - inf,
+// NaN directly, -inf through -inf * 0), which the caller turns into the flag.
+template <int NV>
+__device__ __forceinline__ SoftStats stats_rows(const float* y, int n0) {
+  float mx[NV];
 #pragma unroll
-  for (int k = 6; k >= 0; --k) k_best = (y[k] == m) ? k : k_best;
+  for (int k = 0; k < NV; ++k) mx[k] = y[k];
+#pragma unroll
+  for (int w = NV / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < w; ++k) mx[k] = fmaxf(mx[k], mx[k + w]);
+  const float m = mx[0];
+  int k_best = NV - 1;
+#pragma unroll
+  for (int k = NV - 2; k >= 0; --k) k_best = (y[k] == m) ? k : k_best;
   float r = 0.f, acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const float d = y[k] - m;
     const float e = (k == k_best) ? 0.f : __builtin_amdgcn_exp2f(d);
     r += e;
@@ -45,7 +53,7 @@ __device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
   }
   SoftStats s;
   s.m = m;
-  s.idx = k_best < 4 ? n_a + k_best : n_b + (k_best - 4);
+  s.idx = n0 + (k_best >> 2) * 16 + (k_best & 3);
   s.r = (r != r || acc != acc) ? NAN : r;
   s.a = acc;
   return s;
@@ -61,8 +69,7 @@ __device__ __forceinline__ SoftStats stats8(const float* y, int n_a, int n_b) {
 // logits scaled by log2(e)/T.
 template <int EPI, int NTB, int SEG, int WAVES, int PS, bool F8 = false, int RT = 2>
 __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
-  static_assert(RT == 2 || (EPI != EPI_SWIGLU && EPI != EPI_LMHEAD), "gate/up pairs and the LM-head "
-                "statistics take two row tiles per wave");
+  static_assert(RT == 2 || EPI != EPI_SWIGLU, "gate/up pairs take two row tiles per wave");
   constexpr int NTHR = WAVES * 64;
   constexpr int EB = F8 ? 1 : 2;                    // bytes per element
   constexpr int KSTEP = F8 ? 64 : 32;               // k per step
@@ -164,42 +171,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     }
   }
 
-  // token staging: thread loads XL 16-byte pieces of the MT x SEG segment.  Every load is issued
-  // unconditionally from an in-range address (rows past the tile read its last row, k past the
-  // range reads the range's last piece) and masked afterwards: conditional loads would make the
-  // compiler wait for every outstanding load (the weight ring included) before the LDS store.
-  const uint8_t* X = reinterpret_cast<const uint8_t*>(a.X);
-  const uint8_t* xsrc[XL];
-  int xdst[XL], xcol[XL];
-  uint32_t xrow_mask[XL];
+  // token staging: piece it of a thread is the 16 bytes at column xc16 of segment row
+  // xr0 + it * RS.  Every load is issued unconditionally from an in-range address (rows past the
+  // tile read its last row, k past the range reads the range's last piece) and the piece is
+  // zeroed at the store: conditional loads would make the compiler wait for every outstanding
+  // load (the weight ring included) before the LDS store.  Row addresses are 32-bit byte offsets
+  // from a uniform base (the tile's first row, or row 0 of a gathered matrix: fewer than 65,536
+  // rows of at most 16 KiB), so that a thread's staging state is one register per piece
+  constexpr int PPR = SEGB / 16;                    // 16-byte pieces per staged row
+  constexpr int RS = NTHR / PPR;                    // rows between a thread's pieces
+  static_assert(NTHR % PPR == 0, "a segment row must split evenly over the threads");
+  const int xr0 = tid / PPR, xc16 = tid % PPR;
+  const int xcol = xc16 * (16 / EB);                // element column in the segment
+  const uint8_t* Xb = reinterpret_cast<const uint8_t*>(a.X) +
+                      (a.x_rows ? 0ll : static_cast<long long>(row0) * a.ldx * EB);
+  uint32_t xoff[XL];
 #pragma unroll
   for (int it = 0; it < XL; ++it) {
-    const int idx = tid + it * NTHR;
-    const int r = idx / (SEGB / 16), c16 = idx % (SEGB / 16);
-    const int rr = row0 + min(r, nrows - 1);   // rows past the tile repeat its last row
-    const int xr = a.x_rows ? a.x_rows[rr] : rr;
-    xsrc[it] = X + (static_cast<long long>(xr) * a.ldx) * EB;
-    xdst[it] = r * STRIDE + c16 * 16;
-    xcol[it] = c16 * (16 / EB);
-    xrow_mask[it] = r < nrows ? 0xffffffffu : 0u;   // rows past the tile are zero-filled
+    const int r = min(xr0 + it * RS, nrows - 1);   // rows past the tile repeat its last row
+    const int xr = a.x_rows ? a.x_rows[row0 + r] : r;
+    xoff[it] = static_cast<uint32_t>(xr) * static_cast<uint32_t>(a.ldx * EB);
   }
   const int nseg = (k_end - k_beg + SEG - 1) / SEG;
   u32x4 xr_[XL];
-  uint32_t xm_[XL];                          // mask of the pieces in flight, applied at the store
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto load_seg = [&](int sg) __attribute__((always_inline)) {
-    const int k0 = k_beg + sg * SEG;
-#pragma unroll
-    for (int it = 0; it < XL; ++it) {
-      const int k = k0 + xcol[it];
-      const int kc = min(k, k_end - 16 / EB);
-      xr_[it] = ld16(xsrc[it] + static_cast<long long>(kc) * EB);
-      xm_[it] = k < k_end ? xrow_mask[it] : 0u;
-    }
+  // piece it of segment sg (segments past the range read an in-range piece, stored as zeros)
+  auto load_piece = [&](int it, int sg) __attribute__((always_inline)) {
+    const int kc = min(k_beg + sg * SEG + xcol, k_end - 16 / EB);
+    xr_[it] = ld16(Xb + (xoff[it] + static_cast<uint32_t>(kc * EB)));
   };
-  auto store_seg = [&](int buf) __attribute__((always_inline)) {
+  // piece it, holding segment sg, into buffer sg & 1 (zeros past the tile's rows or the range)
+  auto store_piece = [&](int it, int sg) __attribute__((always_inline)) {
+    const bool ok = xr0 + it * RS < nrows && k_beg + sg * SEG + xcol < k_end;
+    st16(&xs_lds[sg & 1][(xr0 + it * RS) * STRIDE + xc16 * 16], ok ? xr_[it] : zero4);
+  };
+  auto load_seg = [&](int sg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < XL; ++it) st16(&xs_lds[buf][xdst[it]], xr_[it] & xm_[it]);
+    for (int it = 0; it < XL; ++it) load_piece(it, sg);
+  };
+  auto store_seg = [&](int sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < XL; ++it) store_piece(it, sg);
   };
 
   f32x4 acc[RT][NTB];
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   // the next segment's pieces go to the other LDS buffer, then the one after is loaded
   auto next_seg = [&](int sg) __attribute__((always_inline)) {
     if (sg + 1 < nseg) {
-      store_seg((sg + 1) & 1);
+      store_seg(sg + 1);
       if (sg + 2 < nseg) load_seg(sg + 2);
     }
   };
@@ -293,14 +305,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       // With 4 or more token blocks (the dense products, run at one or two waves per SIMD) the
       // token fragments of the whole segment (fragment f = step u * NTB + block tb) stream
       // through a D-deep register ring, each LDS read issued D fragments ahead of its MFMAs, so
-      // the LDS latency hides under independent MFMAs; the grouped expert products (2 token
-      // blocks, several waves per SIMD) keep their registers for occupancy instead
+      // the LDS latency hides under independent MFMAs, and the token staging (the next
+      // segment's pieces into the other buffer, free since the last barrier, then the pieces of
+      // the one after from L2) is spread over the segment instead of waiting for its end; the
+      // grouped expert products (2 token blocks, several waves per SIMD) keep their registers
+      // for occupancy instead
       if constexpr (NTB < 4) {
 #pragma unroll
         for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
+        next_seg(sg);
       } else {
         constexpr int NF = SSTEPS * NTB;
         constexpr int D = NF < (NTB == 4 ? 8 : 4) ? NF : (NTB == 4 ? 8 : 4);
+        static_assert(NF % XL == 0, "token pieces must spread evenly over the fragments");
+        constexpr int EVERY = NF / XL;
         const uint8_t* xf = xb + r16 * STRIDE + g * 16;
         u32x4 br[D];
 #pragma unroll
@@ -324,9 +342,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
             load_step(s_beg + u + PS, wst[u % PS]);
             __builtin_amdgcn_sched_barrier(0);
           }
+          if (f % EVERY == EVERY - 1) {
+            // unconditional: past the last segment the store fills the free buffer with
+            // zeros and the load reads an in-range piece
+            store_piece(f / EVERY, sg + 1);
+            load_piece(f / EVERY, sg + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-      next_seg(sg);
     } else {
       // the last, partial segment (or a wave past the last output row, which only joins the
       // barriers)
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   }
   if constexpr (EPI == EPI_LMHEAD) {
     // bf16 logits; each lane's statistics of the rounded, scaled logits it holds for a token
-    // (8 rows) go to LDS as one of the token's WAVES * 4 partials (the staging buffers are free
+    // (4 rows of each of its RT tiles) go to LDS as one of the token's WAVES * 4 partials (the staging buffers are free
     // after this barrier), then TPT threads per token merge them in a fixed order
     __syncthreads();
     constexpr int NP = WAVES * 4;          // partials per token: (wave, lane group)
@@ -378,9 +402,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       const int t = tb * 16 + r16;
       const bool ok = t < nrows && wave_live;
       uint16_t* o = static_cast<uint16_t*>(a.out) + static_cast<long long>(row0 + t) * a.ldo;
-      float y[8];
+      float y[4 * RT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         uint2 pk;
         pk.x = pack_bf2(acc[rt][tb][0], acc[rt][tb][1]);
         pk.y = pack_bf2(acc[rt][tb][2], acc[rt][tb][3]);
@@ -390,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
         y[rt * 4 + 2] = __uint_as_float(pk.y << 16) * a.inv_t_log2e;
         y[rt * 4 + 3] = __uint_as_float(pk.y & 0xffff0000u) * a.inv_t_log2e;
       }
-      SoftStats st = stats8(y, feat[0] + 4 * g, feat[1] + 4 * g);
+      SoftStats st = stats_rows<4 * RT>(y, feat[0] + 4 * g);
       if (!wave_live) st = SoftStats{-INFINITY, 0x7fffffff, 0.f, 0.f};   // rows past N: neutral
       red[(wave * 4 + g) * MT + t] = st;
     }
@@ -494,7 +518,7 @@ hipError_t launch_stream(WGemmArgs a, hipStream_t s) {
 }  // namespace
 
 int moe_tile_rows() { return 32; }
-int gemm_lmhead_rows_per_block() { return 8 * 32; }
+int gemm_lmhead_rows_per_block() { return 256; }   // both LM-head shapes below
 
 hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_SWIGLU, 2, 256, 4, 4>(a, s);
@@ -509,7 +533,7 @@ hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_F32, 8, 256, 4, 4>(a, s);
 }
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_LMHEAD, 16, 128, 8, 2>(a, s);
+  return launch_stream<EPI_LMHEAD, 16, 128, 8, 4>(a, s);
 }
 
 hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s) {
