@@ -8,17 +8,21 @@
 // Layout of the work: one workgroup = (canvas b, KV head g, 128 query rows, one split of the
 // key range).  The query rows of a KV head are its Hq/Hkv query heads
 // times the canvas positions, so the K/V tiles staged in LDS serve every query head that reads
-// them.  Keys are processed in tiles of 64 (K tile [key][dh] and V tile transposed [dh][key] in
-// LDS, double buffered: tile t + 1 is staged while tile t is computed, one barrier per tile).
+// them.  Keys are processed in tiles of 64 (K and V tiles [key][dh] in LDS, double buffered: tile
+// t + 1 is staged while tile t is computed, one barrier per tile).
 // Up to head_dim 128 there are 4 waves (one per SIMD), each holding 32 query rows as two 16-row
 // MFMA tiles, so every K and V^T fragment read from LDS feeds two MFMAs; at head_dim 256 the
 // registers hold one 16-row tile per wave and there are 8 waves.  Each wave computes S^T = K Q^T, so the probabilities come out of the MFMA in the
 // lane layout that the P V product takes as its B operand (O^T = V^T P^T) with no shuffle.
-// LDS rows are padded to strides whose 16-byte fragment reads run at the full LDS rate, and the
-// keys of each 32-key group of V^T are stored in the order the B operand holds them, so one
-// 16-byte read gives a lane its 8 keys.  Splits of the key range write unnormalised partial
-// outputs with their running max and sum, merged afterwards by log-sum-exp.
+// Staging loads are coalesced (consecutive lanes on consecutive 16-byte pieces of a key row) and
+// both tiles are stored row-major with 16-byte stores; the V^T fragments of the P V product come
+// from CDNA4's transposing LDS read, 8 keys of one dh per lane from two 8-byte reads.  LDS rows
+// are padded to a stride at which the 16-byte K reads and the transposing V reads run at the
+// full LDS rate.  Splits of the key range write unnormalised partial outputs with their running
+// max and sum, merged afterwards by log-sum-exp.
 #include "dg_internal.h"
+
+#include <type_traits>
 
 namespace dg {
 namespace {
@@ -31,26 +35,24 @@ struct AttnCfg {
   static constexpr int QT = DH >= 256 ? 1 : 2;  // 16-row query tiles per wave
   static constexpr int NWAVE = QB / (16 * QT);  // waves per workgroup
   static constexpr int NTHR = NWAVE * 64;
-  static constexpr int KS_STRIDE = DH + 16;  // bf16 per K row in LDS
-  static constexpr int VT_STRIDE = KT + 16;  // bf16 per transposed V row in LDS
+  static constexpr int KS_STRIDE = DH + 16;  // bf16 per K or V row in LDS
   static constexpr int NKS = (DH + 31) / 32; // 32-wide dh steps of QK^T
   static constexpr int NDT = DH / 16;        // 16-row dh tiles of O^T
   static constexpr int KBUF = KT * KS_STRIDE;
-  static constexpr int VBUF = DH * VT_STRIDE;
-  static constexpr int KCH = DH / 8;                          // 16-byte chunks per key row
-  // staging: thread t holds key t % KT of the tile (K) and key pair t % (KT / 2) (V), with the
-  // chunks t / KT + j * KSTEP, j < KIT (K) and t / (KT / 2) + j * VSTEP, j < VIT (V)
-  static constexpr int KSTEP = NTHR / KT, VSTEP = NTHR / (KT / 2);
-  static constexpr int KIT = (KCH + KSTEP - 1) / KSTEP;
-  static constexpr int VIT = (KCH + VSTEP - 1) / VSTEP;
+  static constexpr int KCH = DH / 8;         // 16-byte pieces per key row
+  // staging: piece p = t + j * NTHR (j < PIT) of thread t is chunk p % KCH of key p / KCH
+  static constexpr int NPC = KT * KCH;       // pieces per tile (K or V)
+  static constexpr int PIT = (NPC + NTHR - 1) / NTHR;
   static constexpr int RING = 8 / QT;  // fragment ring depth: 8 MFMAs of cover
 };
 
-// position of key k of a tile in a V^T row: inside each 32-key group, key 16 h + 4 l + j goes to
-// 8 l + 4 h + j, the order in which lane group l of the P V product's B operand holds its keys
-__device__ __forceinline__ int vt_pos(int k) {
-  const int q = k & 31;
-  return (k & ~31) + 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// CDNA4 transposing LDS read of 16-bit data: within each group of 16 lanes, lane 4a + b receives
+// element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12 (in that order)
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
 template <int DH>
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   using C = AttnCfg<DH>;
   constexpr int QT = C::QT, NTHR = C::NTHR;
   __shared__ __align__(16) uint16_t ks[2][C::KBUF];
-  __shared__ __align__(16) uint16_t vt[2][C::VBUF];
+  __shared__ __align__(16) uint16_t vs[2][C::KBUF];
 
   // logical block -> (canvas, KV head, key split, query block); the query blocks that share a
   // KV head and split are consecutive, so they run on one XCD and share its L2 for K/V tiles
@@ -107,9 +109,6 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
       const int d0 = ks_ * 32 + lg * 8;
       qf[ks_][q] = (d0 < DH) ? ld16(qp + d0) : zero4;
-      // opaque to the compiler: the fragments stay in registers for the whole key range
-      // instead of being re-loaded (behind the tile prefetches) in every tile
-      asm volatile("" : "+v"(qf[ks_][q]));
     }
   }
 
@@ -146,14 +145,11 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   qi_lo = __builtin_amdgcn_readfirstlane(qi_lo);
   qi_hi = __builtin_amdgcn_readfirstlane(qi_hi);
 
-  // staging.  K pieces: (key kk, 16-byte chunk c), consecutive threads on consecutive keys; V
-  // items: (key pair p, chunk c), the two keys' rows written transposed.  K of the next tile is
-  // fetched before this tile's S^T and stored after it; V of the next tile is fetched then and
-  // stored after the P V product.
-  // every load is unconditional: a key past the range reads the last key of the range (finite
-  // data whose scores are masked to -inf, so its probability is 0), and the cache or canvas row
-  // is chosen by bit arithmetic on both (clamped) addresses, so no branch makes the compiler
-  // wait for loads in flight
+  // staging: K of the next tile is fetched before this tile's S^T and stored after it; V of the
+  // next tile is fetched then and stored after the P V product.  Every load is unconditional: a
+  // key past the range reads the last key of the range (finite data whose scores are masked to
+  // -inf, so its probability is 0), and the cache or canvas row is chosen by bit arithmetic on
+  // both (clamped) addresses, so no branch makes the compiler wait for loads in flight
   auto kv_row = [&](int kk, const uint16_t* cache, const uint16_t* canvas) -> const uint16_t* {
     const int kc = min(kk, nk - 1);
     const uintptr_t pc = reinterpret_cast<uintptr_t>(
@@ -163,55 +159,34 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
     return reinterpret_cast<const uint16_t*>((pc & m) | (pn & ~m));
   };
-  constexpr bool KFULL = C::KCH % C::KSTEP == 0;   // every thread has all its K pieces
-  constexpr bool VFULL = C::KCH % C::VSTEP == 0;   // and V items
-  const int k_key = tid % KT, k_c0 = tid / KT;             // this thread's K key and first chunk
-  const int v_pair = tid % (KT / 2), v_c0 = tid / (KT / 2);  // its V key pair and first chunk
-  u32x4 pk[C::KIT], pv0[C::VIT], pv1[C::VIT];
+  constexpr bool PFULL = C::NPC % NTHR == 0;   // every thread has all its pieces
+  int p_key[C::PIT], p_off[C::PIT];            // piece -> key in the tile, offset in a row
+#pragma unroll
+  for (int it = 0; it < C::PIT; ++it) {
+    const int pc = min(tid + it * NTHR, C::NPC - 1);
+    p_key[it] = pc / C::KCH;
+    p_off[it] = (pc % C::KCH) * 8;
+  }
+  u32x4 pk[C::PIT], pv[C::PIT];
   auto fetch_k = [&](int tt) __attribute__((always_inline)) {
-    const uint16_t* row = kv_row(tt * KT + k_key, kcache, kcanvas);
 #pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int c = min(k_c0 + it * C::KSTEP, C::KCH - 1);
-      pk[it] = ld16(row + c * 8);
-    }
-  };
-  auto stage_k = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int c = k_c0 + it * C::KSTEP;
-      if (!KFULL && c >= C::KCH) continue;
-      st16(ks[buf] + k_key * C::KS_STRIDE + c * 8, pk[it]);
-    }
+    for (int it = 0; it < C::PIT; ++it)
+      pk[it] = ld16(kv_row(tt * KT + p_key[it], kcache, kcanvas) + p_off[it]);
   };
   auto fetch_v = [&](int tt) __attribute__((always_inline)) {
-    const int k0 = tt * KT + 2 * v_pair;
-    const uint16_t* row0 = kv_row(k0, vcache, vcanvas);
-    const uint16_t* row1 = kv_row(k0 + 1, vcache, vcanvas);
 #pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int c = min(v_c0 + it * C::VSTEP, C::KCH - 1);
-      pv0[it] = ld16(row0 + c * 8);
-      pv1[it] = ld16(row1 + c * 8);
+    for (int it = 0; it < C::PIT; ++it)
+      pv[it] = ld16(kv_row(tt * KT + p_key[it], vcache, vcanvas) + p_off[it]);
+  };
+  auto stage = [&](uint16_t* dst, const u32x4 (&pr)[C::PIT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < C::PIT; ++it) {
+      if (!PFULL && tid + it * NTHR >= C::NPC) continue;
+      st16(dst + p_key[it] * C::KS_STRIDE + p_off[it], pr[it]);
     }
   };
-  auto stage_v = [&](int buf) __attribute__((always_inline)) {
-    const int w0 = vt_pos(2 * v_pair) >> 1;   // keys 2p, 2p+1 stay adjacent: one 32-bit word
-#pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int c = v_c0 + it * C::VSTEP;
-      if (!VFULL && c >= C::KCH) continue;
-      // V^T[dh][key]: each 32-bit store holds keys 2p and 2p+1 of one dh
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a0 = pv0[it][e], a1 = pv1[it][e];
-        uint32_t* row0 = reinterpret_cast<uint32_t*>(vt[buf] + (c * 8 + 2 * e) * C::VT_STRIDE) + w0;
-        uint32_t* row1 = reinterpret_cast<uint32_t*>(vt[buf] + (c * 8 + 2 * e + 1) * C::VT_STRIDE) + w0;
-        *row0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // low halves: key 2p, key 2p+1
-        *row1 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // high halves
-      }
-    }
-  };
+  auto stage_k = [&](int buf) __attribute__((always_inline)) { stage(ks[buf], pk); };
+  auto stage_v = [&](int buf) __attribute__((always_inline)) { stage(vs[buf], pv); };
 
   const float sc = a.scale_log2e;
   if (t_beg < t_end) {
@@ -220,14 +195,24 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     stage_k(0);
     stage_v(0);
   }
+  // the query fragments, opaque to the compiler from here on (after the first tile's loads are
+  // issued, so that all of them overlap): they stay in registers for the whole key range instead
+  // of being re-loaded in every tile
+#pragma unroll
+  for (int q = 0; q < QT; ++q)
+#pragma unroll
+    for (int ks_ = 0; ks_ < C::NKS; ++ks_) asm volatile("" : "+v"(qf[ks_][q]));
   __syncthreads();
-  for (int tt = t_beg; tt < t_end; ++tt) {
+  // one key tile; STAGE: also stage tile tt + 1 into the other buffers.  Every tile but the last
+  // stages, so the loop body is straight-line code (a branch around the staging would make the
+  // compiler wait for the next tile's loads as soon as they are issued)
+  auto tile = [&](int tt, auto stage_tag) __attribute__((always_inline)) {
+    constexpr bool STAGE = decltype(stage_tag)::value;
     const int kbase = tt * KT;
     const int cur = (tt - t_beg) & 1;
-    const bool more = tt + 1 < t_end;
     const uint16_t* ksb = ks[cur];
-    const uint16_t* vtb = vt[cur];
-    if (more) fetch_k(tt + 1);
+    const uint16_t* vsb = vs[cur];
+    if constexpr (STAGE) fetch_k(tt + 1);
 
     // S^T[key][q] for 4 sub-tiles of 16 keys and the wave's query tiles (raw dot products).  The
     // K fragments run ks-major through a ring read from LDS RING fragments ahead of use (pinned
@@ -253,14 +238,22 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       if (i + KR < NS) kr[i % KR] = kfrag(i + KR);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
+    if constexpr (STAGE) {
       stage_k(cur ^ 1);   // the other buffer was last read before the previous barrier
       fetch_v(tt + 1);
     }
     // the first V^T fragments of the P V product, read while the softmax below runs
+    // V^T fragment (dh tile i % NDT, key half kp = i / NDT): lane (dh r16, group lg) gets V at
+    // keys 32 kp + 4 lg + 0..3 and 32 kp + 16 + 4 lg + 0..3, the keys (in that order) of its P
+    // fragment; lane r16 of the group addresses key row 4 lg + r16 / 4 (+ 16), columns
+    // 16 (i % NDT) + 4 (r16 % 4) .. + 3
     constexpr int NP = 2 * C::NDT;
+    const uint16_t* vlane = vsb + (4 * lg + (r16 >> 2)) * C::KS_STRIDE + 4 * (r16 & 3);
     auto vfrag = [&](int i) -> u32x4 {
-      return ld16(vtb + ((i % C::NDT) * 16 + r16) * C::VT_STRIDE + (i / C::NDT) * 32 + 8 * lg);
+      const uint16_t* p = vlane + (i / C::NDT) * 32 * C::KS_STRIDE + (i % C::NDT) * 16;
+      const s16x4 lo = lds_read_tr16(p);
+      const s16x4 hi = lds_read_tr16(p + 16 * C::KS_STRIDE);
+      return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     constexpr int VR = C::RING < NP ? C::RING : NP;
     u32x4 vr[VR];
@@ -325,8 +318,8 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       }
     }
     // O^T[dh][q] += V^T[dh][keys] P^T[keys][q]; the B operand's 8 keys per lane are
-    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}, the 16 bytes at V^T column 32 kp + 8 lg.
-    // kp-major V^T fragment ring; each fragment feeds every query tile
+    // {32 kp + 4 lg + 0..3, 32 kp + 16 + 4 lg + 0..3}.  kp-major V^T fragment ring; each
+    // fragment feeds every query tile
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
 #pragma unroll
@@ -335,9 +328,11 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       if (i + VR < NP) vr[i % VR] = vfrag(i + VR);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) stage_v(cur ^ 1);
+    if constexpr (STAGE) stage_v(cur ^ 1);
     __syncthreads();
-  }
+  };
+  for (int tt = t_beg; tt + 1 < t_end; ++tt) tile(tt, std::true_type{});
+  if (t_beg < t_end) tile(t_end - 1, std::false_type{});
 
 #pragma unroll
   for (int q = 0; q < QT; ++q) {
