@@ -16,54 +16,19 @@ namespace dg {
 
 namespace {
 
-constexpr int kStatsThreads = 256;
-constexpr int kStatsChunk = 32768;   // vocabulary entries per statistics workgroup
+constexpr int kStatsThreads = 64;    // one wave per statistics workgroup
+constexpr int kStatsChunk = 4096;    // vocabulary entries per statistics workgroup (8 groups of 8 per lane)
 constexpr int kCandThreads = 256;
 constexpr int kCandChunk = 4096;     // vocabulary entries per candidate workgroup
 
-// Fold a group of 8 consecutive logits (indices base .. base+7) into running statistics of
-// y = z c (c = log2(e) / T > 0, so the maximum and its position are those of z).  The group's
-// maximum comes from a max tree and its first position from a reverse scan, so the lowest index
-// wins ties; y - m is one fma.  Non-finite inputs need no separate test: +inf makes d = inf -
-// inf, a NaN propagates, and -inf gives d * e = -inf * 0, so r or a ends NaN (checked once per
-// thread).  2^d uses the hardware exp2 (d <= 0; results below 2^-126 flush to 0, nothing at the
-// scale of the sums, which hold the maximum's 1 implicitly).
-__device__ __forceinline__ void stats_fold8(SoftStats& s, const uint4 raw, int base, float c) {
-  float z[8];
+constexpr int kStatsGroups = kStatsChunk / (kStatsThreads * 8);   // groups of 8 per thread
+
+__device__ __forceinline__ void unpack8(const uint4 raw, float (&z)[8]) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     z[2 * k] = __uint_as_float(w[k] << 16);
     z[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-  }
-  const float gz = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  const float gm = gz * c;
-  int gi = 7;
-#pragma unroll
-  for (int k = 6; k >= 0; --k) gi = (z[k] == gz) ? k : gi;
-  int skip = -1;
-  if (gm > s.m) {
-    if (s.m == -INFINITY) {
-      s.r = 0.f;
-      s.a = 0.f;
-    } else {
-      const float d = s.m - gm;
-      const float sc = __builtin_amdgcn_exp2f(d);
-      s.a = (s.a + d * (1.0f + s.r)) * sc;
-      s.r = (1.0f + s.r) * sc;
-    }
-    s.m = gm;
-    s.idx = base + gi;
-    skip = gi;
-  }
-  const float neg_m = -s.m;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float d = __builtin_fmaf(z[k], c, neg_m);
-    const float e = (k == skip) ? 0.f : __builtin_amdgcn_exp2f(d);
-    s.r += e;
-    s.a = __builtin_fmaf(d, e, s.a);
   }
 }
 
@@ -90,29 +55,90 @@ __device__ SoftStats stats_block_reduce(SoftStats s) {
   return s;
 }
 
+// Statistics of one thread's entries of a chunk: its groups of 8 (group g at v0 + (g * threads +
+// thread) * 8, ascending in g) are all loaded first; pass 1 finds the thread's maximum M of z and
+// the first group G holding it; pass 2 sums 2^d and d 2^d (d = z c - M c, one fma, hardware exp2
+// with d <= 0) over the other groups against that final maximum, so no rescaling and no
+// per-entry test is needed (group G's offset is a huge negative number, which sends its terms to
+// 0); group G is then re-read (from L2) and folded with its first maximum left out of the sums,
+// which gives the index (lowest on ties) and keeps R = sum over the other entries exact to
+// rounding however small it is.  Non-finite inputs need no separate test: +inf makes d = inf -
+// inf, a NaN propagates, and -inf gives d * e = -inf * 0, so r or a ends NaN (checked once per
+// thread).  FULL: the chunk holds kStatsChunk entries (every group is in range).
+template <bool FULL>
+__device__ __forceinline__ SoftStats chunk_stats(const uint16_t* z, int v0, int v1, float c) {
+  constexpr int NG = kStatsGroups;
+  const int tid = threadIdx.x;
+  auto base = [&](int g) { return v0 + (g * kStatsThreads + tid) * 8; };
+  auto valid = [&](int g) { return FULL || base(g) < v1; };
+  if (!valid(0)) return stats_empty();          // no entries for this thread
+  uint4 raw[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    raw[g] = *reinterpret_cast<const uint4*>(z + (FULL ? base(g) : min(base(g), v1 - 8)));
+  // pass 1
+  float gmax[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float x[8];
+    unpack8(raw[g], x);
+    const float gm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    gmax[g] = valid(g) ? gm : -INFINITY;
+  }
+  float M = gmax[0];
+#pragma unroll
+  for (int g = 1; g < NG; ++g) M = fmaxf(M, gmax[g]);
+  int G = NG - 1;
+#pragma unroll
+  for (int g = NG - 2; g >= 0; --g) G = (gmax[g] == M) ? g : G;
+  const int vG = min(base(G), v1 - 8);
+  const uint4 rawG = *reinterpret_cast<const uint4*>(z + vG);   // in flight during pass 2
+  // pass 2
+  const float neg_m = -(M * c);
+  float r = 0.f, acc = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float x[8];
+    unpack8(raw[g], x);
+    const float nm = (g == G || !valid(g)) ? -3.0e38f : neg_m;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float d = __builtin_fmaf(x[k], c, nm);
+      const float e = __builtin_amdgcn_exp2f(d);
+      r += e;
+      acc = __builtin_fmaf(d, e, acc);
+    }
+  }
+  // group G
+  float x[8];
+  unpack8(rawG, x);
+  int gi = 7;
+#pragma unroll
+  for (int k = 6; k >= 0; --k) gi = (x[k] == M) ? k : gi;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = __builtin_fmaf(x[k], c, neg_m);
+    const float e = (k == gi) ? 0.f : __builtin_amdgcn_exp2f(d);
+    r += e;
+    acc = __builtin_fmaf(d, e, acc);
+  }
+  SoftStats st;
+  st.m = -neg_m;
+  st.idx = vG + gi;
+  st.r = (r != r || acc != acc) ? NAN : r;
+  st.a = acc;
+  return st;
+}
+
 __global__ __launch_bounds__(kStatsThreads) void k_logit_stats(EbArgs a) {
   const int row = blockIdx.x;
   const int chunk = blockIdx.y;
   const int v0 = chunk * kStatsChunk;
   const int v1 = min(a.V, v0 + kStatsChunk);
   const uint16_t* z = a.logits + static_cast<size_t>(row) * a.V;
-  SoftStats s = stats_empty();
-  // the thread's groups of 8 are loaded NG at a time, then folded in index order
-  constexpr int NG = 8;
-  for (int v00 = v0 + threadIdx.x * 8; v00 < v1; v00 += NG * kStatsThreads * 8) {
-    uint4 raw[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const int v = min(v00 + g * kStatsThreads * 8, v1 - 8);
-      raw[g] = *reinterpret_cast<const uint4*>(z + v);
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const int v = v00 + g * kStatsThreads * 8;
-      if (v < v1) stats_fold8(s, raw[g], v, a.inv_t_log2e);
-    }
-  }
-  if (isnan(s.r) || isnan(s.a)) s.r = NAN;
+  SoftStats s = (v1 - v0 == kStatsChunk) ? chunk_stats<true>(z, v0, v1, a.inv_t_log2e)
+                                         : chunk_stats<false>(z, v0, v1, a.inv_t_log2e);
   s = stats_block_reduce(s);
   if (threadIdx.x == 0) a.part[static_cast<size_t>(row) * a.n_part + chunk] = s;
 }
