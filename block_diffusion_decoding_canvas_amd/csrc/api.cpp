@@ -400,7 +400,7 @@ struct DecWs {
   uint16_t* u;        // [T][d] normed activations (bf16)
   uint16_t* qkv;      // [T][(Hq + 2 Hkv) dh]
   uint16_t* attn;     // [T][Hq dh]
-  float* o_part;      // attention split partials
+  uint16_t* o_part;   // attention split partials (bf16)
   float* ml_part;
   int max_split;
   float* proj_part;   // [kOProjSplit][T][d] output-projection partials
@@ -441,7 +441,7 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
   w.attn = c.take<uint16_t>(T * d.n_q_heads * d.head_dim);
   w.max_split = std::max(1, 1024 / attn_base_blocks(d, B));
   const size_t prow = static_cast<size_t>(B) * d.n_q_heads * d.canvas_len;
-  w.o_part = c.take<float>(static_cast<size_t>(w.max_split) * prow * d.head_dim);
+  w.o_part = c.take<uint16_t>(static_cast<size_t>(w.max_split) * prow * d.head_dim);
   w.ml_part = c.take<float>(static_cast<size_t>(w.max_split) * prow * 2);
   w.proj_part = c.take<float>(static_cast<size_t>(kOProjSplit) * T * d.d_model);
   w.router_part = c.take<float>(static_cast<size_t>(kRouterSplit) * T * d.n_experts);

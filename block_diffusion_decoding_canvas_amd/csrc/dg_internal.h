@@ -240,7 +240,7 @@ struct AttnArgs {
   int causal;             // encoder: canvas key j visible to query i iff j <= i
   float scale_log2e;      // log2(e) / sqrt(dh)
   int n_split;
-  float* o_part;          // [n_split][B][Hkv][R][dh] (R = Hq/Hkv * C)
+  uint16_t* o_part;       // [n_split][B][Hkv][R][dh] bf16 (R = Hq/Hkv * C)
   float* ml_part;         // [n_split][B][Hkv][R][2]
   uint16_t* out;          // [B*C][Hq*dh]
 };

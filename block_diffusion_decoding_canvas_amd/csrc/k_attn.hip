@@ -18,8 +18,8 @@
 // both tiles are stored row-major with 16-byte stores; the V^T fragments of the P V product come
 // from CDNA4's transposing LDS read, 8 keys of one dh per lane from two 8-byte reads.  LDS rows
 // are padded to a stride at which the 16-byte K reads and the transposing V reads run at the
-// full LDS rate.  Splits of the key range write unnormalised partial outputs with their running
-// max and sum, merged afterwards by log-sum-exp.
+// full LDS rate.  Splits of the key range write unnormalised partial outputs (bf16) with their
+// running max and sum (fp32), merged afterwards by log-sum-exp.
 #include "dg_internal.h"
 
 #include <type_traits>
@@ -353,11 +353,15 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       }
     } else {
       const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + r[q];
-      float* op = a.o_part + prow * DH;
+      // unnormalised partial rows in bf16 (one rounding, well inside the output's own)
+      uint16_t* op = a.o_part + prow * DH;
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-        *reinterpret_cast<float4*>(op + dt * 16 + 4 * lg) =
-            make_float4(o[dt][q][0], o[dt][q][1], o[dt][q][2], o[dt][q][3]);
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        uint2 pk2;
+        pk2.x = pack_bf2(o[dt][q][0], o[dt][q][1]);
+        pk2.y = pack_bf2(o[dt][q][2], o[dt][q][3]);
+        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * lg) = pk2;
+      }
       if (lg == 0) {
         a.ml_part[prow * 2] = m_run[q];
         a.ml_part[prow * 2 + 1] = l;
@@ -385,12 +389,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int sp0 = 0; sp0 < a.n_split; sp0 += 8) {
     float2 ml[8];
-    float4 v[8];
+    uint2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const long long r2 = static_cast<long long>(min(sp0 + u, a.n_split - 1)) * stride + row;
       ml[u] = *reinterpret_cast<const float2*>(a.ml_part + r2 * 2);
-      v[u] = *reinterpret_cast<const float4*>(a.o_part + r2 * DH + c4);
+      v[u] = *reinterpret_cast<const uint2*>(a.o_part + r2 * DH + c4);
     }
     float gmax = mmax;
 #pragma unroll
@@ -411,10 +415,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         const float m = ml[u].x;
         const float w = (m == -INFINITY) ? 0.f : exp2f(m - mmax);
         l += w * ml[u].y;
-        acc.x += w * v[u].x;
-        acc.y += w * v[u].y;
-        acc.z += w * v[u].z;
-        acc.w += w * v[u].w;
+        acc.x += w * __uint_as_float(v[u].x << 16);
+        acc.y += w * __uint_as_float(v[u].x & 0xffff0000u);
+        acc.z += w * __uint_as_float(v[u].y << 16);
+        acc.w += w * __uint_as_float(v[u].y & 0xffff0000u);
       }
     }
   }
