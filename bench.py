@@ -65,6 +65,40 @@ def copy_calibration(mib, launches=4):
     print(json.dumps(dict(copy_bytes_per_launch=n, launches=launches)))
 
 
+def measured_peaks(driver, mib=1024, launches=5, mfma_iters=20000):
+    """Measured ceilings, timed with events on the stream the kernels run on, after one untimed
+    launch each: a plain read stream and a plain copy of `mib` MiB buffers (larger than the
+    256 MB last-level cache), in bytes moved per second, and the bf16 MFMA loop in flop/s."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    blocks = driver.mfma_loop_blocks()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / launches
+    t_read = timed(lambda: driver.read_stream(src, n, word, stream))
+    t_copy = timed(lambda: driver.copy_bytes(dst, src, n, stream))
+    t_mfma = timed(lambda: driver.mfma_loop(mfma_iters, out, stream))
+    assert int(word.item()) == 0   # an even number of words of 0x01010101
+    mfma_flops = blocks * 4 * mfma_iters * 8 * 2.0 * 16 * 16 * 32
+    del src, dst
+    return dict(hbm_read_gbs=round(n / t_read / 1e9, 1), hbm_copy_gbs=round(2.0 * n / t_copy / 1e9, 1),
+                mfma_bf16_tfs=round(mfma_flops / t_mfma / 1e12, 1),
+                note=("library kernels: read stream and copy on 1 GiB buffers (bytes moved / s), "
+                      "16x16x32 bf16 MFMA loop at 2 waves per SIMD"))
+
+
 def moe_gateup_bytes(dims, n_touched):
     """Algorithmic HBM bytes of one gate/up launch: each touched expert's [2F, d] weights and
     the shared expert's once, the token rows once, the SwiGLU activations written once."""
@@ -320,6 +354,14 @@ def main():
                        flops_per_launch=round(at_flops / max(n_at, 1))))
     log("timing the standalone EB sampler")
     rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
+    # every line also against a measured ceiling: a plain read stream for the HBM lines, the
+    # bf16 MFMA loop for the MFMA lines
+    peaks = measured_peaks(driver)
+    for line in rooflines.values():
+        if line["bound"] == "hbm":
+            line["frac_of_measured"] = round(line["achieved"] / peaks["hbm_read_gbs"], 4)
+        else:
+            line["frac_of_measured"] = round(line["achieved"] / peaks["mfma_bf16_tfs"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -342,6 +384,7 @@ def main():
         tokens_per_s=round(tokens / elapsed, 2),
         decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
         roofline=roofline, cpu_baseline=cpu, rooflines=rooflines,
+        measured_peaks=peaks,
         kernel_ms_per_bench_step=kernel_ms)
     print(json.dumps(line))
 

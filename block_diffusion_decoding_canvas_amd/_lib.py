@@ -79,6 +79,9 @@ _SIGS = {
                                    ctypes.c_int64, c_void_p]),
     "dg_pack_weight_fp8": (i32, [c_void_p, c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p]),
     "dg_copy_bytes": (i32, [c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_bench_read_stream": (i32, [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]),
+    "dg_bench_mfma_loop_blocks": (i32, []),
+    "dg_bench_mfma_loop": (i32, [i32, c_void_p, c_void_p]),
     "dg_pack_weight": (i32, [c_void_p, c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p]),
     "dg_prof_num_classes": (i32, []),
     "dg_prof_class_name": (ctypes.c_char_p, [i32]),

@@ -352,6 +352,24 @@ dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream) {
   return DG_OK;
 }
 
+dg_status dg_bench_read_stream(const void* src, size_t n, uint32_t* xor_out, void* stream) {
+  if (!src || !xor_out) return fail(DG_ERR_NULL, "NULL pointer");
+  if (n % 16) return fail(DG_ERR_SHAPE, "n must be a multiple of 16");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  DG_LAUNCH(PC_COPY, hs, dg::launch_read_stream(src, n, xor_out, hs));
+  return DG_OK;
+}
+
+int32_t dg_bench_mfma_loop_blocks(void) { return dg::mfma_loop_blocks(); }
+
+dg_status dg_bench_mfma_loop(int32_t iters, float* out, void* stream) {
+  if (!out) return fail(DG_ERR_NULL, "NULL pointer");
+  if (iters < 1) return fail(DG_ERR_SHAPE, "iters must be >= 1");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  DG_LAUNCH(PC_COPY, hs, dg::launch_mfma_loop(iters, out, hs));
+  return DG_OK;
+}
+
 int32_t dg_prof_num_classes(void) { return PC_COUNT; }
 
 const char* dg_prof_class_name(int32_t cls) {

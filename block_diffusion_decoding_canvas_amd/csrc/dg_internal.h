@@ -268,6 +268,9 @@ hipError_t launch_combine(float* h, const uint16_t* Y, const int32_t* inv, const
 hipError_t launch_kv_write(const uint16_t* qkv, uint16_t* kc, uint16_t* vc, int B, int C,
                            int Hq, int Hkv, int dh, int cap, const int* len, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t n, hipStream_t s);
+hipError_t launch_read_stream(const void* src, size_t n, uint32_t* out, hipStream_t s);
+hipError_t launch_mfma_loop(int iters, float* out, hipStream_t s);
+int mfma_loop_blocks();
 
 // sampler kernels
 struct EbArgs {

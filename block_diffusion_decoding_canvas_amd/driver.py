@@ -284,6 +284,22 @@ def copy_bytes(dst, src, nbytes, stream=None):
           "dg_copy_bytes")
 
 
+def read_stream(src, nbytes, xor_out, stream=None):
+    """XOR of the 32-bit words of the first nbytes of src into the one-word tensor xor_out."""
+    check(_lib.load().dg_bench_read_stream(ptr(src), nbytes, ptr(xor_out), stream_ptr(stream)),
+          "dg_bench_read_stream")
+
+
+def mfma_loop_blocks():
+    return _lib.load().dg_bench_mfma_loop_blocks()
+
+
+def mfma_loop(iters, out, stream=None):
+    """The bf16 MFMA loop: out holds mfma_loop_blocks() * 256 floats."""
+    check(_lib.load().dg_bench_mfma_loop(iters, ptr(out), stream_ptr(stream)),
+          "dg_bench_mfma_loop")
+
+
 class KernelTimer:
     """HIP-event timing of library kernel classes (dg_prof_*)."""
 

@@ -222,6 +222,18 @@ dg_status dg_pack_weight_fp8(const uint8_t* src, uint8_t* dst, int64_t rows, int
 /* Plain device copy of n bytes (bandwidth / counter calibration). */
 dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream);
 
+/* Measured ceilings for the benchmark's roofline lines (measurement only, not part of the
+ * decoding path).
+ * dg_bench_read_stream: reads the n bytes at device `src` (n a multiple of 16) and writes the XOR
+ *   of all its 32-bit words to the device word `xor_out`; the read rate of a plain stream.
+ * dg_bench_mfma_loop: dg_bench_mfma_loop_blocks() workgroups of 4 waves, each wave `iters` rounds
+ *   of 8 independent 16x16x32 bf16 MFMAs (2 * 16 * 16 * 32 flops each), one float per thread
+ *   written to device `out` (blocks * 256 floats); the matrix-core rate the chip sustains.
+ * Errors: DG_ERR_NULL for a NULL pointer, DG_ERR_SHAPE for n % 16 != 0 or iters < 1. */
+dg_status dg_bench_read_stream(const void* src, size_t n, uint32_t* xor_out, void* stream);
+int32_t dg_bench_mfma_loop_blocks(void);
+dg_status dg_bench_mfma_loop(int32_t iters, float* out, void* stream);
+
 /* Kernel timing: the library records HIP events around every launch of the kernel classes set
  * in `mask` (bit i = class i; 0 = off) on the call's stream and accumulates their durations.
  * Classes are listed by dg_prof_class_name(i) for i in [0, dg_prof_num_classes()). */
