@@ -197,3 +197,47 @@ def test_nonfinite_logits_freeze_canvas_and_set_status():
     assert int(gs.dev_status[0]) == 9          # DG_ERR_NONFINITE
     assert h["done"][1] and np.array_equal(h["canvas"][1], st["canvas"][1])
     assert not h["done"][0]
+
+
+def test_logit_stats_exact_ties():
+    """Exact ties at the row maximum where the statistics kernel's lanes, groups and chunks meet:
+    the argmax is the lowest tied index and the other tied entries count fully in the entropy.
+    V = 3 x 4096 + 512, so the last chunk is partial.  Chunk c holds entries 4096 c ..; lane l's
+    8-group g of a chunk starts at 4096 c + 8 (64 g + l)."""
+    V, C = 3 * 4096 + 512, 10
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((1, C, V)).astype(np.float32)
+    ties = [
+        [4096 + 8 * (64 * 3 + 7), 4096 + 8 * (64 * 3 + 7) + 3],    # one 8-group
+        [8192 + 8 * (64 + 9), 8192 + 8 * (64 + 9) + 512],          # one lane, two groups
+        [800, 808],                                                 # adjacent lanes
+        [512, 40],                                                  # lane 0 group 1 vs lane 5 group 0
+        [3000, 3000 + 4096],                                        # two chunks
+        [12288 + 100, 12288 + 260],                                 # the partial chunk
+        [0, V - 1],                                                 # first and last entries
+        [],                                                         # all entries equal
+        [4095, 4096, 8191],                                         # across chunk boundaries
+        [V - 1],                                                    # single maximum, last entry
+    ]
+    for i, pos in enumerate(ties):
+        if pos:
+            z[0, i, pos] = 6.0
+        else:
+            z[0, i, :] = 0.5
+    z = synth.to_bf16_values(z)
+    st = osamp.new_state(osamp.init_canvas(2, [0], C, V))
+    gs = _gpu_state_from_host(st, 1, C)
+    out = driver.StepOut(1, C, V, DEV, with_logits=False)
+    params = dict(osamp.default_params(), entropy_bound=0.0)
+    driver.eb_sample(synth.to_device_bf16(z, DEV), 0, driver.eb_params_from_dict(params, 2),
+                     gs, out)
+    torch.cuda.synchronize()
+    inv_t = osamp.inv_temperature_f32(0, params["max_steps"], params["t_max"], params["t_min"])
+    h_ref, a_ref = osamp.entropy_argmax(z[0].astype(np.float64), inv_t)
+    a_gpu = out.argmax.cpu().numpy()[0]
+    for i, pos in enumerate(ties):
+        assert a_gpu[i] == (min(pos) if pos else 0), (i, a_gpu[i], pos)
+    assert np.array_equal(a_gpu, a_ref)
+    assert_entropy_close(out.entropy.cpu().numpy().astype(np.float64)[None], h_ref[None],
+                         "exact ties")
+    assert abs(float(out.entropy[0, 7]) - np.log(V)) < 1e-5 * np.log(V)   # uniform row

@@ -233,3 +233,51 @@ def test_router_exact_ties_lowest_id_first():
                 seen_one += 1
     print(f"twin pairs selected together {seen_both}, lower twin alone {seen_one}")
     assert seen_both + seen_one > 0
+
+
+@pytest.mark.parametrize("off", [1, 4, 16, 32, 256, 1024])
+def test_lm_head_statistics_exact_ties(off):
+    """Duplicated LM-head rows (row v equals row v ^ off) give bit-identical logits, so every
+    logit value occurs at a pair of vocabulary rows.  The pairs sit, by offset: among one lane's
+    4 consecutive rows (1), in other lane groups (4), in a wave's other 16-row tile (16), in
+    another wave (32), in another 256-row workgroup block (256, 1024).  The fused statistics must
+    return the lower row of its pair, within the certified logit error of the maximum, and count
+    the duplicate in the entropy."""
+    from oracle.numerics import round_bf16
+    from tests.parity_util import assert_entropy_close, entropy_sensitivity, entropy_tolerance
+    dims = dict(n_layers=1, d=128, hq=4, hkv=2, dh=32, E=8, top_k=2, F=64, Fs=64, V=2048, C=40,
+                window=0, global_every=1, eps=1e-6)
+    mnp = synth.make_model(dims, seed=50 + off, norm_gain_std=0.1, lm_std=0.1)
+    w = mnp["w_lm"]
+    V = dims["V"]
+    for v in range(V):
+        if v & off:
+            w[v] = w[v ^ off]
+    m64 = synth.model_to_f64(mnp)
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    B, T = 1, dims["C"]
+    ws = driver.workspace(model.workspace_bytes(B))
+    h = synth.hidden_states(T, dims["d"], seed=60 + off)
+    params = osamp.default_params()
+    step = 30
+    out = driver.StepOut(B, dims["C"], V, DEV)
+    driver.lm_head_forward(model, B, torch.from_numpy(h).to(DEV), step,
+                           driver.eb_params_from_dict(params, 1), out, ws)
+    torch.cuda.synchronize()
+    z64 = om.linear(om.rms_norm(h.astype(np.float64), m64["final_norm"], dims["eps"]),
+                    m64["w_lm"])
+    zr = round_bf16(z64)
+    zg = out.logits.float().cpu().numpy().reshape(T, -1)
+    assert_close_rel(zg, zr, what="logits")
+    # the GPU's own logits are exactly paired
+    assert np.array_equal(zg[:, np.arange(V) & off == 0], zg[:, np.arange(V) & off != 0])
+    ag = out.argmax.cpu().numpy().reshape(-1)
+    dz = np.abs(zg - z64).max(axis=1)
+    for t in range(T):
+        assert ag[t] & off == 0, f"token {t}: argmax {ag[t]} is the higher row of its pair"
+        assert zg[t, ag[t]] == zg[t].max(), f"token {t}: argmax is not a maximum of the logits"
+        assert zr[t, ag[t]] >= zr[t].max() - 2.0 * dz[t] - 2.0 ** -7 * abs(zr[t].max())
+    inv_t = osamp.inv_temperature_f32(step, params["max_steps"])
+    h_ref, _ = osamp.entropy_argmax(zr, inv_t)
+    tol = entropy_tolerance(h_ref, dz * float(inv_t), entropy_sensitivity(z64, inv_t))
+    assert_entropy_close(out.entropy.cpu().numpy().reshape(-1), h_ref, "paired-row entropy", tol)
