@@ -126,6 +126,52 @@ def attention_flops(dims, cache_len, causal):
     return 4.0 * hq * c * keys * dh
 
 
+def prefill_flops(dims, prompt, chunk):
+    """Algorithmic flops of the chunked prefill of a `prompt`-token prompt on an empty cache: per
+    token and layer the QKV product, causal attention over the cache and the chunk's earlier
+    tokens, and (every layer but the last, whose keys and values are all an append adds) the O
+    product, the router and the top-k + shared SwiGLU experts."""
+    d, hq, hkv, dh = dims["d"], dims["hq"], dims["hkv"], dims["dh"]
+    e, k, f, fs, nl = dims["E"], dims["top_k"], dims["F"], dims["Fs"], dims["n_layers"]
+    qkv = 2.0 * d * (hq + 2 * hkv) * dh
+    rest = 2.0 * d * hq * dh + 2.0 * d * e + k * 6.0 * d * f + 6.0 * d * fs
+    keys = prompt * (prompt + 1) / 2.0          # sum over tokens of the keys each one sees
+    attn = 4.0 * hq * dh * keys
+    return nl * (prompt * qkv + attn) + (nl - 1) * prompt * rest
+
+
+def prefill_measure(driver, model, dims, dev, prompt=8192, chunk=2048, reps=2):
+    """Chunked prefill of a `prompt`-token prompt into an empty cache, `chunk` tokens per call;
+    the mean wall time of `reps` timed prefills after one untimed."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    tokens = torch.randint(0, dims["V"], (1, prompt), generator=g, device=dev, dtype=torch.int32)
+    kv = driver.KVCache(dims, 1, prompt, dev)
+    ws = driver.workspace(model.append_workspace_bytes(1, chunk), dev)
+
+    def run():
+        kv.len[0] = 0
+        for c0 in range(0, prompt, chunk):
+            driver.kv_append_tokens(model, kv, tokens[:, c0:c0 + chunk].contiguous(), ws)
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / reps
+    flops = prefill_flops(dims, prompt, chunk)
+    tf = flops / t / 1e12
+    del kv, ws
+    return dict(workload=f"{prompt}-token prompt into an empty cache, {chunk}-token chunks, "
+                         f"{dims['n_layers']} layers", tokens_per_s=round(prompt / t, 1),
+                ms=round(t * 1e3, 2), reps=reps,
+                roofline=dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFS,
+                              unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFS, 4),
+                              flops=round(flops)))
+
+
 def sampler_roofline(driver, timer, dev, vocab, steps=8):
     """The standalone EB sampler (dg_eb_sample) on the standalone sampler workload: HBM rate of
     its statistics kernel (one read of the logits) and the time of the whole call."""
@@ -359,6 +405,8 @@ def main():
         attention=dict(mfma_line(at_flops / max(n_at, 1), t_at, n_at,
                                  "attention (+ split merge), averaged over the pass"),
                        flops_per_launch=round(at_flops / max(n_at, 1))))
+    log("timing the chunked prefill")
+    prefill = prefill_measure(driver, model, dims, dev)
     log("timing the standalone EB sampler")
     rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
     # every line also against a measured ceiling: a plain read stream for the HBM lines, the
@@ -391,7 +439,7 @@ def main():
         tokens_per_s=round(tokens / elapsed, 2),
         decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
         roofline=roofline, cpu_baseline=cpu, rooflines=rooflines,
-        measured_peaks=peaks,
+        measured_peaks=peaks, prefill=prefill,
         kernel_ms_per_bench_step=kernel_ms)
     print(json.dumps(line))
 

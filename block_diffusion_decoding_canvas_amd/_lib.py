@@ -69,6 +69,9 @@ _SIGS = {
                            P(dg_step_out), c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_kv_append_canvas": (i32, [c_void_p, P(dg_kv), c_void_p, c_void_p, ctypes.c_size_t,
                                   c_void_p]),
+    "dg_append_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32, i32]),
+    "dg_kv_append_tokens": (i32, [c_void_p, P(dg_kv), c_void_p, i32, c_void_p, ctypes.c_size_t,
+                                  c_void_p]),
     "dg_layer_forward": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_ffn_forward": (i32, [c_void_p, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -442,14 +442,15 @@ struct DecWs {
   uint8_t* hot;       // 1 KiB read by the streaming kernels' past-the-end loads (never used)
 };
 
-int attn_base_blocks(const dg_dims& d, int B) {
-  const int R = (d.n_q_heads / d.n_kv_heads) * d.canvas_len;
+int attn_base_blocks(const dg_dims& d, int B, int C) {
+  const int R = (d.n_q_heads / d.n_kv_heads) * C;
   return B * d.n_kv_heads * ((R + 63) / 64);
 }
 
-DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
+// C: tokens per canvas in the call (the canvas length, or an append's token count)
+DecWs carve_dec(Carver& c, const dg_dims& d, int B, int C) {
   DecWs w;
-  const size_t T = static_cast<size_t>(B) * d.canvas_len;
+  const size_t T = static_cast<size_t>(B) * C;
   const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const int fmax = std::max(d.ffn_inner, d.shared_inner);
   const size_t rows = T * d.top_k + T;
@@ -457,17 +458,20 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B) {
   w.u = c.take<uint16_t>(T * d.d_model);
   w.qkv = c.take<uint16_t>(T * dq);
   w.attn = c.take<uint16_t>(T * d.n_q_heads * d.head_dim);
-  w.max_split = std::max(1, 1024 / attn_base_blocks(d, B));
-  const size_t prow = static_cast<size_t>(B) * d.n_q_heads * d.canvas_len;
-  w.o_part = c.take<uint16_t>(static_cast<size_t>(w.max_split) * prow * d.head_dim);
-  w.ml_part = c.take<float>(static_cast<size_t>(w.max_split) * prow * 2);
+  w.max_split = std::max(1, 1024 / attn_base_blocks(d, B, C));
+  // split partial rows: max_split * prow <= max(prow, 65,536), because prow <= 64 * base blocks;
+  // sized by that bound, the workspace grows monotonically with C
+  const size_t prow = static_cast<size_t>(B) * d.n_q_heads * C;
+  const size_t part_rows = std::max<size_t>(prow, 65536);
+  w.o_part = c.take<uint16_t>(part_rows * d.head_dim);
+  w.ml_part = c.take<float>(part_rows * 2);
   w.proj_part = c.take<float>(static_cast<size_t>(kOProjSplit) * T * d.d_model);
   w.router_part = c.take<float>(static_cast<size_t>(kRouterSplit) * T * d.n_experts);
   w.topk = c.take<int32_t>(T * d.top_k);
   w.gates = c.take<float>(T * d.top_k);
   w.perm = c.take<int32_t>(rows);
   w.inv = c.take<int32_t>(T * d.top_k);
-  const int tr = dg::moe_tile_rows();
+  const int tr = dg::moe_tile_rows_min();   // the most tiles any tile size produces
   w.max_chunks = d.n_experts + static_cast<int>((T * d.top_k + tr - 1) / tr) +
                  static_cast<int>((T + tr - 1) / tr);
   w.chunks = c.take<int32_t>(static_cast<size_t>(w.max_chunks) * 3);
@@ -495,16 +499,17 @@ size_t kv_layer_elems(const dg_dims& d, const dg_kv* kv) {
   return static_cast<size_t>(kv->batch) * d.n_kv_heads * kv->cap * d.head_dim;
 }
 
-dg_status check_kv(const dg_model* m, const dg_kv* kv, bool need_room) {
+// need_room: the call appends C tokens per canvas
+dg_status check_kv(const dg_model* m, const dg_kv* kv, bool need_room, int C = 0) {
   if (!kv || !kv->k || !kv->v || !kv->len) return fail(DG_ERR_NULL, "kv or a kv pointer is NULL");
   if (kv->batch < 1 || kv->batch > 64) return fail(DG_ERR_SHAPE, "kv batch must be in [1, 64]");
   if (kv->cap < 1) return fail(DG_ERR_SHAPE, "kv capacity must be >= 1");
   for (int b = 0; b < kv->batch; ++b) {
     if (kv->len[b] < 0 || kv->len[b] > kv->cap)
       return fail(DG_ERR_CAPACITY, "kv len[%d] = %d outside [0, cap = %d]", b, kv->len[b], kv->cap);
-    if (need_room && kv->len[b] + m->dims.canvas_len > kv->cap)
-      return fail(DG_ERR_CAPACITY, "kv len[%d] + canvas_len = %d exceeds cap %d", b,
-                  kv->len[b] + m->dims.canvas_len, kv->cap);
+    if (need_room && kv->len[b] + C > kv->cap)
+      return fail(DG_ERR_CAPACITY, "kv len[%d] + %d appended tokens = %d exceeds cap %d", b, C,
+                  kv->len[b] + C, kv->cap);
   }
   return DG_OK;
 }
@@ -513,16 +518,17 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
                   bool next_q8, float* trace_logits, int32_t* trace_idx, float* trace_gates,
                   hipStream_t s);
 
-// One transformer layer on ws.h (the attention norm of this layer must already be in ws.u).
-// causal: encoder pass (causal canvas, writes K/V into the cache); next_gain: the norm of the
+// One transformer layer on ws.h (the attention norm of this layer must already be in ws.u), over
+// C tokens per canvas (the canvas, or the tokens an encoder pass appends).  causal: encoder pass
+// (causal among the C tokens, writes their K/V into the cache); next_gain: the norm of the
 // following consumer applied to the new h (NULL: none), with its e4m3 codes when next_q8.
 // Optional router traces.
-dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, bool causal, DecWs& w,
+dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causal, DecWs& w,
                     const uint16_t* next_gain, bool next_q8, bool skip_ffn, float* trace_logits,
                     int32_t* trace_idx, float* trace_gates, hipStream_t s) {
   const dg_dims& d = m->dims;
   const dg_layer_w& lw = m->layers[l];
-  const int B = kv->batch, C = d.canvas_len, T = B * C;
+  const int B = kv->batch, T = B * C;
   const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const size_t kvl = kv_layer_elems(d, kv);
   uint16_t* kc = static_cast<uint16_t*>(kv->k) + kvl * l;
@@ -595,8 +601,10 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   float* gates = trace_gates ? trace_gates : w.gates;
   DG_LAUNCH(PC_TOPK, s, dg::launch_topk(w.router_part, kRouterSplit, T, d.n_experts, d.top_k, idx,
                                         gates, trace_logits, s));
+  // expert tiles: wide ones for long prefill chunks (bf16 weights)
+  const int tile_rows = fp8 ? dg::moe_tile_rows_min() : dg::moe_tile_rows(T);
   DG_LAUNCH(PC_PERMUTE, s, dg::launch_permute(idx, T, d.top_k, d.n_experts,
-                                              dg::moe_tile_rows(), w.perm, w.inv, w.chunks,
+                                              tile_rows, w.perm, w.inv, w.chunks,
                                               w.n_chunks, w.max_chunks, s));
   // routed + shared experts: gate/up with SwiGLU, then down
   const int fmax = std::max(d.ffn_inner, d.shared_inner);
@@ -609,7 +617,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   g.K = g.K_sh = d.d_model; g.N = d.ffn_inner; g.N_sh = d.shared_inner;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.act; g.ldo = fmax; g.ksplit = 1;
-  g.sh_tiles = (T + dg::moe_tile_rows() - 1) / dg::moe_tile_rows();
+  g.sh_tiles = (T + tile_rows - 1) / tile_rows;
   const long long rows = static_cast<long long>(T) * d.top_k + T;
   if (fp8) {
     // e4m3 codes of u (gathered through the permutation), fp32 SwiGLU output, then its codes
@@ -621,7 +629,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
                                                  static_cast<long long>(T) * d.top_k,
                                                  d.ffn_inner, d.shared_inner, s));
   } else {
-    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, s));
+    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup(g, tile_rows, s));
   }
   memset(&g, 0, sizeof(g));
   g.hot = w.hot;
@@ -631,13 +639,13 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   g.K = d.ffn_inner; g.K_sh = d.shared_inner; g.N = g.N_sh = d.d_model;
   g.n_experts = d.n_experts; g.chunks = w.chunks; g.n_chunks = w.n_chunks;
   g.grid_tiles = w.max_chunks; g.out = w.y; g.ldo = d.d_model; g.ksplit = 1;
-  g.sh_tiles = (T + dg::moe_tile_rows() - 1) / dg::moe_tile_rows();
+  g.sh_tiles = (T + tile_rows - 1) / tile_rows;
   if (fp8) {
     g.X = reinterpret_cast<const uint16_t*>(w.act8); g.x_scale = w.act8s;
     g.w_scale = lw.s_down; g.wsc_estride = d.d_model; g.w_scale_sh = lw.ss_down;
     DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down_fp8(g, s));
   } else {
-    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, s));
+    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, tile_rows, s));
   }
   DG_LAUNCH(PC_COMBINE, s, dg::launch_combine(w.h, w.y, w.inv, gates, T, d.top_k, d.d_model,
                                               next_gain, w.u, d.norm_eps,
@@ -678,7 +686,16 @@ extern "C" {
 size_t dg_workspace_bytes(const dg_model* m, int32_t batch) {
   if (!m || batch < 1 || batch > 64) return 0;
   Carver c(nullptr);
-  carve_dec(c, m->dims, batch);
+  carve_dec(c, m->dims, batch, m->dims.canvas_len);
+  return c.off + 256;
+}
+
+size_t dg_append_workspace_bytes(const dg_model* m, int32_t batch, int32_t max_tokens) {
+  if (!m || batch < 1 || batch > 64 || max_tokens < 1 || max_tokens > DG_MAX_APPEND_TOKENS ||
+      static_cast<long long>(batch) * max_tokens > 65536)
+    return 0;
+  Carver c(nullptr);
+  carve_dec(c, m->dims, batch, max_tokens);
   return c.off + 256;
 }
 
@@ -698,7 +715,7 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
   const int B = kv->batch, C = d.canvas_len, T = B * C;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver c(ws);
-  DecWs w = carve_dec(c, d, B);
+  DecWs w = carve_dec(c, d, B, C);
 
   DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(st->canvas, m->embed, w.h, T, d.d_model, d.vocab, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
@@ -707,7 +724,7 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
     const bool last = l + 1 == d.n_layers;
     const uint16_t* next = !last ? static_cast<const uint16_t*>(m->layers[l + 1].attn_norm)
                                  : m->final_norm;
-    if ((s = run_layer(m, kv, l, false, w, next, last && m->fp8(), false, nullptr, nullptr,
+    if ((s = run_layer(m, kv, l, C, false, w, next, last && m->fp8(), false, nullptr, nullptr,
                        nullptr, hs)) != DG_OK)
       return s;
   }
@@ -717,26 +734,26 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
   return run_sampler_tail(a, hs);
 }
 
-dg_status dg_kv_append_canvas(const dg_model* m, dg_kv* kv, const int32_t* tokens, void* ws,
-                              size_t ws_bytes, void* stream) {
-  dg_status s = check_model(m);
-  if (s != DG_OK) return s;
-  if ((s = check_kv(m, kv, true)) != DG_OK) return s;
-  if (!tokens || !ws) return fail(DG_ERR_NULL, "tokens or workspace is NULL");
-  const size_t need = dg_workspace_bytes(m, kv->batch);
-  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+// The encoder pass over C new tokens per canvas (checked by the caller): causal among them,
+// each layer writing their keys and values at [len, len + C); then len += C
+static dg_status encoder_append(const dg_model* m, dg_kv* kv, const int32_t* tokens, int C,
+                                void* ws, size_t ws_bytes, hipStream_t hs) {
   const dg_dims& d = m->dims;
-  const int B = kv->batch, C = d.canvas_len, T = B * C;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int B = kv->batch, T = B * C;
+  Carver sz(nullptr);
+  carve_dec(sz, d, B, C);
+  if (ws_bytes < sz.off + 256)
+    return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, sz.off + 256);
   Carver c(ws);
-  DecWs w = carve_dec(c, d, B);
+  DecWs w = carve_dec(c, d, B, C);
+  dg_status s;
   DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(tokens, m->embed, w.h, T, d.d_model, d.vocab, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
                                                w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
   for (int l = 0; l < d.n_layers; ++l) {
     const bool last = l + 1 == d.n_layers;  // its keys/values are all the last layer adds
     const uint16_t* next = last ? nullptr : static_cast<const uint16_t*>(m->layers[l + 1].attn_norm);
-    if ((s = run_layer(m, kv, l, true, w, next, false, last, nullptr, nullptr, nullptr, hs)) !=
+    if ((s = run_layer(m, kv, l, C, true, w, next, false, last, nullptr, nullptr, nullptr, hs)) !=
         DG_OK)
       return s;
   }
@@ -744,12 +761,39 @@ dg_status dg_kv_append_canvas(const dg_model* m, dg_kv* kv, const int32_t* token
   return DG_OK;
 }
 
+dg_status dg_kv_append_canvas(const dg_model* m, dg_kv* kv, const int32_t* tokens, void* ws,
+                              size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, true, m->dims.canvas_len)) != DG_OK) return s;
+  if (!tokens || !ws) return fail(DG_ERR_NULL, "tokens or workspace is NULL");
+  return encoder_append(m, kv, tokens, m->dims.canvas_len, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_kv_append_tokens(const dg_model* m, dg_kv* kv, const int32_t* tokens,
+                              int32_t n_tokens, void* ws, size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if (!tokens || !ws) return fail(DG_ERR_NULL, "tokens or workspace is NULL");
+  if (n_tokens < 1 || n_tokens > DG_MAX_APPEND_TOKENS)
+    return fail(DG_ERR_SHAPE, "n_tokens = %d outside [1, %d]", n_tokens, DG_MAX_APPEND_TOKENS);
+  if (m->dims.window > 0 && n_tokens > m->dims.window)
+    return fail(DG_ERR_SHAPE, "n_tokens = %d exceeds the sliding window %d", n_tokens,
+                m->dims.window);
+  if ((s = check_kv(m, kv, true, n_tokens)) != DG_OK) return s;
+  if (static_cast<long long>(kv->batch) * n_tokens > 65536)
+    return fail(DG_ERR_SHAPE, "batch * n_tokens = %lld exceeds 65,536",
+                static_cast<long long>(kv->batch) * n_tokens);
+  return encoder_append(m, kv, tokens, n_tokens, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
 dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, int32_t causal,
                            float* h, float* router_logits, int32_t* topk_idx, float* gates,
                            void* ws, size_t ws_bytes, void* stream) {
   dg_status s = check_model(m);
   if (s != DG_OK) return s;
-  if ((s = check_kv(m, kv, causal != 0)) != DG_OK) return s;
+  if ((s = check_kv(m, kv, causal != 0, m->dims.canvas_len)) != DG_OK) return s;
   if (!h || !ws) return fail(DG_ERR_NULL, "h or workspace is NULL");
   if (layer < 0 || layer >= m->dims.n_layers) return fail(DG_ERR_SHAPE, "layer out of range");
   const size_t need = dg_workspace_bytes(m, kv->batch);
@@ -758,11 +802,12 @@ dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, in
   const int T = kv->batch * d.canvas_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver c(ws);
-  DecWs w = carve_dec(c, d, kv->batch);
+  DecWs w = carve_dec(c, d, kv->batch, d.canvas_len);
   DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].attn_norm),
                                                w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
-  if ((s = run_layer(m, kv, layer, causal != 0, w, nullptr, false, false, router_logits, topk_idx,
+  if ((s = run_layer(m, kv, layer, d.canvas_len, causal != 0, w, nullptr, false, false,
+                     router_logits, topk_idx,
                      gates, hs)) != DG_OK)
     return s;
   DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
@@ -783,7 +828,7 @@ dg_status dg_ffn_forward(const dg_model* m, int32_t layer, int32_t batch, float*
   const int T = batch * d.canvas_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver c(ws);
-  DecWs w = carve_dec(c, d, batch);
+  DecWs w = carve_dec(c, d, batch, d.canvas_len);
   DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].ffn_norm),
                                                w.u, T, d.d_model, d.norm_eps, w.u8, w.u8s, hs));
@@ -809,7 +854,7 @@ dg_status dg_lm_head_forward(const dg_model* m, int32_t batch, const float* h, i
   const int T = batch * d.canvas_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver c(ws);
-  DecWs w = carve_dec(c, d, batch);
+  DecWs w = carve_dec(c, d, batch, d.canvas_len);
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(h, m->final_norm, w.u, T, d.d_model, d.norm_eps,
                                                w.u8, w.u8s, hs));
   dg_eb_state none;

@@ -210,10 +210,13 @@ hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out
 hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // fp32 split partials
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s);       // logits + stats
 int gemm_lmhead_rows_per_block();
-// expert products over fragment-major ("packed") weights, tiles of moe_tile_rows() tokens
-hipError_t launch_moe_gateup(const WGemmArgs& a, hipStream_t s);          // SwiGLU act
-hipError_t launch_moe_down(const WGemmArgs& a, hipStream_t s);            // Y rows bf16
-int moe_tile_rows();
+// expert products over fragment-major ("packed") weights, in tiles of tile_rows gathered rows:
+// moe_tile_rows(ntok) for bf16 weights (32, or 128 once a call routes ntok >= 1,024 tokens,
+// about 64 rows per expert and more), moe_tile_rows_min() for e4m3 weights and for sizing
+hipError_t launch_moe_gateup(const WGemmArgs& a, int tile_rows, hipStream_t s);  // SwiGLU act
+hipError_t launch_moe_down(const WGemmArgs& a, int tile_rows, hipStream_t s);    // Y rows bf16
+int moe_tile_rows(int ntok);
+int moe_tile_rows_min();
 // dense products over packed weights, 64-token tiles (bf16 out, or fp32 k-split partials)
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s);

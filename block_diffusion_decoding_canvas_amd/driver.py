@@ -159,6 +159,9 @@ class Model:
     def workspace_bytes(self, batch):
         return _lib.load().dg_workspace_bytes(self.handle, batch)
 
+    def append_workspace_bytes(self, batch, max_tokens):
+        return _lib.load().dg_append_workspace_bytes(self.handle, batch, max_tokens)
+
     def close(self):
         if self.handle:
             _lib.load().dg_model_destroy(self.handle)
@@ -209,6 +212,15 @@ def kv_append_canvas(model, kv, tokens, ws, stream=None):
     kvs = kv.struct()
     check(lib.dg_kv_append_canvas(model.handle, ctypes.byref(kvs), ptr(tokens), ptr(ws),
                                   ws.numel(), stream_ptr(stream)), "dg_kv_append_canvas")
+
+
+def kv_append_tokens(model, kv, tokens, ws, stream=None):
+    """Chunked prefill: encoder pass over tokens [B, n] (int32 device), appended to the cache."""
+    lib = _lib.load()
+    kvs = kv.struct()
+    n = int(tokens.shape[1])
+    check(lib.dg_kv_append_tokens(model.handle, ctypes.byref(kvs), ptr(tokens), n, ptr(ws),
+                                  ws.numel(), stream_ptr(stream)), "dg_kv_append_tokens")
 
 
 def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=None,

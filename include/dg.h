@@ -175,6 +175,29 @@ dg_status dg_eb_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len
 dg_status dg_kv_append_canvas(const dg_model* model, dg_kv* kv, const int32_t* tokens,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Largest token count per canvas of one dg_kv_append_tokens call. */
+#define DG_MAX_APPEND_TOKENS 8192
+
+/* Workspace for dg_kv_append_tokens calls of up to max_tokens tokens per canvas
+ * (1 <= max_tokens <= DG_MAX_APPEND_TOKENS and batch * max_tokens <= 65,536; else 0).  The size
+ * grows with max_tokens, so it also covers every smaller call. */
+size_t dg_append_workspace_bytes(const dg_model* model, int32_t batch, int32_t max_tokens);
+
+/* Chunked prefill (DiffusionGemma model card, "Model overview": the encoder works as the prefill
+ * stage, processing the prompt autoregressively into the KV cache).  Encoder pass over n_tokens
+ * new tokens per canvas, tokens [B, n_tokens] int32 row-major: the same layers as
+ * dg_kv_append_canvas, causal among the new tokens, every cached key visible (sliding-window
+ * layers: cache position j is visible to new token i iff (len[b] + i) - j < window).  Every layer
+ * writes the new tokens' keys/values at [len[b], len[b] + n_tokens).  A prompt split into
+ * consecutive calls is encoded as in one causal pass (up to rounding), for any split.
+ * Errors: DG_ERR_NULL (model, kv, tokens or ws), DG_ERR_SHAPE (n_tokens outside
+ * [1, DG_MAX_APPEND_TOKENS]; n_tokens > window on a windowed model, where the window would also
+ * have to cut inside the new tokens; batch * n_tokens > 65,536), DG_ERR_CAPACITY
+ * (len[b] + n_tokens > cap), DG_ERR_WORKSPACE (ws_bytes below the size for n_tokens).  On DG_OK
+ * the HOST array kv->len advances by n_tokens immediately (the device writes are enqueued). */
+dg_status dg_kv_append_tokens(const dg_model* model, dg_kv* kv, const int32_t* tokens,
+                              int32_t n_tokens, void* ws, size_t ws_bytes, void* stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* dg_last_error(void);
 

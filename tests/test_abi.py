@@ -178,6 +178,39 @@ def test_decoder_calls_validate_kv_and_step():
     lib.dg_model_destroy(h)
 
 
+def test_append_tokens_validate():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    assert st == 0
+    lens = (ctypes.c_int32 * 1)(60)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens)
+    fake = ctypes.c_void_p(0x1000)
+    sizes = [lib.dg_append_workspace_bytes(h, 1, n) for n in (1, 4, 15, 16, 17, 100, 1000, 8192)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    assert lib.dg_append_workspace_bytes(h, 1, 16) == lib.dg_workspace_bytes(h, 1)
+    assert lib.dg_append_workspace_bytes(h, 1, 0) == 0
+    assert lib.dg_append_workspace_bytes(h, 1, 8193) == 0
+    assert lib.dg_append_workspace_bytes(h, 16, 8192) == 0      # batch * tokens > 65,536
+    ws4 = lib.dg_append_workspace_bytes(h, 1, 4)
+
+    def call(n, ws=ws4, tokens=fake):
+        return lib.dg_kv_append_tokens(h, ctypes.byref(kv), tokens, n, fake, ws, None)
+
+    assert call(0) == 2                          # DG_ERR_SHAPE
+    assert call(8193, ws=1 << 40) == 2
+    assert call(5, ws=1 << 40) == 4              # 60 + 5 > cap 64: DG_ERR_CAPACITY
+    assert call(4, ws=ws4 - 1) == 5              # DG_ERR_WORKSPACE
+    assert call(4, tokens=None) == 1             # DG_ERR_NULL
+    assert lens[0] == 60                         # nothing appended
+    lib.dg_model_destroy(h)
+    # a windowed model takes at most `window` tokens per call
+    st, h = _create(_tiny_dims(window=32, global_every=2))
+    assert st == 0
+    lens[0] = 0
+    assert lib.dg_kv_append_tokens(h, ctypes.byref(kv), fake, 33, fake, 1 << 40, None) == 2
+    lib.dg_model_destroy(h)
+
+
 def test_prof_classes_named():
     t = driver.KernelTimer()
     assert "moe_gateup" in t.names and "lmhead" in t.names and "attention" in t.names
