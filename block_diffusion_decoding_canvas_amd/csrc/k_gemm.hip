@@ -232,6 +232,8 @@ hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s) {
   return launch_s<4, 1, EPI_BF16, 2>(a, s);
 }
 hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s) {
+  // long prefill chunks: 64-token tiles, so the router weights are re-read 4x less often
+  if (a.ntok >= 1024) return launch_s<4, 1, EPI_F32, 3>(a, s);
   return launch_s<1, 1, EPI_F32, 3>(a, s);
 }
 
