@@ -172,6 +172,26 @@ def prefill_measure(driver, model, dims, dev, prompt=8192, chunk=2048, reps=2):
                               flops=round(flops)))
 
 
+def generate_measure(driver, model, kv, params, dims, dev, cache_len, gen_length=512):
+    """The native generation loop (dg_generate) for gen_length tokens on the benchmark's cache:
+    canvases of up to 48 steps with the done flags read after every step, each appended."""
+    import torch
+    state = driver.SamplerState(1, dims["C"], dev)
+    out = driver.StepOut(1, dims["C"], dims["V"], dev)
+    ws = driver.workspace(driver._lib.load().dg_generate_workspace_bytes(model.handle, 1), dev)
+    kv.len[0] = cache_len
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, n, steps = driver.generate(model, kv, params, state, out, gen_length, ws=ws)
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    kv.len[0] = cache_len
+    return dict(workload=f"{gen_length} tokens after a {cache_len}-token cache, "
+                         f"{dims['n_layers']} layers, adaptive stop on",
+                tokens_per_s=round(n * dims["C"] / t, 2), ms=round(t * 1e3, 1), canvases=n,
+                steps_per_canvas=steps)
+
+
 def sampler_roofline(driver, timer, dev, vocab, steps=8):
     """The standalone EB sampler (dg_eb_sample) on the standalone sampler workload: HBM rate of
     its statistics kernel (one read of the logits) and the time of the whole call."""
@@ -405,6 +425,8 @@ def main():
         attention=dict(mfma_line(at_flops / max(n_at, 1), t_at, n_at,
                                  "attention (+ split merge), averaged over the pass"),
                        flops_per_launch=round(at_flops / max(n_at, 1))))
+    log("timing the native generation loop")
+    gen = generate_measure(driver, model, kv, params, dims, dev, args.cache)
     log("timing the chunked prefill")
     prefill = prefill_measure(driver, model, dims, dev)
     log("timing the standalone EB sampler")
@@ -439,7 +461,7 @@ def main():
         tokens_per_s=round(tokens / elapsed, 2),
         decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
         roofline=roofline, cpu_baseline=cpu, rooflines=rooflines,
-        measured_peaks=peaks, prefill=prefill,
+        measured_peaks=peaks, prefill=prefill, generate=gen,
         kernel_ms_per_bench_step=kernel_ms)
     print(json.dumps(line))
 

@@ -54,6 +54,10 @@ class dg_step_out(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("entropy", "argmax", "commit_now", "logits")]
 
 
+class dg_gen_params(ctypes.Structure):
+    _fields_ = [("gen_length", i32), ("eos_token_id", i32), ("eos_early_stop", i32)]
+
+
 P = ctypes.POINTER
 _SIGS = {
     "dg_last_error": (ctypes.c_char_p, []),
@@ -70,6 +74,10 @@ _SIGS = {
     "dg_kv_append_canvas": (i32, [c_void_p, P(dg_kv), c_void_p, c_void_p, ctypes.c_size_t,
                                   c_void_p]),
     "dg_append_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32, i32]),
+    "dg_generate_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32]),
+    "dg_generate": (i32, [c_void_p, P(dg_kv), P(dg_gen_params), P(dg_eb_params), P(dg_eb_state),
+                          P(dg_step_out), c_void_p, P(i32), c_void_p, c_void_p, ctypes.c_size_t,
+                          c_void_p]),
     "dg_kv_append_tokens": (i32, [c_void_p, P(dg_kv), c_void_p, i32, c_void_p, ctypes.c_size_t,
                                   c_void_p]),
     "dg_layer_forward": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p, c_void_p,

@@ -788,6 +788,81 @@ dg_status dg_kv_append_tokens(const dg_model* m, dg_kv* kv, const int32_t* token
   return encoder_append(m, kv, tokens, n_tokens, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+size_t dg_generate_workspace_bytes(const dg_model* m, int32_t batch) {
+  const size_t base = dg_workspace_bytes(m, batch);
+  return base ? base + 512 : 0;   // + the canvas ids of the current canvas, 256-byte aligned
+}
+
+dg_status dg_generate(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
+                      const dg_eb_params* p, dg_eb_state* state, dg_step_out* out,
+                      int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
+                      size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if (!gen || !tokens || !canvases || !ws) return fail(DG_ERR_NULL, "gen, tokens, canvases or ws is NULL");
+  const int C = m->dims.canvas_len;
+  if (gen->gen_length < 1) return fail(DG_ERR_SHAPE, "gen_length must be >= 1");
+  const long long total_ll = (static_cast<long long>(gen->gen_length) + C - 1) / C;
+  if ((s = check_params(p, 0)) != DG_OK) return s;
+  if ((s = check_state(state)) != DG_OK) return s;
+  if ((s = check_out(out, true)) != DG_OK) return s;
+  if ((s = check_kv(m, kv, false)) != DG_OK) return s;
+  for (int b = 0; b < kv->batch; ++b)
+    if (kv->len[b] + total_ll * C > kv->cap)
+      return fail(DG_ERR_CAPACITY, "kv len[%d] + %lld generated tokens exceeds cap %d", b,
+                  total_ll * C, kv->cap);
+  const int B = kv->batch, total = static_cast<int>(total_ll);
+  if (static_cast<long long>(total) * B > (1ll << 31))
+    return fail(DG_ERR_SHAPE, "too many canvases for 31-bit canvas ids");
+  const size_t need = dg_generate_workspace_bytes(m, B);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t step_ws = dg_workspace_bytes(m, B);
+  uint32_t* ids = reinterpret_cast<uint32_t*>(
+      (reinterpret_cast<uintptr_t>(ws) + step_ws + 255) & ~static_cast<uintptr_t>(255));
+  dg_eb_state st = *state;
+  st.canvas_id = ids;
+  std::vector<uint32_t> hid(B);
+  std::vector<int32_t> hdone(B), hcanvas(static_cast<size_t>(B) * C);
+  std::vector<char> has_eos(B, 0);
+  *canvases = 0;
+  for (int c = 0; c < total; ++c) {
+    // canvas c of sequence b draws its noise with canvas id c * B + b
+    for (int b = 0; b < B; ++b) hid[b] = static_cast<uint32_t>(c * B + b);
+    DG_HIP(hipMemcpyAsync(ids, hid.data(), sizeof(uint32_t) * B, hipMemcpyHostToDevice, hs));
+    if ((s = dg_canvas_init(p, &st, B, C, m->dims.vocab, stream)) != DG_OK) return s;
+    int n = 0;
+    for (int step = 0; step < p->max_steps; ++step) {
+      if ((s = dg_decoder_step(m, kv, step, p, &st, out, ws, step_ws, stream)) != DG_OK) return s;
+      ++n;
+      // adaptive stop: the canvas's loop ends once every sample is frozen
+      DG_HIP(hipMemcpyAsync(hdone.data(), st.done, sizeof(int32_t) * B, hipMemcpyDeviceToHost, hs));
+      DG_HIP(hipStreamSynchronize(hs));
+      bool all = true;
+      for (int b = 0; b < B; ++b) all = all && hdone[b] != 0;
+      if (all) break;
+    }
+    DG_HIP(hipMemcpy2DAsync(tokens + static_cast<size_t>(c) * C, sizeof(int32_t) * total * C,
+                            st.canvas, sizeof(int32_t) * C, sizeof(int32_t) * C, B,
+                            hipMemcpyDeviceToDevice, hs));
+    if ((s = dg_kv_append_canvas(m, kv, st.canvas, ws, step_ws, stream)) != DG_OK) return s;
+    if (steps) steps[c] = n;
+    *canvases = c + 1;
+    if (gen->eos_token_id >= 0) {
+      DG_HIP(hipMemcpyAsync(hcanvas.data(), st.canvas, sizeof(int32_t) * B * C,
+                            hipMemcpyDeviceToHost, hs));
+      DG_HIP(hipStreamSynchronize(hs));
+      bool all = true;
+      for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < C && !has_eos[b]; ++i) has_eos[b] = hcanvas[b * C + i] == gen->eos_token_id;
+        all = all && has_eos[b];
+      }
+      if (gen->eos_early_stop && all) break;
+    }
+  }
+  return DG_OK;
+}
+
 dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, int32_t causal,
                            float* h, float* router_logits, int32_t* topk_idx, float* gates,
                            void* ws, size_t ws_bytes, void* stream) {

@@ -223,6 +223,29 @@ def kv_append_tokens(model, kv, tokens, ws, stream=None):
                                   ws.numel(), stream_ptr(stream)), "dg_kv_append_tokens")
 
 
+def generate(model, kv, params, state, out, gen_length, eos_token_id=-1, eos_early_stop=True,
+             ws=None, stream=None):
+    """The canvas loop on a cache that holds the prompt: returns (tokens [B, n*C] int32 device,
+    canvases generated, decoder steps per canvas)."""
+    lib = _lib.load()
+    c = state.C
+    n = -(-int(gen_length) // c)
+    tokens = torch.zeros((state.B, n * c), dtype=torch.int32, device=state.canvas.device)
+    if ws is None:
+        ws = workspace(lib.dg_generate_workspace_bytes(model.handle, state.B),
+                       state.canvas.device)
+    gen = _lib.dg_gen_params(int(gen_length), int(eos_token_id), 1 if eos_early_stop else 0)
+    kvs, st, o = kv.struct(), state.struct(), out.struct()
+    done = ctypes.c_int32(0)
+    steps = (ctypes.c_int32 * n)()
+    check(lib.dg_generate(model.handle, ctypes.byref(kvs), ctypes.byref(gen), ctypes.byref(params),
+                          ctypes.byref(st), ctypes.byref(o), ptr(tokens), ctypes.byref(done),
+                          ctypes.cast(steps, ctypes.c_void_p), ptr(ws), ws.numel(),
+                          stream_ptr(stream)), "dg_generate")
+    k = done.value
+    return tokens[:, :k * c], k, [steps[i] for i in range(k)]
+
+
 def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=None,
                   gates=None, stream=None):
     lib = _lib.load()

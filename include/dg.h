@@ -198,6 +198,38 @@ size_t dg_append_workspace_bytes(const dg_model* model, int32_t batch, int32_t m
 dg_status dg_kv_append_tokens(const dg_model* model, dg_kv* kv, const int32_t* tokens,
                               int32_t n_tokens, void* ws, size_t ws_bytes, void* stream);
 
+/* The outer generation loop (diffusers DiffusionGemmaPipeline docs, the __call__ parameters
+ * gen_length, num_inference_steps, eos_early_stop, eos_token_id, and "Adaptive stopping";
+ * DiffusionGemma model card, "Model overview": a finished canvas is encoded and appended before
+ * the next one starts). */
+typedef struct {
+  int32_t gen_length;       /* tokens per sequence, rounded up to whole canvases (>= 1)       */
+  int32_t eos_token_id;     /* < 0: no EOS check                                              */
+  int32_t eos_early_stop;   /* nonzero: start no further canvas once every sequence has
+                               produced eos_token_id (at any position of a finished canvas)   */
+} dg_gen_params;
+
+/* Workspace of dg_generate: dg_workspace_bytes(model, batch) + 512 (0 on invalid arguments). */
+size_t dg_generate_workspace_bytes(const dg_model* model, int32_t batch);
+
+/* Generates up to n = ceil(gen_length / canvas_len) canvases per sequence on a cache that holds
+ * the prompt (see dg_kv_append_tokens).  For canvas c: the initial canvas with canvas ids
+ * c * B + b (state->canvas_id is not read), then dg_decoder_step for steps 0, 1, ... until every
+ * sample is frozen or max_steps steps ran, then the canvas is copied to
+ * tokens[b, c*C : (c+1)*C] and appended with dg_kv_append_canvas.  The EOS check follows each
+ * canvas.  tokens: device int32 [B, n * C]; *canvases (host): canvases generated; steps (host,
+ * optional, [n]): decoder steps run per canvas.  state and out hold the last canvas's state and
+ * step outputs (out->logits is required).  Unlike the step calls, this call synchronises the
+ * stream after every step (to read the done flags) and after every canvas with an EOS check;
+ * it returns with the last canvas's copy and append enqueued.  kv->len advances by C per
+ * canvas.  Errors: those of the calls it makes, checked first where possible: DG_ERR_NULL,
+ * DG_ERR_SHAPE (gen_length < 1), DG_ERR_CAPACITY (len + n * C > cap), DG_ERR_WORKSPACE,
+ * DG_ERR_STATE, DG_ERR_HIP. */
+dg_status dg_generate(const dg_model* model, dg_kv* kv, const dg_gen_params* gen,
+                      const dg_eb_params* params, dg_eb_state* state, dg_step_out* out,
+                      int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* dg_last_error(void);
 

@@ -211,6 +211,38 @@ def test_append_tokens_validate():
     lib.dg_model_destroy(h)
 
 
+def test_generate_validates():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    assert st == 0
+    lens = (ctypes.c_int32 * 1)(60)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens)
+    p = driver.eb_params(max_steps=8)
+    state = _lib.dg_eb_state(*([0x1000] * 7))
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0x1000)
+    need = lib.dg_generate_workspace_bytes(h, 1)
+    assert need == lib.dg_workspace_bytes(h, 1) + 512
+    fake = ctypes.c_void_p(0x1000)
+    done = ctypes.c_int32(-7)
+
+    def call(g, ws=need, tokens=fake, o=out):
+        gen = _lib.dg_gen_params(g, -1, 1)
+        return lib.dg_generate(h, ctypes.byref(kv), ctypes.byref(gen), ctypes.byref(p),
+                               ctypes.byref(state), ctypes.byref(o), tokens, ctypes.byref(done),
+                               None, fake, ws, None)
+
+    assert call(4) == 4                  # 60 + one 16-token canvas > cap 64: DG_ERR_CAPACITY
+    lens[0] = 0
+    assert call(0) == 2                  # gen_length < 1: DG_ERR_SHAPE
+    assert call(65) == 4                 # 5 canvases = 80 tokens > 64
+    assert call(64, ws=need - 1) == 5    # DG_ERR_WORKSPACE
+    assert call(64, tokens=None) == 1    # DG_ERR_NULL
+    out2 = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0)
+    assert call(64, o=out2) == 1         # logits are required
+    assert lens[0] == 0 and done.value == -7
+    lib.dg_model_destroy(h)
+
+
 def test_prof_classes_named():
     t = driver.KernelTimer()
     assert "moe_gateup" in t.names and "lmhead" in t.names and "attention" in t.names
