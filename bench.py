@@ -300,8 +300,8 @@ def cpu_baseline(dims, n_layers_sample, cache_len):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
-              f"across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library does not "
+              f"shard the path across GPUs.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
@@ -395,7 +395,8 @@ def main():
                     experts_touched=n_touched)
     kernel_ms = {n: round(v[0], 3) for n, v in per_class.items() if v[1]}
 
-    # the other kernels the path is judged on, from the per-class pass (HIP events per launch)
+    # the other kernels of the path with a roofline line, from the per-class pass (HIP events per
+    # launch)
     def rate(name):
         ms, n = per_class[name]
         return ms / max(n, 1) * 1e-3, n

@@ -50,7 +50,7 @@ typedef enum {
   DG_ERR_CAPACITY = 4,     /* len[b] + canvas_len > KV capacity                               */
   DG_ERR_WORKSPACE = 5,    /* workspace smaller than the size query returned                  */
   DG_ERR_STATE = 6,        /* step index outside [0, max_steps) or bad sampler parameters     */
-  DG_ERR_UNSUPPORTED = 7,  /* valid request this build does not implement                     */
+  DG_ERR_UNSUPPORTED = 7,  /* valid request the library does not implement                   */
   DG_ERR_HIP = 8,          /* a HIP runtime call failed                                        */
   DG_ERR_NONFINITE = 9     /* written to *dev_status when a logit row is not finite           */
 } dg_status;
