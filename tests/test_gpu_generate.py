@@ -8,6 +8,8 @@ to generate (3 canvases of 16).
   for 2 sequences: tokens, canvases, steps per canvas and the cache agree bit for bit.
 - Against the oracle's loop (oracle/generate.py) for 1 sequence: tokens, canvases and steps per
   canvas agree exactly, without and with an EOS id taken from the first canvas (one canvas).
+- Two sequences with an EOS id that one of them produces only in its second canvas: the loop
+  stops after that canvas, with the tokens of the full run.
 """
 import numpy as np
 import pytest
@@ -90,3 +92,27 @@ def test_generate_matches_oracle(use_eos):
     assert n == ref["canvases"] == (1 if use_eos else 3)
     assert steps == ref["steps"]
     np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])
+
+
+def test_generate_eos_waits_for_every_sequence():
+    """Two sequences: an EOS id that sequence 0 produces in its first canvas and sequence 1 only
+    in its second stops the native loop after the second canvas, with the tokens of the full
+    run."""
+    B = 2
+    dims, mnp, model, prompt, kv = _gpu_setup(B)
+    p = driver.eb_params_from_dict(dict(osamp.default_params(), max_steps=8), 2)
+    state = driver.SamplerState(B, dims["C"], DEV)
+    out = driver.StepOut(B, dims["C"], dims["V"], DEV)
+    full, n, _ = driver.generate(model, kv, p, state, out, gen_length=48)
+    t = full.cpu().numpy()
+    canv = [[set(t[b, 16 * c:16 * c + 16].tolist()) for c in range(3)] for b in range(B)]
+    cands = [v for v in sorted(canv[0][0]) if v not in canv[1][0] and v in canv[1][1]]
+    cands += [v for v in sorted(canv[1][0]) if v not in canv[0][0] and v in canv[0][1]]
+    assert n == 3 and cands, "no token with the needed pattern"
+    _, _, _, _, kv2 = _gpu_setup(B)
+    print(f"generate case: EOS {cands[0]} with 2 sequences", flush=True)
+    tok, n2, _ = driver.generate(model, kv2, p, state, out, gen_length=48, eos_token_id=cands[0])
+    torch.cuda.synchronize()
+    assert n2 == 2
+    assert torch.equal(tok, full[:, :32])
+    assert kv2.lengths() == [32 + 32] * B
