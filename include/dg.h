@@ -24,8 +24,9 @@
  *   - bf16 tensors are passed as uint16_t bit patterns (or const void*), row-major, with the
  *     layouts stated below.  Weight matrices are [out_features, in_features].
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous on it:
- *     DG_OK means "validated and enqueued".  No call synchronises the host or allocates, so a
- *     decoder step can be captured in a HIP graph.
+ *     DG_OK means "validated and enqueued".  No call allocates device memory, and no call but
+ *     dg_generate (which reads the done flags on the host) synchronises the host, so a decoder
+ *     step can be captured in a HIP graph.
  *   - Validation is synchronous and happens before anything is enqueued: on a non-OK status
  *     nothing was enqueued and dg_last_error() describes the problem.  No C++ exception crosses
  *     the ABI.
