@@ -11,6 +11,9 @@ Workloads:
   256, 16 experts top-4 + shared): a 1,024-token prompt in one call, in four canvas-sized calls
   and in a ragged split (300 + 724), each against the oracle's one-pass encoding, with at most 1%
   of the token rows outside the tolerance (routing near-ties);
+- the toy decoder with a 24-token sliding window on layer 0: 96 tokens in 4 calls of 24, against
+  the oracle encoding with the same split (the window applies to cached keys only, so a windowed
+  prefill depends on the split);
 - two full-width layers (d 2816, 16/8 heads of 256, 128 experts top-8 + shared): a 1,024-token
   prompt on top of a 512-entry N(0,1) cache, appended in one call and in a ragged split
   (300 + 724), against four canvas appends of 256 tokens (the path the decoder tests compare with
@@ -164,3 +167,33 @@ def test_prefill_mid_width_matches_oracle(split):
             print(f"  layer {layer} {name}: rel {rel:.3g}, bad rows {bad.size}: {bad[:12]}",
                   flush=True)
             assert rel <= REL and ok.mean() >= 0.99, f"layer {layer} {name} split {split}"
+
+
+def test_prefill_windowed_matches_oracle_chunk_by_chunk():
+    """Sliding-window layers: with the window on cached keys only (the canvas, here the new
+    tokens, is always fully visible), a windowed prefill depends on the split, so the oracle
+    encodes with the same split.  Layer 0 keeps a 24-token window, layer 1 is global; 96 tokens
+    in 4 calls of 24, so from the second call on the window cuts into earlier calls' keys."""
+    dims = dict(synth.dims_tiny(), window=24, global_every=2)
+    mnp = synth.make_model(dims, seed=3, norm_gain_std=0.1)
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    prompt = synth.prompt_ids(96, dims["V"], seed=11)
+    cap, split = 128, (24, 24, 24, 24)
+    kv = driver.KVCache(dims, 1, cap, DEV)
+    ws = driver.workspace(model.append_workspace_bytes(1, 24))
+    print("prefill case windowed tiny, 4 x 24", flush=True)
+    _append_split(model, kv, prompt, split, ws)
+    torch.cuda.synchronize()
+    ref = synth.empty_cache(dims, 1, cap)
+    ref = dict(k=[a.astype(np.float64) for a in ref["k"]], v=[a.astype(np.float64) for a in ref["v"]],
+               len=np.array(ref["len"]))
+    m64 = synth.model_to_f64(mnp)
+    c0 = 0
+    for n in split:
+        om.encoder_append(prompt[None, c0:c0 + n], m64, ref)
+        c0 += n
+    for layer in range(dims["n_layers"]):
+        assert_close_rel(kv.k[layer].float().cpu().numpy()[:, :, :96], ref["k"][layer][:, :, :96],
+                         what=f"K layer {layer} (windowed)")
+        assert_close_rel(kv.v[layer].float().cpu().numpy()[:, :, :96], ref["v"][layer][:, :, :96],
+                         what=f"V layer {layer} (windowed)")
