@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--canvases", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=1)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill measurement (one JSON object) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run only the library's plain copy kernel on buffers of this many MiB "
                          "(known bytes, to scale hardware byte counters) and exit")
@@ -312,6 +314,10 @@ def main():
 
     dev = "cuda"
     dims = synth.dims_full(n_layers=args.layers)
+    if args.prefill_only:
+        pmodel = driver.Model(synth.make_model_device(dims, dev, seed=0))
+        print(json.dumps(prefill_measure(driver, pmodel, dims, dev)))
+        return
     C, B = dims["C"], 1
     cap = args.cache + C * args.canvases
     weights = synth.make_model_device(dims, dev, seed=0)
