@@ -14,6 +14,9 @@ from HIP events in an untimed pass: the MFMA fraction of the LM head and of atte
 flops), the HBM fraction of the MoE down product, and the HBM fraction of the standalone EB
 sampler's statistics kernel on the standalone sampler workload (bf16 logits [256 x 262144]:
 30% peaked rows with one logit 12 over N(0,1), 40% N(0,2) rows, 30% N(0,0.1) rows).
+Also, outside the timed region: the native generation loop (dg_generate) for 512 tokens on the
+same cache (`generate`), and the chunked prefill of an 8,192-token prompt in 2,048-token calls
+with its MFMA fraction from exact flops (`prefill`; `--prefill-only` runs just that).
 """
 import argparse
 import json
