@@ -50,6 +50,17 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=1)
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill measurement (one JSON object) and exit")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
+    ap.add_argument("--no-generate", action="store_true", help="skip the generation-loop line")
+    ap.add_argument("--no-sampler", action="store_true",
+                    help="skip the standalone sampler line and the measured ceilings")
+    ap.add_argument("--long-fp8-only", action="store_true",
+                    help="run only the long-context batched fp8 workload (one JSON object)")
+    ap.add_argument("--no-long-fp8", action="store_true",
+                    help="skip the long-context batched fp8 line")
+    ap.add_argument("--decoder-only", action="store_true",
+                    help="only the decoder steps and appends (for hardware-counter runs: no "
+                         "prefill, generation loop, standalone sampler, ceilings or CPU oracle)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run only the library's plain copy kernel on buffers of this many MiB "
                          "(known bytes, to scale hardware byte counters) and exit")
@@ -258,6 +269,184 @@ def measured_traffic():
         return None
 
 
+def touched_experts(driver, model, kv, state, embed, params, dims, ws, cache_len, canvases):
+    """(step, distinct routed experts) of every expert launch of one pass, in launch order: the
+    pass is replayed, and before each decoder step the layer chain runs on the step's canvas with
+    top-k traces (the chain's expert sets are the step's own)."""
+    import torch
+    B, C, k, V = kv.batch, dims["C"], dims["top_k"], dims["V"]
+    out = driver.StepOut(B, C, V, "cuda")
+    h = torch.empty((B * C, dims["d"]), dtype=torch.float32, device="cuda")
+    ti = torch.empty((B * C, k), dtype=torch.int32, device="cuda")
+    counts = []
+    kv.len[0] = cache_len
+    for _ in range(canvases):
+        driver.canvas_init(params, state, V)
+        for s in range(params.max_steps):
+            ids = state.canvas.view(-1).long().clamp(0, V - 1)
+            h.copy_(torch.index_select(embed, 0, ids).float())
+            for layer in range(dims["n_layers"]):
+                driver.layer_forward(model, kv, layer, 0, h, ws, None, ti, None)
+                counts.append((s, int(torch.unique(ti).numel())))
+            driver.decoder_step(model, kv, s, params, state, out, ws)
+            if bool(state.done.all()):
+                break
+        driver.kv_append_canvas(model, kv, state.canvas, ws)
+    torch.cuda.synchronize()
+    kv.len[0] = cache_len
+    return counts
+
+
+def attention_flops_windowed(dims, cache_len, window, causal):
+    """Algorithmic flops of one sliding-window layer's attention: canvas query i sees the cache
+    positions less than `window` back from its absolute position, and the canvas (all of it, or
+    the causal prefix)."""
+    c, hq, dh = dims["C"], dims["hq"], dims["dh"]
+    keys = 0.0
+    for i in range(c):
+        keys += min(cache_len, max(window - 1 - i, 0)) + ((i + 1) if causal else c)
+    return 4.0 * hq * keys * dh
+
+
+def long_fp8_measure(driver, dev, layers=30, batch=4, cache=131072, steps=1, warmup=1,
+                     cpu=True):
+    """The long-context batched fp8 workload: the full-width decoder with e4m3 expert and LM-head
+    weights (per-row fp32 scales), 4 canvases of 256 tokens each on its own 131,072-token N(0,1)
+    cache, 5 sliding-window (1,024) layers to 1 global; one bench step = every canvas's EB steps
+    (48, adaptive stop on) + the append of the 4 canvases.  Returns one JSON-able dict."""
+    import torch
+    from block_diffusion_decoding_canvas_amd import synth
+    dims = synth.dims_long(n_layers=layers)
+    B, C, V = batch, dims["C"], dims["V"]
+    log(f"long fp8: drawing the model and {batch} x {cache}-token caches")
+    w = synth.make_model_device(dims, dev, seed=0)
+    model = driver.Model(w, wdtype="e4m3")
+    cap = cache + C
+    kc, vc = synth.make_cache_device(dims, B, cap, cache, dev, seed=1)
+    kv = driver.KVCache(dims, B, cap, dev, kc, vc, [cache] * B)
+    ws = driver.workspace(model.workspace_bytes(B), dev)
+    params = driver.eb_params()
+    state = driver.SamplerState(B, C, dev)
+    out = driver.StepOut(B, C, V, dev)
+    timer = driver.KernelTimer()
+    torch.cuda.synchronize()
+
+    def one_pass():
+        for b in range(B):
+            kv.len[b] = cache
+        driver.canvas_init(params, state, V)
+        n = 0
+        for s in range(params.max_steps):
+            driver.decoder_step(model, kv, s, params, state, out, ws)
+            n += 1
+            if bool(state.done.all()):
+                break
+        driver.kv_append_canvas(model, kv, state.canvas, ws)
+        return n
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    log("long fp8: timing")
+    t0 = time.perf_counter()
+    n_steps = sum(one_pass() for _ in range(steps))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # per-class pass: attention and the fp8 expert stream
+    timer.reset()
+    timer.enable(["attention", "moe_gateup", "lmhead"])
+    n_pass = one_pass()
+    torch.cuda.synchronize()
+    timer.enable([])
+    ms_at, n_at = timer.read("attention")
+    ms_gu, n_gu = timer.read("moe_gateup")
+    at_flops = 0.0
+    for layer in range(layers):
+        glob = (layer + 1) % dims["global_every"] == 0
+        f_dec = (attention_flops(dims, cache, False) if glob else
+                 attention_flops_windowed(dims, cache, dims["window"], False))
+        f_app = (attention_flops(dims, cache, True) if glob else
+                 attention_flops_windowed(dims, cache, dims["window"], True))
+        at_flops += B * (n_pass * f_dec + f_app)
+    t_at = ms_at * 1e-3
+    at_tf = at_flops / t_at / 1e12
+    # fp8 expert bytes per gate/up launch: every expert is touched at 1,024 routed tokens x 8
+    d, f, fs, k = dims["d"], dims["F"], dims["Fs"], dims["top_k"]
+    T = B * C
+    gu_bytes = (dims["E"] * 2 * f * d + 2 * fs * d) + T * d + (T * k * f + T * fs) * 4
+    gu_t = ms_gu / max(n_gu, 1) * 1e-3
+    gu_gbs = gu_bytes / gu_t / 1e9
+    res = dict(
+        workload=(f"{layers}-layer full-width decoder, e4m3 experts + LM head, {B} x 256-token "
+                  f"canvases on {cache}-token caches each, 5 sliding-window (1024) : 1 global "
+                  f"layers, 48 EB steps max (adaptive stop) + append per bench step"),
+        steps_per_s=round(n_steps / elapsed, 3), tokens_per_s=round(B * C * steps / elapsed, 2),
+        ms_per_bench_step=round(elapsed / steps * 1e3, 1), decoder_steps=n_steps,
+        bench_steps=steps, warmup=warmup, dtype="e4m3 experts and LM head, bf16 attention",
+        roofline=dict(bound="mfma", achieved=round(at_tf, 1), peak=MFMA_BF16_PEAK_TFS,
+                      unit="TFLOP/s", frac=round(at_tf / MFMA_BF16_PEAK_TFS, 4),
+                      kernel="attention (+ split merge): global and windowed layers",
+                      launches=n_at, ms_per_pass=round(ms_at, 2)),
+        moe_gateup_fp8=dict(bound="hbm", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
+                            unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4),
+                            bytes_per_launch=gu_bytes, avg_launch_us=round(gu_t * 1e6, 2),
+                            launches=n_gu))
+    del model, w, kv, kc, vc, ws, out
+    torch.cuda.empty_cache()
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_long(dims, B, cache)
+    return res
+
+
+def cpu_baseline_long(dims, batch, cache_len):
+    """The oracle on a bounded sample of the long-context fp8 step: one global and one windowed
+    full-width layer (e4m3 experts) over one 256-token canvas on a cache of `cache_len`, the fp8
+    LM head and the EB sampler; per step = batch x (global layers x global + windowed layers x
+    windowed + LM head + sampler)."""
+    import numpy as np
+    from block_diffusion_decoding_canvas_amd import synth
+    from oracle import model as om
+    from oracle import sampler as osamp
+    from oracle.numerics import quantize_rows_e4m3, round_bf16
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    C, d = dims["C"], dims["d"]
+    h = synth.hidden_states(C, d, seed=1).astype(np.float64)[None]
+    times = {}
+    for name, layer in (("windowed", 0), ("global", dims["global_every"] - 1)):
+        lw = om.quantize_layer_e4m3({k: v.astype(np.float64)
+                                     for k, v in synth.make_layer(dims, rng).items()})
+        n_keys = cache_len if name == "global" else dims["window"] - 1
+        cache = synth.make_cache(dict(dims, n_layers=1), 1, n_keys, n_keys, seed=1)
+        kc, vc = cache["k"][0].astype(np.float64), cache["v"][0].astype(np.float64)
+        t0 = time.perf_counter()
+        om.layer_forward(h, lw, dims, layer, kc, vc, np.array([n_keys]), causal=False)
+        times[name] = time.perf_counter() - t0
+        log(f"oracle {name} layer: {times[name]:.1f} s")
+        del lw, kc, vc
+    w_lm = synth.to_bf16_values(rng.standard_normal((dims["V"], d), dtype=np.float32) * 0.02)
+    wq, s_lm = quantize_rows_e4m3(w_lm.astype(np.float64))
+    del w_lm
+    t0 = time.perf_counter()
+    z = om.fp8_linear(om.rms_norm(h, np.ones(d), dims["eps"]), wq, s_lm)
+    zr = round_bf16(z)
+    t_lm = time.perf_counter() - t0
+    del wq, z
+    st = osamp.new_state(osamp.init_canvas(2, [0], C, dims["V"]))
+    t0 = time.perf_counter()
+    osamp.eb_step(zr, 0, osamp.default_params(), st, 2, [0])
+    t_samp = time.perf_counter() - t0
+    n_glob = dims["n_layers"] // dims["global_every"]
+    per_canvas = (n_glob * times["global"] + (dims["n_layers"] - n_glob) * times["windowed"] +
+                  t_lm + t_samp)
+    return dict(value=1.0 / (batch * per_canvas), unit="steps/s", cores=cores, kind="oracle",
+                sample=(f"one global ({times['global']:.1f} s, {cache_len} cached keys) and one "
+                        f"windowed ({times['windowed']:.1f} s) full-width e4m3 layer, the fp8 LM "
+                        f"head ({t_lm:.1f} s) and the EB sampler ({t_samp:.1f} s) for one 256-token "
+                        f"canvas, fp64 numpy; per step = {batch} canvases x ({n_glob} global + "
+                        f"{dims['n_layers'] - n_glob} windowed layers + LM head + sampler)"))
+
+
 def cpu_baseline(dims, n_layers_sample, cache_len):
     """The oracle (fp64 numpy) on a bounded sample of one decoder step: `n_layers_sample`
     full-width layers over the 256-token canvas with the N(0,1) cache, the LM head and the EB
@@ -321,6 +510,10 @@ def main():
         pmodel = driver.Model(synth.make_model_device(dims, dev, seed=0))
         print(json.dumps(prefill_measure(driver, pmodel, dims, dev)))
         return
+    if args.long_fp8_only:
+        print(json.dumps(long_fp8_measure(driver, dev, layers=args.layers,
+                                          cpu=not args.no_cpu_baseline)))
+        return
     C, B = dims["C"], 1
     cap = args.cache + C * args.canvases
     weights = synth.make_model_device(dims, dev, seed=0)
@@ -383,25 +576,28 @@ def main():
     timer.enable([])
     per_class = {n: timer.read(n) for n in timer.names}
 
-    # experts touched in a layer: count distinct routed experts on layer 0's router
-    h0 = torch.zeros((B * C, dims["d"]), dtype=torch.float32, device=dev)
-    h0.copy_(torch.index_select(weights["embed"], 0, state.canvas.view(-1).long()).float())
-    ti = torch.zeros((B * C, dims["top_k"]), dtype=torch.int32, device=dev)
-    kv.len[0] = args.cache
-    driver.layer_forward(model, kv, 0, 0, h0, ws, None, ti, None)
-    torch.cuda.synchronize()
-    n_touched = int(torch.unique(ti).numel())
-
+    # experts touched by each timed gate/up launch: the passes are deterministic (same seed,
+    # canvas ids and cache lengths), so one more pass replays the sampled steps exactly; before
+    # each of them the GPU layer chain (dg_layer_forward, the step's own kernels) yields every
+    # layer's expert sets
+    every_step = touched_experts(driver, model, kv, state, weights["embed"], params, dims, ws,
+                                 args.cache, args.canvases)
+    touched = [n for s_, n in every_step if s_ % GATEUP_SAMPLE_EVERY == 0]
     avg_gu = ms_gu / max(n_gu, 1) * 1e-3
-    bytes_gu = moe_gateup_bytes(dims, n_touched)
+    per_pass = len(touched)
+    assert n_gu == per_pass * args.steps, (n_gu, per_pass)
+    bytes_gu = sum(moe_gateup_bytes(dims, n) for n in touched) / per_pass
     achieved = bytes_gu / avg_gu / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
-                    kernel="moe_gateup", bytes_per_launch=bytes_gu,
+                    kernel="moe_gateup", bytes_per_launch=round(bytes_gu),
                     avg_launch_us=round(avg_gu * 1e6, 2), launches=n_gu,
                     launches_sampled=(f"every {GATEUP_SAMPLE_EVERY}th decoder step of the timed "
                                       f"region, every layer"),
-                    experts_touched=n_touched)
+                    experts_touched=dict(min=min(touched), max=max(touched),
+                                         mean=round(sum(touched) / per_pass, 2)))
+    # the down product is timed over every launch of the per-class pass: every step's counts
+    n_touched = sum(n for _, n in every_step) / len(every_step)
     kernel_ms = {n: round(v[0], 3) for n, v in per_class.items() if v[1]}
 
     # the other kernels of the path with a roofline line, from the per-class pass (HIP events per
@@ -435,23 +631,29 @@ def main():
         attention=dict(mfma_line(at_flops / max(n_at, 1), t_at, n_at,
                                  "attention (+ split merge), averaged over the pass"),
                        flops_per_launch=round(at_flops / max(n_at, 1))))
-    log("timing the native generation loop")
-    gen = generate_measure(driver, model, kv, params, dims, dev, args.cache)
-    log("timing the chunked prefill")
-    prefill = prefill_measure(driver, model, dims, dev)
-    log("timing the standalone EB sampler")
-    rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
-    # every line also against a measured ceiling: a plain read stream for the HBM lines, the
-    # bf16 MFMA loop for the MFMA lines
-    peaks = measured_peaks(driver)
-    for line in rooflines.values():
-        if line["bound"] == "hbm":
-            line["frac_of_measured"] = round(line["achieved"] / peaks["hbm_read_gbs"], 4)
-        else:
-            line["frac_of_measured"] = round(line["achieved"] / peaks["mfma_bf16_tfs"], 4)
+    gen = prefill = peaks = None
+    if not (args.no_generate or args.decoder_only):
+        log("timing the native generation loop")
+        gen = generate_measure(driver, model, kv, params, dims, dev, args.cache)
+    if not (args.no_prefill or args.decoder_only):
+        log("timing the chunked prefill")
+        prefill = prefill_measure(driver, model, dims, dev)
+    if not (args.no_sampler or args.decoder_only):
+        log("timing the standalone EB sampler")
+        rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
+        # context only: what the library's plain read stream, copy and MFMA loop reach here
+        peaks = measured_peaks(driver)
+
+    long_fp8 = None
+    if not (args.no_long_fp8 or args.decoder_only):
+        log("freeing the bf16 model; timing the long-context fp8 workload")
+        del model, weights, kv, kc, vc, ws, out, state
+        torch.cuda.empty_cache()
+        long_fp8 = long_fp8_measure(driver, dev, layers=args.layers,
+                                    cpu=not args.no_cpu_baseline)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not (args.no_cpu_baseline or args.decoder_only):
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(dims, args.cpu_layers, args.cache)
 
@@ -471,7 +673,7 @@ def main():
         tokens_per_s=round(tokens / elapsed, 2),
         decoder_step_ms=round(elapsed / total_steps * 1e3, 3),
         roofline=roofline, cpu_baseline=cpu, rooflines=rooflines,
-        measured_peaks=peaks, prefill=prefill, generate=gen,
+        measured_peaks=peaks, prefill=prefill, generate=gen, long_fp8=long_fp8,
         kernel_ms_per_bench_step=kernel_ms)
     print(json.dumps(line))
 

@@ -45,6 +45,21 @@ class dg_eb_params(ctypes.Structure):
                 ("stability", i32), ("seed", ctypes.c_uint64)]
 
 
+DG_SCHED_ENTROPY_BOUND = 0
+DG_SCHED_BLOCK_REFINEMENT = 1
+DG_SCHED_DISCRETE_DDIM = 2
+
+
+class dg_sched_params(ctypes.Structure):
+    _fields_ = [("kind", i32), ("max_steps", i32), ("t_max", ctypes.c_double),
+                ("t_min", ctypes.c_double), ("entropy_bound", ctypes.c_double),
+                ("temperature", ctypes.c_double), ("threshold", ctypes.c_double),
+                ("editing_threshold", ctypes.c_double), ("top_k", i32),
+                ("corrector_steps", i32), ("corrector_k", i32),
+                ("stop_entropy", ctypes.c_double), ("stability", i32),
+                ("seed", ctypes.c_uint64)]
+
+
 class dg_eb_state(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("canvas", "committed", "prev_argmax", "stable_count",
                                         "done", "canvas_id", "dev_status")]
@@ -55,7 +70,8 @@ class dg_step_out(ctypes.Structure):
 
 
 class dg_gen_params(ctypes.Structure):
-    _fields_ = [("gen_length", i32), ("eos_token_id", i32), ("eos_early_stop", i32)]
+    _fields_ = [("gen_length", i32), ("eos_token_id", i32), ("eos_early_stop", i32),
+                ("compact_frozen", i32)]
 
 
 P = ctypes.POINTER
@@ -71,6 +87,16 @@ _SIGS = {
                               P(dg_step_out), c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_eb_sample": (i32, [c_void_p, i32, i32, i32, i32, P(dg_eb_params), P(dg_eb_state),
                            P(dg_step_out), c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_sample": (i32, [c_void_p, i32, i32, i32, i32, P(dg_sched_params), P(dg_eb_state),
+                        P(dg_step_out), c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_decoder_step_sched": (i32, [c_void_p, P(dg_kv), i32, P(dg_sched_params), P(dg_eb_state),
+                                    P(dg_step_out), c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_decoder_step_live": (i32, [c_void_p, P(dg_kv), i32, P(dg_sched_params), P(dg_eb_state),
+                                   P(dg_step_out), i32, P(i32), c_void_p, ctypes.c_size_t,
+                                   c_void_p]),
+    "dg_generate_sched": (i32, [c_void_p, P(dg_kv), P(dg_gen_params), P(dg_sched_params),
+                                P(dg_eb_state), P(dg_step_out), c_void_p, P(i32), c_void_p,
+                                c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_kv_append_canvas": (i32, [c_void_p, P(dg_kv), c_void_p, c_void_p, ctypes.c_size_t,
                                   c_void_p]),
     "dg_append_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32, i32]),
@@ -82,6 +108,8 @@ _SIGS = {
                                   c_void_p]),
     "dg_layer_forward": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_layer_forward_tokens": (i32, [c_void_p, P(dg_kv), i32, i32, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_ffn_forward": (i32, [c_void_p, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, ctypes.c_size_t, c_void_p]),
     "dg_lm_head_forward": (i32, [c_void_p, i32, c_void_p, i32, P(dg_eb_params), P(dg_step_out),

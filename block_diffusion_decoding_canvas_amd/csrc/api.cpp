@@ -145,9 +145,11 @@ struct EbWs {
   double* cand_score;
   int32_t* cand_idx;
   int n_cand;
+  dg::SoftStats* row;   // merged statistics per row
+  int32_t* cand;        // block refinement candidates per row
 };
 
-// The sampler's scratch, carved the same way for dg_eb_sample and dg_decoder_step.
+// The sampler's scratch, carved the same way for the standalone sampler and the decoder step.
 EbWs carve_eb(Carver& c, int rows, int n_part, int vocab) {
   EbWs w;
   w.n_part = n_part;
@@ -156,18 +158,66 @@ EbWs carve_eb(Carver& c, int rows, int n_part, int vocab) {
   w.n_cand = dg::cand_chunks(vocab);
   w.cand_score = c.take<double>(static_cast<size_t>(rows) * w.n_cand);
   w.cand_idx = c.take<int32_t>(static_cast<size_t>(rows) * w.n_cand);
+  w.row = c.take<dg::SoftStats>(rows);
+  w.cand = c.take<int32_t>(rows);
   return w;
 }
 
-dg_status check_params(const dg_eb_params* p, int32_t step) {
+// the entropy-bound constants as scheduler parameters
+dg_sched_params sched_from_eb(const dg_eb_params* p) {
+  dg_sched_params q;
+  memset(&q, 0, sizeof(q));
+  q.kind = DG_SCHED_ENTROPY_BOUND;
+  q.max_steps = p->max_steps;
+  q.t_max = p->t_max;
+  q.t_min = p->t_min;
+  q.entropy_bound = p->entropy_bound;
+  q.stop_entropy = p->stop_entropy;
+  q.stability = p->stability;
+  q.seed = p->seed;
+  q.editing_threshold = -1.0;
+  return q;
+}
+
+dg_status check_sched(const dg_sched_params* p, int32_t step) {
   if (!p) return fail(DG_ERR_NULL, "params is NULL");
   if (p->max_steps < 1) return fail(DG_ERR_STATE, "max_steps must be >= 1");
   if (step < 0 || step >= p->max_steps)
     return fail(DG_ERR_STATE, "step %d outside [0, %d)", step, p->max_steps);
-  if (!(p->t_max > 0.0) || !(p->t_min > 0.0)) return fail(DG_ERR_STATE, "temperatures must be > 0");
-  if (!(p->entropy_bound >= 0.0)) return fail(DG_ERR_STATE, "entropy_bound must be >= 0");
   if (p->stability < 0) return fail(DG_ERR_STATE, "stability must be >= 0");
-  return DG_OK;
+  switch (p->kind) {
+    case DG_SCHED_ENTROPY_BOUND:
+      if (!(p->t_max > 0.0) || !(p->t_min > 0.0))
+        return fail(DG_ERR_STATE, "temperatures must be > 0");
+      if (!(p->entropy_bound >= 0.0)) return fail(DG_ERR_STATE, "entropy_bound must be >= 0");
+      return DG_OK;
+    case DG_SCHED_BLOCK_REFINEMENT:
+      if (!(p->temperature >= 0.0) || !(p->temperature < 1e30))
+        return fail(DG_ERR_STATE, "temperature must be finite and >= 0");
+      if (!(p->threshold == p->threshold)) return fail(DG_ERR_STATE, "threshold is NaN");
+      if (!(p->editing_threshold == p->editing_threshold))
+        return fail(DG_ERR_STATE, "editing_threshold is NaN");
+      if (p->top_k != 0)
+        return fail(DG_ERR_UNSUPPORTED, "top_k = %d: the vocabulary top-k filter is not built",
+                    p->top_k);
+      return DG_OK;
+    case DG_SCHED_DISCRETE_DDIM:
+      if (!(p->temperature >= 0.0) || !(p->temperature < 1e30))
+        return fail(DG_ERR_STATE, "temperature must be finite and >= 0");
+      if (p->corrector_steps < 0 || p->corrector_steps > p->max_steps - 1)
+        return fail(DG_ERR_STATE, "corrector_steps = %d outside [0, max_steps - 1]",
+                    p->corrector_steps);
+      if (p->corrector_k < 0) return fail(DG_ERR_STATE, "corrector_k must be >= 0");
+      return DG_OK;
+    default:
+      return fail(DG_ERR_STATE, "unknown scheduler kind %d", p->kind);
+  }
+}
+
+dg_status check_params(const dg_eb_params* p, int32_t step) {
+  if (!p) return fail(DG_ERR_NULL, "params is NULL");
+  const dg_sched_params q = sched_from_eb(p);
+  return check_sched(&q, step);
 }
 
 dg_status check_state(const dg_eb_state* s) {
@@ -186,18 +236,25 @@ dg_status check_out(const dg_step_out* o, bool need_logits) {
   return DG_OK;
 }
 
-// T_s = t_max + (t_min - t_max) s / (S - 1) in fp64; the kernels use fp32(1 / T_s)
-void temperature(const dg_eb_params* p, int step, float* inv_t, float* inv_t_log2e) {
-  double t = p->t_max;
-  if (p->max_steps > 1)
-    t = p->t_max + (p->t_min - p->t_max) * static_cast<double>(step) /
-                       static_cast<double>(p->max_steps - 1);
+// The fp32 multiplier of the logits.  Entropy bound: T_s = t_max + (t_min - t_max) s / (S - 1)
+// in fp64; the others: the fixed temperature, 1 when greedy.  The kernels use fp32(1 / T).
+void temperature(const dg_sched_params* p, int step, float* inv_t, float* inv_t_log2e) {
+  double t = 1.0;
+  if (p->kind == DG_SCHED_ENTROPY_BOUND) {
+    t = p->t_max;
+    if (p->max_steps > 1)
+      t = p->t_max + (p->t_min - p->t_max) * static_cast<double>(step) /
+                         static_cast<double>(p->max_steps - 1);
+  } else if (p->temperature > 0.0) {
+    t = p->temperature;
+  }
   *inv_t = static_cast<float>(1.0 / t);
   *inv_t_log2e = static_cast<float>(static_cast<double>(*inv_t) * 1.4426950408889634);
 }
 
-dg::EbArgs eb_args(const dg_eb_params* p, int B, int C, int V, int step, const dg_eb_state* st,
-                   const dg_step_out* out, const uint16_t* logits, const EbWs& w) {
+dg::EbArgs eb_args(const dg_sched_params* p, int B, int C, int V, int step,
+                   const dg_eb_state* st, const dg_step_out* out, const uint16_t* logits,
+                   const EbWs& w) {
   dg::EbArgs a;
   memset(&a, 0, sizeof(a));
   a.B = B;
@@ -219,16 +276,64 @@ dg::EbArgs eb_args(const dg_eb_params* p, int B, int C, int V, int step, const d
   a.cand_score = w.cand_score;
   a.cand_idx = w.cand_idx;
   a.n_cand_chunks = w.n_cand;
+  a.row = w.row;
+  a.cand = w.cand;
+  a.kind = p->kind == DG_SCHED_BLOCK_REFINEMENT ? dg::SCHED_BLOCK_REFINEMENT
+           : p->kind == DG_SCHED_DISCRETE_DDIM  ? dg::SCHED_DDIM
+                                                : dg::SCHED_EB;
+  a.greedy = (p->kind != DG_SCHED_ENTROPY_BOUND && !(p->temperature > 0.0)) ? 1 : 0;
+  if (p->kind == DG_SCHED_BLOCK_REFINEMENT) {
+    a.threshold = p->threshold;
+    a.editing = p->editing_threshold >= 0.0 ? 1 : 0;
+    a.edit_threshold = p->editing_threshold;
+    const long long S = p->max_steps, s = step, c = C;
+    a.quota = static_cast<int>((s + 1) * c / S - s * c / S);
+  }
+  if (p->kind == DG_SCHED_DISCRETE_DDIM) {
+    // P predictor steps from t = 1 (pure noise) to t = 0, alpha(t) = 1 - t, then the corrector
+    // sweeps at the last noisy level t = 1 / P, then the final deterministic step
+    const int S = p->max_steps, P = S - p->corrector_steps;
+    a.corrector_k = p->corrector_k;
+    if (step == S - 1) {
+      a.phase = dg::DDIM_FINAL;
+    } else if (step < P - 1) {
+      const double t = 1.0 - static_cast<double>(step) / P;
+      const double tn = 1.0 - static_cast<double>(step + 1) / P;
+      a.phase = dg::DDIM_PREDICT;
+      a.alpha_t = 1.0 - t;
+      a.alpha_next = 1.0 - tn;
+      a.a_step = a.alpha_t / a.alpha_next;
+    } else {
+      a.phase = dg::DDIM_CORRECT;
+      a.alpha_t = 1.0 - 1.0 / P;
+    }
+  }
   return a;
 }
 
-// stats partials are ready: merge, commit, candidates
+// stats partials are ready: merge, then the scheduler's decisions and draws
 dg_status run_sampler_tail(const dg::EbArgs& a, hipStream_t s) {
   DG_LAUNCH(PC_STATS_MERGE, s, dg::launch_stats_merge(a, s));
-  DG_LAUNCH(PC_EB_COMMIT, s, dg::launch_eb_commit(a, s));
-  DG_LAUNCH(PC_CANDIDATES, s, dg::launch_candidates(a, s));
-  DG_LAUNCH(PC_CAND_APPLY, s, dg::launch_cand_apply(a, s));
-  return DG_OK;
+  switch (a.kind) {
+    case dg::SCHED_BLOCK_REFINEMENT:
+      DG_LAUNCH(PC_EB_COMMIT, s, dg::launch_sched_prepare(a, s));
+      if (!a.greedy) {
+        DG_LAUNCH(PC_CANDIDATES, s, dg::launch_candidates(a, s));
+        DG_LAUNCH(PC_CAND_APPLY, s, dg::launch_cand_apply(a, s));
+      }
+      DG_LAUNCH(PC_EB_COMMIT, s, dg::launch_br_commit(a, s));
+      return DG_OK;
+    case dg::SCHED_DDIM:
+      DG_LAUNCH(PC_EB_COMMIT, s, dg::launch_sched_prepare(a, s));
+      DG_LAUNCH(PC_CANDIDATES, s, dg::launch_ddim_candidates(a, s));
+      DG_LAUNCH(PC_CAND_APPLY, s, dg::launch_cand_apply(a, s));
+      return DG_OK;
+    default:
+      DG_LAUNCH(PC_EB_COMMIT, s, dg::launch_eb_commit(a, s));
+      DG_LAUNCH(PC_CANDIDATES, s, dg::launch_candidates(a, s));
+      DG_LAUNCH(PC_CAND_APPLY, s, dg::launch_cand_apply(a, s));
+      return DG_OK;
+  }
 }
 
 }  // namespace
@@ -313,11 +418,11 @@ dg_status dg_canvas_init(const dg_eb_params* p, dg_eb_state* st, int32_t B, int3
   return DG_OK;
 }
 
-dg_status dg_eb_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, int32_t step,
-                       const dg_eb_params* p, dg_eb_state* st, dg_step_out* out, void* ws,
-                       size_t ws_bytes, void* stream) {
+dg_status dg_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, int32_t step,
+                    const dg_sched_params* p, dg_eb_state* st, dg_step_out* out, void* ws,
+                    size_t ws_bytes, void* stream) {
   if (!logits || !ws) return fail(DG_ERR_NULL, "logits or workspace is NULL");
-  dg_status s = check_params(p, step);
+  dg_status s = check_sched(p, step);
   if (s != DG_OK) return s;
   if ((s = check_state(st)) != DG_OK) return s;
   if ((s = check_out(out, false)) != DG_OK) return s;
@@ -332,6 +437,14 @@ dg_status dg_eb_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, 
   dg::EbArgs a = eb_args(p, B, C, V, step, st, out, logits, w);
   DG_LAUNCH(PC_STATS, hs, dg::launch_logit_stats(a, hs));
   return run_sampler_tail(a, hs);
+}
+
+dg_status dg_eb_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, int32_t step,
+                       const dg_eb_params* p, dg_eb_state* st, dg_step_out* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!p) return fail(DG_ERR_NULL, "params is NULL");
+  const dg_sched_params q = sched_from_eb(p);
+  return dg_sample(logits, B, C, V, step, &q, st, out, ws, ws_bytes, stream);
 }
 
 dg_status dg_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* stream) {
@@ -523,12 +636,21 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
 // (causal among the C tokens, writes their K/V into the cache); next_gain: the norm of the
 // following consumer applied to the new h (NULL: none), with its e4m3 codes when next_q8.
 // Optional router traces.
+// A compacted decoder step runs only the canvases idx[0 .. n) of the batch (n == 0: all of them,
+// in order); their cache rows, state rows and output rows are reached through idx.
+struct BatchMap {
+  int n = 0;
+  int idx[64];
+};
+
 dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causal, DecWs& w,
                     const uint16_t* next_gain, bool next_q8, bool skip_ffn, float* trace_logits,
-                    int32_t* trace_idx, float* trace_gates, hipStream_t s) {
+                    int32_t* trace_idx, float* trace_gates, hipStream_t s,
+                    const BatchMap* bm = nullptr) {
   const dg_dims& d = m->dims;
   const dg_layer_w& lw = m->layers[l];
-  const int B = kv->batch, T = B * C;
+  const bool mapped = bm && bm->n > 0;
+  const int B = mapped ? bm->n : kv->batch, T = B * C;
   const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const size_t kvl = kv_layer_elems(d, kv);
   uint16_t* kc = static_cast<uint16_t*>(kv->k) + kvl * l;
@@ -549,15 +671,20 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causa
   at.B = B; at.C = C; at.Hq = d.n_q_heads; at.Hkv = d.n_kv_heads; at.dh = d.head_dim;
   at.window = layer_global(d, l) ? 0 : d.window;
   at.causal = causal ? 1 : 0;
-  int max_keys = 0;
   for (int b = 0; b < B; ++b) {
-    at.len[b] = kv->len[b];
+    at.kvb[b] = mapped ? bm->idx[b] : b;
+    at.len[b] = kv->len[at.kvb[b]];
+  }
+  // the key split is chosen for the whole batch, so a compacted step splits (and rounds) every
+  // canvas's attention exactly as the full step does
+  int max_keys = 0;
+  for (int b = 0; b < kv->batch; ++b) {
     const int lo = at.window > 0 ? std::max(0, kv->len[b] - at.window + 1) : 0;
     max_keys = std::max(max_keys, kv->len[b] - lo + C);
   }
   at.scale_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.head_dim)));
-  at.n_split = std::min(w.max_split,
-                        dg::attention_pick_split(B, C, d.n_q_heads, d.n_kv_heads, max_keys));
+  at.n_split = std::min(w.max_split, dg::attention_pick_split(kv->batch, C, d.n_q_heads,
+                                                              d.n_kv_heads, max_keys));
   at.o_part = w.o_part; at.ml_part = w.ml_part; at.out = w.attn;
   DG_LAUNCH(PC_ATTENTION, s, dg::launch_attention(at, s));
   if (causal) {
@@ -662,10 +789,14 @@ dg_status check_model(const dg_model* m) {
 // LM head over the final norm in ws.u (fp8: its e4m3 codes in ws.u8) with the tempered
 // statistics epilogue; logits [T][V] bf16
 dg_status run_lm_head(const dg_model* m, int T, DecWs& w, uint16_t* logits, float inv_t_log2e,
-                      hipStream_t s) {
+                      hipStream_t s, const BatchMap* bm = nullptr) {
   const dg_dims& d = m->dims;
   dg::WGemmArgs g;
   memset(&g, 0, sizeof(g));
+  if (bm && bm->n > 0) {
+    g.omap_C = d.canvas_len;
+    for (int b = 0; b < bm->n; ++b) g.omap[b] = bm->idx[b];
+  }
   g.hot = w.hot;
   g.X = w.u; g.ldx = d.d_model; g.W = static_cast<const uint16_t*>(m->w_lm);
   g.K = g.K_sh = d.d_model; g.N = g.N_sh = d.vocab; g.ntok = T; g.out = logits;
@@ -699,25 +830,18 @@ size_t dg_append_workspace_bytes(const dg_model* m, int32_t batch, int32_t max_t
   return c.off + 256;
 }
 
-dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, const dg_eb_params* p,
-                          dg_eb_state* st, dg_step_out* out, void* ws, size_t ws_bytes,
-                          void* stream) {
-  dg_status s = check_model(m);
-  if (s != DG_OK) return s;
-  if ((s = check_kv(m, kv, false)) != DG_OK) return s;
-  if ((s = check_params(p, step)) != DG_OK) return s;
-  if ((s = check_state(st)) != DG_OK) return s;
-  if ((s = check_out(out, true)) != DG_OK) return s;
-  if (!ws) return fail(DG_ERR_NULL, "workspace is NULL");
-  const size_t need = dg_workspace_bytes(m, kv->batch);
-  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+// The decoder step over the canvases of `bm` (all of them when bm is NULL), checked by the caller
+static dg_status decoder_step_rows(const dg_model* m, const dg_kv* kv, int32_t step,
+                                   const dg_sched_params* p, dg_eb_state* st, dg_step_out* out,
+                                   void* ws, hipStream_t hs, const BatchMap* bm) {
   const dg_dims& d = m->dims;
-  const int B = kv->batch, C = d.canvas_len, T = B * C;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool mapped = bm && bm->n > 0;
+  const int B = mapped ? bm->n : kv->batch, C = d.canvas_len, T = B * C;
   Carver c(ws);
-  DecWs w = carve_dec(c, d, B, C);
-
-  DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(st->canvas, m->embed, w.h, T, d.d_model, d.vocab, hs));
+  DecWs w = carve_dec(c, d, kv->batch, C);
+  dg_status s;
+  DG_LAUNCH(PC_EMBED, hs, dg::launch_embed(st->canvas, m->embed, w.h, T, d.d_model, d.vocab, hs,
+                                           C, mapped ? bm->n : 0, mapped ? bm->idx : nullptr));
   DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[0].attn_norm),
                                                w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
   for (int l = 0; l < d.n_layers; ++l) {
@@ -725,13 +849,68 @@ dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, cons
     const uint16_t* next = !last ? static_cast<const uint16_t*>(m->layers[l + 1].attn_norm)
                                  : m->final_norm;
     if ((s = run_layer(m, kv, l, C, false, w, next, last && m->fp8(), false, nullptr, nullptr,
-                       nullptr, hs)) != DG_OK)
+                       nullptr, hs, bm)) != DG_OK)
       return s;
   }
   // LM head with the tempered statistics, then the sampler
   dg::EbArgs a = eb_args(p, B, C, d.vocab, step, st, out, out->logits, w.eb);
-  if ((s = run_lm_head(m, T, w, out->logits, a.inv_t_log2e, hs)) != DG_OK) return s;
+  if (mapped) {
+    a.mapped = 1;
+    for (int b = 0; b < bm->n; ++b) a.bmap[b] = bm->idx[b];
+  }
+  if ((s = run_lm_head(m, T, w, out->logits, a.inv_t_log2e, hs, bm)) != DG_OK) return s;
   return run_sampler_tail(a, hs);
+}
+
+dg_status dg_decoder_step_sched(const dg_model* m, const dg_kv* kv, int32_t step,
+                                const dg_sched_params* p, dg_eb_state* st, dg_step_out* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, false)) != DG_OK) return s;
+  if ((s = check_sched(p, step)) != DG_OK) return s;
+  if ((s = check_state(st)) != DG_OK) return s;
+  if ((s = check_out(out, true)) != DG_OK) return s;
+  if (!ws) return fail(DG_ERR_NULL, "workspace is NULL");
+  const size_t need = dg_workspace_bytes(m, kv->batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return decoder_step_rows(m, kv, step, p, st, out, ws, static_cast<hipStream_t>(stream),
+                           nullptr);
+}
+
+dg_status dg_decoder_step_live(const dg_model* m, const dg_kv* kv, int32_t step,
+                               const dg_sched_params* p, dg_eb_state* st, dg_step_out* out,
+                               int32_t n_live, const int32_t* live, void* ws, size_t ws_bytes,
+                               void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if ((s = check_kv(m, kv, false)) != DG_OK) return s;
+  if ((s = check_sched(p, step)) != DG_OK) return s;
+  if ((s = check_state(st)) != DG_OK) return s;
+  if ((s = check_out(out, true)) != DG_OK) return s;
+  if (!ws || !live) return fail(DG_ERR_NULL, "workspace or live is NULL");
+  if (n_live < 1 || n_live > kv->batch)
+    return fail(DG_ERR_SHAPE, "n_live = %d outside [1, %d]", n_live, kv->batch);
+  BatchMap bm;
+  bm.n = n_live;
+  bool seen[64] = {};
+  for (int j = 0; j < n_live; ++j) {
+    if (live[j] < 0 || live[j] >= kv->batch || seen[live[j]])
+      return fail(DG_ERR_SHAPE, "live[%d] = %d is out of range or repeated", j, live[j]);
+    seen[live[j]] = true;
+    bm.idx[j] = live[j];
+  }
+  const size_t need = dg_workspace_bytes(m, kv->batch);
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return decoder_step_rows(m, kv, step, p, st, out, ws, static_cast<hipStream_t>(stream), &bm);
+}
+
+dg_status dg_decoder_step(const dg_model* m, const dg_kv* kv, int32_t step, const dg_eb_params* p,
+                          dg_eb_state* st, dg_step_out* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!p) return fail(DG_ERR_NULL, "params is NULL");
+  const dg_sched_params q = sched_from_eb(p);
+  return dg_decoder_step_sched(m, kv, step, &q, st, out, ws, ws_bytes, stream);
 }
 
 // The encoder pass over C new tokens per canvas (checked by the caller): causal among them,
@@ -793,17 +972,17 @@ size_t dg_generate_workspace_bytes(const dg_model* m, int32_t batch) {
   return base ? base + 512 : 0;   // + the canvas ids of the current canvas, 256-byte aligned
 }
 
-dg_status dg_generate(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
-                      const dg_eb_params* p, dg_eb_state* state, dg_step_out* out,
-                      int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
-                      size_t ws_bytes, void* stream) {
+dg_status dg_generate_sched(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
+                            const dg_sched_params* p, dg_eb_state* state, dg_step_out* out,
+                            int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
+                            size_t ws_bytes, void* stream) {
   dg_status s = check_model(m);
   if (s != DG_OK) return s;
   if (!gen || !tokens || !canvases || !ws) return fail(DG_ERR_NULL, "gen, tokens, canvases or ws is NULL");
   const int C = m->dims.canvas_len;
   if (gen->gen_length < 1) return fail(DG_ERR_SHAPE, "gen_length must be >= 1");
   const long long total_ll = (static_cast<long long>(gen->gen_length) + C - 1) / C;
-  if ((s = check_params(p, 0)) != DG_OK) return s;
+  if ((s = check_sched(p, 0)) != DG_OK) return s;
   if ((s = check_state(state)) != DG_OK) return s;
   if ((s = check_out(out, true)) != DG_OK) return s;
   if ((s = check_kv(m, kv, false)) != DG_OK) return s;
@@ -823,24 +1002,33 @@ dg_status dg_generate(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
   dg_eb_state st = *state;
   st.canvas_id = ids;
   std::vector<uint32_t> hid(B);
-  std::vector<int32_t> hdone(B), hcanvas(static_cast<size_t>(B) * C);
+  std::vector<int32_t> hdone(B), hcanvas(static_cast<size_t>(B) * C), live;
   std::vector<char> has_eos(B, 0);
   *canvases = 0;
   for (int c = 0; c < total; ++c) {
     // canvas c of sequence b draws its noise with canvas id c * B + b
     for (int b = 0; b < B; ++b) hid[b] = static_cast<uint32_t>(c * B + b);
     DG_HIP(hipMemcpyAsync(ids, hid.data(), sizeof(uint32_t) * B, hipMemcpyHostToDevice, hs));
-    if ((s = dg_canvas_init(p, &st, B, C, m->dims.vocab, stream)) != DG_OK) return s;
+    DG_LAUNCH(PC_EB_COMMIT, hs, dg::launch_canvas_init(p->seed, st, B, C, m->dims.vocab, hs));
+    live.resize(B);
+    for (int b = 0; b < B; ++b) live[b] = b;
     int n = 0;
     for (int step = 0; step < p->max_steps; ++step) {
-      if ((s = dg_decoder_step(m, kv, step, p, &st, out, ws, step_ws, stream)) != DG_OK) return s;
+      // with compaction, a step runs only the samples not yet frozen
+      if (gen->compact_frozen && static_cast<int>(live.size()) < B)
+        s = dg_decoder_step_live(m, kv, step, p, &st, out, static_cast<int32_t>(live.size()),
+                                 live.data(), ws, step_ws, stream);
+      else
+        s = dg_decoder_step_sched(m, kv, step, p, &st, out, ws, step_ws, stream);
+      if (s != DG_OK) return s;
       ++n;
       // adaptive stop: the canvas's loop ends once every sample is frozen
       DG_HIP(hipMemcpyAsync(hdone.data(), st.done, sizeof(int32_t) * B, hipMemcpyDeviceToHost, hs));
       DG_HIP(hipStreamSynchronize(hs));
-      bool all = true;
-      for (int b = 0; b < B; ++b) all = all && hdone[b] != 0;
-      if (all) break;
+      live.clear();
+      for (int b = 0; b < B; ++b)
+        if (!hdone[b]) live.push_back(b);
+      if (live.empty()) break;
     }
     DG_HIP(hipMemcpy2DAsync(tokens + static_cast<size_t>(c) * C, sizeof(int32_t) * total * C,
                             st.canvas, sizeof(int32_t) * C, sizeof(int32_t) * C, B,
@@ -863,6 +1051,40 @@ dg_status dg_generate(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
   return DG_OK;
 }
 
+dg_status dg_generate(const dg_model* m, dg_kv* kv, const dg_gen_params* gen,
+                      const dg_eb_params* p, dg_eb_state* state, dg_step_out* out,
+                      int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!p) return fail(DG_ERR_NULL, "params is NULL");
+  const dg_sched_params q = sched_from_eb(p);
+  return dg_generate_sched(m, kv, gen, &q, state, out, tokens, canvases, steps, ws, ws_bytes,
+                           stream);
+}
+
+// One layer over C tokens per canvas (the canvas, or an encoder call's token count) on the
+// caller's residual stream; ws is carved for C tokens per canvas
+static dg_status layer_forward_n(const dg_model* m, const dg_kv* kv, int layer, bool causal,
+                                 int C, float* h, float* router_logits, int32_t* topk_idx,
+                                 float* gates, void* ws, size_t ws_bytes, hipStream_t hs) {
+  const dg_dims& d = m->dims;
+  Carver sz(nullptr);
+  carve_dec(sz, d, kv->batch, C);
+  if (ws_bytes < sz.off + 256)
+    return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, sz.off + 256);
+  const int T = kv->batch * C;
+  Carver c(ws);
+  DecWs w = carve_dec(c, d, kv->batch, C);
+  dg_status s;
+  DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].attn_norm),
+                                               w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
+  if ((s = run_layer(m, kv, layer, C, causal, w, nullptr, false, false, router_logits, topk_idx,
+                     gates, hs)) != DG_OK)
+    return s;
+  DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
+  return DG_OK;
+}
+
 dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, int32_t causal,
                            float* h, float* router_logits, int32_t* topk_idx, float* gates,
                            void* ws, size_t ws_bytes, void* stream) {
@@ -873,20 +1095,28 @@ dg_status dg_layer_forward(const dg_model* m, const dg_kv* kv, int32_t layer, in
   if (layer < 0 || layer >= m->dims.n_layers) return fail(DG_ERR_SHAPE, "layer out of range");
   const size_t need = dg_workspace_bytes(m, kv->batch);
   if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  const dg_dims& d = m->dims;
-  const int T = kv->batch * d.canvas_len;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  Carver c(ws);
-  DecWs w = carve_dec(c, d, kv->batch, d.canvas_len);
-  DG_HIP(hipMemcpyAsync(w.h, h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
-  DG_LAUNCH(PC_RMSNORM, hs, dg::launch_rmsnorm(w.h, static_cast<const uint16_t*>(m->layers[layer].attn_norm),
-                                               w.u, T, d.d_model, d.norm_eps, nullptr, nullptr, hs));
-  if ((s = run_layer(m, kv, layer, d.canvas_len, causal != 0, w, nullptr, false, false,
-                     router_logits, topk_idx,
-                     gates, hs)) != DG_OK)
-    return s;
-  DG_HIP(hipMemcpyAsync(h, w.h, sizeof(float) * T * d.d_model, hipMemcpyDeviceToDevice, hs));
-  return DG_OK;
+  return layer_forward_n(m, kv, layer, causal != 0, m->dims.canvas_len, h, router_logits,
+                         topk_idx, gates, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_layer_forward_tokens(const dg_model* m, const dg_kv* kv, int32_t layer,
+                                  int32_t n_tokens, float* h, float* router_logits,
+                                  int32_t* topk_idx, float* gates, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  dg_status s = check_model(m);
+  if (s != DG_OK) return s;
+  if (!h || !ws) return fail(DG_ERR_NULL, "h or workspace is NULL");
+  if (layer < 0 || layer >= m->dims.n_layers) return fail(DG_ERR_SHAPE, "layer out of range");
+  if (n_tokens < 1 || n_tokens > DG_MAX_APPEND_TOKENS)
+    return fail(DG_ERR_SHAPE, "n_tokens = %d outside [1, %d]", n_tokens, DG_MAX_APPEND_TOKENS);
+  if (m->dims.window > 0 && n_tokens > m->dims.window)
+    return fail(DG_ERR_SHAPE, "n_tokens = %d exceeds the sliding window %d", n_tokens,
+                m->dims.window);
+  if ((s = check_kv(m, kv, true, n_tokens)) != DG_OK) return s;
+  if (static_cast<long long>(kv->batch) * n_tokens > 65536)
+    return fail(DG_ERR_SHAPE, "batch * n_tokens exceeds 65,536");
+  return layer_forward_n(m, kv, layer, true, n_tokens, h, router_logits, topk_idx, gates, ws,
+                         ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_ffn_forward(const dg_model* m, int32_t layer, int32_t batch, float* h,
@@ -934,7 +1164,8 @@ dg_status dg_lm_head_forward(const dg_model* m, int32_t batch, const float* h, i
                                                w.u8, w.u8s, hs));
   dg_eb_state none;
   memset(&none, 0, sizeof(none));
-  dg::EbArgs a = eb_args(p, batch, d.canvas_len, d.vocab, step, &none, out, out->logits, w.eb);
+  const dg_sched_params q = sched_from_eb(p);
+  dg::EbArgs a = eb_args(&q, batch, d.canvas_len, d.vocab, step, &none, out, out->logits, w.eb);
   if ((s = run_lm_head(m, T, w, out->logits, a.inv_t_log2e, hs)) != DG_OK) return s;
   DG_LAUNCH(PC_STATS_MERGE, hs, dg::launch_stats_merge(a, hs));
   return DG_OK;

@@ -201,13 +201,17 @@ struct WGemmArgs {
   // grouped products: the shared expert's tiles (the last sh_tiles of the tile list; 0 = none)
   // are ordered token tile fastest, so its weights are read into one L2 per row block
   int sh_tiles;
+  // LM head of a compacted step: token row r is written to output row
+  // omap[r / omap_C] * omap_C + r % omap_C (omap_C = 0: row r)
+  int omap_C;
+  int omap[64];
 };
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 
 // launchers; each returns the hip error of the launch
-hipError_t launch_gemm_dense_bf16(const WGemmArgs& a, hipStream_t s);     // out bf16 [rows][N]
-hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);      // fp32 split partials
+// router projection: fp32 k-split partial planes [ksplit][ntok][N], any N
+hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s);       // logits + stats
 int gemm_lmhead_rows_per_block();
 // expert products over fragment-major ("packed") weights, in tiles of tile_rows gathered rows:
@@ -239,6 +243,7 @@ struct AttnArgs {
   int cap;
   int B, C, Hq, Hkv, dh;
   int len[64];            // visible cache length per canvas (host copy)
+  int kvb[64];            // cache batch index of each canvas of the call
   int window;             // 0 = global
   int causal;             // encoder: canvas key j visible to query i iff j <= i
   float scale_log2e;      // log2(e) / sqrt(dh)
@@ -251,8 +256,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys);
 
 // per-token kernels
+// h[t] = E[token t]; with n_map > 0 (compacted step) the token of row t is
+// tokens[map[t / C] * C + t % C]
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, int ntok, int d,
-                        int vocab, hipStream_t s);
+                        int vocab, hipStream_t s, int C = 0, int n_map = 0,
+                        const int* map = nullptr);
 // norms: u = bf16(RMSNorm(h) * gain); with q8 != NULL also the e4m3 codes of the fp32 normed
 // row and its scale (q8s)
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* u, int ntok, int d,
@@ -276,9 +284,12 @@ hipError_t launch_mfma_loop(int iters, float* out, hipStream_t s);
 int mfma_loop_blocks();
 
 // sampler kernels
+enum SchedKind { SCHED_EB = 0, SCHED_BLOCK_REFINEMENT = 1, SCHED_DDIM = 2 };
+enum DdimPhase { DDIM_PREDICT = 0, DDIM_CORRECT = 1, DDIM_FINAL = 2 };
+
 struct EbArgs {
   int B, C, V, step, max_steps;
-  float inv_t;            // fp32(1 / T_s)
+  float inv_t;            // fp32 multiplier of the logits: 1 / T_s (EB), 1 / T or 1 (greedy)
   float inv_t_log2e;      // fp32(inv_t * log2 e)
   double bound;
   double stop_entropy;
@@ -293,6 +304,23 @@ struct EbArgs {
   double* cand_score;     // [B*C][n_cand_chunks]
   int32_t* cand_idx;
   int n_cand_chunks;
+  // the other schedulers
+  int kind;               // SchedKind
+  SoftStats* row;         // [B*C] merged statistics of each row (m, argmax, R, A)
+  int32_t* cand;          // [B*C] block refinement: each row's candidate token
+  int greedy;             // temperature 0: the candidate is the argmax
+  double threshold;       // block refinement: commit above this confidence
+  double edit_threshold;  // block refinement: re-edit above this confidence (editing != 0)
+  int editing;
+  int quota;              // block refinement: this step's even share of the canvas
+  int phase;              // DDIM: DdimPhase of this call step
+  double a_step;          // DDIM predictor: alpha(t) / alpha(t_next)
+  double alpha_t;         // DDIM: alpha at the current level
+  double alpha_next;      // DDIM predictor: alpha at the next level
+  int corrector_k;        // DDIM corrector: positions resampled per sweep
+  // compacted step: compact canvas b is canvas bmap[b] of the state, outputs and logits
+  int mapped;
+  int bmap[64];
 };
 hipError_t launch_logit_stats(const EbArgs& a, hipStream_t s);   // partials from logits
 int logit_stats_chunks(int V);
@@ -302,5 +330,10 @@ hipError_t launch_candidates(const EbArgs& a, hipStream_t s);    // Gumbel-max p
 hipError_t launch_cand_apply(const EbArgs& a, hipStream_t s);    // write candidates
 int cand_chunks(int V);
 hipError_t launch_canvas_init(uint64_t seed, dg_eb_state st, int B, int C, int V, hipStream_t s);
+// block refinement and DDIM: stop / finalise and the rows needing a draw; the DDIM draw; the
+// block-refinement commit (threshold + quota, editing, renoise)
+hipError_t launch_sched_prepare(const EbArgs& a, hipStream_t s);
+hipError_t launch_ddim_candidates(const EbArgs& a, hipStream_t s);
+hipError_t launch_br_commit(const EbArgs& a, hipStream_t s);
 
 }  // namespace dg

@@ -103,7 +103,15 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   const int c_lo = a.window > 0 ? max(0, len - a.window + 1) : 0;
   const int nc = len - c_lo;           // cache keys in the union of the visible ranges
   const int nk = nc + a.C;             // + canvas keys
-  const int ntiles = (nk + KT - 1) / KT;
+  int ntiles = (nk + KT - 1) / KT;
+  if (a.causal) {
+    // the block's last canvas position: canvas keys past it are masked for every query of the
+    // block, so their tiles are not visited (the rows of a block are consecutive positions of
+    // one query head unless the block straddles two heads)
+    const int r0 = qblk * QB, r1 = min(R, r0 + QB) - 1;
+    const int qmax = (r0 / a.C == r1 / a.C) ? r1 % a.C : a.C - 1;
+    ntiles = min(ntiles, (nc + qmax + 1 + KT - 1) / KT);
+  }
   const int per = (ntiles + a.n_split - 1) / a.n_split;
   const int t_beg = split * per;
   const int t_end = min(ntiles, t_beg + per);
@@ -144,8 +152,8 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     l_run[q] = 0.f;
   }
 
-  const uint16_t* kcache = a.kc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
-  const uint16_t* vcache = a.vc + (static_cast<long long>(b) * a.Hkv + g) * a.cap * DH;
+  const uint16_t* kcache = a.kc + (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap * DH;
+  const uint16_t* vcache = a.vc + (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap * DH;
   const uint16_t* kcanvas = a.qkv + static_cast<long long>(b) * a.C * ldqkv + (a.Hq + g) * DH;
   const uint16_t* vcanvas = kcanvas + a.Hkv * DH;
 

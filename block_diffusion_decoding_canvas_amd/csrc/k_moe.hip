@@ -401,7 +401,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     for (int tb = 0; tb < NTB; ++tb) {
       const int t = tb * 16 + r16;
       const bool ok = t < nrows && wave_live;
-      uint16_t* o = static_cast<uint16_t*>(a.out) + static_cast<long long>(row0 + t) * a.ldo;
+      const int orow = row0 + min(t, nrows - 1);   // rows past the tile are never stored
+      const long long orow_out =
+          a.omap_C > 0 ? static_cast<long long>(a.omap[orow / a.omap_C]) * a.omap_C + orow % a.omap_C
+                       : orow;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow_out * a.ldo;
       float y[4 * RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {

@@ -32,6 +32,14 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float (&z)[8]) {
   }
 }
 
+// Batch map of a compacted step: compact canvas b of the call is canvas map_b(b) of the state,
+// outputs and logits; the workspace arrays (partials, flags, candidates) stay compact.
+__device__ __forceinline__ int map_b(const EbArgs& a, int b) { return a.mapped ? a.bmap[b] : b; }
+__device__ __forceinline__ size_t map_row(const EbArgs& a, int row) {
+  return a.mapped ? static_cast<size_t>(a.bmap[row / a.C]) * a.C + row % a.C
+                  : static_cast<size_t>(row);
+}
+
 __device__ __forceinline__ SoftStats stats_empty() { return SoftStats{-INFINITY, 0x7fffffff, 0.f, 0.f}; }
 
 __device__ __forceinline__ SoftStats stats_merge_nan(SoftStats x, SoftStats y) {
@@ -156,8 +164,10 @@ __global__ __launch_bounds__(256) void k_stats_merge(EbArgs a) {
   if (lane == 0) {
     float h = log1pf(s.r) - 0.69314718055994531f * s.a / (1.0f + s.r);
     h = (h < 0.f) ? 0.f : h;  // keeps NaN
-    a.out.entropy[row] = h;
-    a.out.argmax[row] = s.idx;
+    const size_t rr = map_row(a, row);
+    a.out.entropy[rr] = h;
+    a.out.argmax[rr] = s.idx;
+    if (a.row) a.row[row] = s;
   }
 }
 
@@ -171,34 +181,36 @@ __global__ __launch_bounds__(1024) void k_eb_commit(EbArgs a) {
   const int i = threadIdx.x;
   const bool live = i < a.C;
   const size_t at = static_cast<size_t>(b) * a.C + i;
-  const int32_t* done_p = a.st.done + b;
+  const int rb = map_b(a, b);
+  const size_t ra = static_cast<size_t>(rb) * a.C + i;
+  const int32_t* done_p = a.st.done + rb;
   if (*done_p) {  // a frozen canvas never changes
     if (live) {
-      a.out.commit_now[at] = 0;
+      a.out.commit_now[ra] = 0;
       a.need_cand[at] = 0;
     }
     return;
   }
-  const float h = live ? a.out.entropy[at] : 0.f;
-  const int am = live ? a.out.argmax[at] : 0;
-  const bool committed = live ? (a.st.committed[at] != 0) : true;
-  const int prev = live ? a.st.prev_argmax[at] : 0;
+  const float h = live ? a.out.entropy[ra] : 0.f;
+  const int am = live ? a.out.argmax[ra] : 0;
+  const bool committed = live ? (a.st.committed[ra] != 0) : true;
+  const int prev = live ? a.st.prev_argmax[ra] : 0;
 
   const int bad = __syncthreads_or(live && !(fabsf(h) <= FLT_MAX));
   if (bad) {  // non-finite logits: sticky status, the canvas is frozen unchanged
     if (live) {
-      a.out.commit_now[at] = 0;
+      a.out.commit_now[ra] = 0;
       a.need_cand[at] = 0;
     }
     if (i == 0) {
       if (a.st.dev_status) atomicExch(a.st.dev_status, static_cast<int>(DG_ERR_NONFINITE));
-      a.st.done[b] = 1;
+      a.st.done[rb] = 1;
     }
     return;
   }
   const int all_same = __syncthreads_and(!live || am == prev);
-  const int stable = (a.step >= 1 && all_same) ? a.st.stable_count[b] + 1 : 0;
-  if (live) a.st.prev_argmax[at] = am;
+  const int stable = (a.step >= 1 && all_same) ? a.st.stable_count[rb] + 1 : 0;
+  if (live) a.st.prev_argmax[ra] = am;
 
   // mean entropy: fp64 sum in a fixed tree order
   dsum[i] = live ? static_cast<double>(h) : 0.0;
@@ -210,20 +222,20 @@ __global__ __launch_bounds__(1024) void k_eb_commit(EbArgs a) {
   const double mean_h = dsum[0] / a.C;
   const int any_unc = __syncthreads_or(live && !committed);
   const bool stop = a.stop_entropy >= 0.0 && stable >= a.stability && mean_h < a.stop_entropy;
-  if (i == 0) a.st.stable_count[b] = stable;
+  if (i == 0) a.st.stable_count[rb] = stable;
 
   if (stop || a.step == a.max_steps - 1 || !any_unc) {  // finalise: remaining take the argmax
     if (live) {
       a.need_cand[at] = 0;
       if (!committed) {
-        a.st.canvas[at] = am;
-        a.st.committed[at] = 1;
-        a.out.commit_now[at] = 1;
+        a.st.canvas[ra] = am;
+        a.st.committed[ra] = 1;
+        a.out.commit_now[ra] = 1;
       } else {
-        a.out.commit_now[at] = 0;
+        a.out.commit_now[ra] = 0;
       }
     }
-    if (i == 0) a.st.done[b] = 1;
+    if (i == 0) a.st.done[rb] = 1;
     return;
   }
 
@@ -271,21 +283,21 @@ __global__ __launch_bounds__(1024) void k_eb_commit(EbArgs a) {
     if (!committed) {
       if (chosen) {
         a.need_cand[at] = 1;
-        a.out.commit_now[at] = 1;
-        a.st.committed[at] = 1;
+        a.out.commit_now[ra] = 1;
+        a.st.committed[ra] = 1;
       } else {  // full renoise: a fresh uniform token
         a.need_cand[at] = 0;
-        a.out.commit_now[at] = 0;
-        a.st.canvas[at] = uniform_token(a.seed, a.st.canvas_id[b], static_cast<uint32_t>(a.step),
+        a.out.commit_now[ra] = 0;
+        a.st.canvas[ra] = uniform_token(a.seed, a.st.canvas_id[rb], static_cast<uint32_t>(a.step),
                                         static_cast<uint32_t>(i), static_cast<uint32_t>(a.V));
       }
     } else {
       a.need_cand[at] = 0;
-      a.out.commit_now[at] = 0;
+      a.out.commit_now[ra] = 0;
     }
   }
   const int all_committed = __syncthreads_and(!live || committed || chosen);
-  if (i == 0 && all_committed) a.st.done[b] = 1;
+  if (i == 0 && all_committed) a.st.done[rb] = 1;
 }
 
 // Gumbel-max over one vocabulary chunk of one row: score_v = z_v * (1/T) + g_v in fp64,
@@ -296,9 +308,9 @@ __global__ __launch_bounds__(kCandThreads) void k_candidates(EbArgs a) {
   if (!a.need_cand[row]) return;
   const int chunk = blockIdx.y;
   const int b = row / a.C, pos = row % a.C;
-  const uint32_t cid = a.st.canvas_id[b];
+  const uint32_t cid = a.st.canvas_id[map_b(a, b)];
   const uint32_t k0 = static_cast<uint32_t>(a.seed), k1 = static_cast<uint32_t>(a.seed >> 32);
-  const uint16_t* z = a.logits + static_cast<size_t>(row) * a.V;
+  const uint16_t* z = a.logits + map_row(a, row) * a.V;
   const double inv_t = static_cast<double>(a.inv_t);
   const int v0 = chunk * kCandChunk;
   const int v1 = min(a.V, v0 + kCandChunk);
@@ -376,7 +388,290 @@ __global__ __launch_bounds__(256) void k_cand_apply(EbArgs a) {
       best_v = ov;
     }
   }
-  if (lane == 0) a.st.canvas[row] = best_v;
+  if (lane == 0) {
+    if (a.kind == SCHED_BLOCK_REFINEMENT)
+      a.cand[row] = best_v;       // the commit kernel decides whether it is taken
+    else
+      a.st.canvas[map_row(a, row)] = best_v;  // entropy bound: committed rows; DDIM: new token
+  }
+}
+
+// ---- block refinement and DDIM -----------------------------------------------------------------
+// (diffusers DiffusionGemmaPipeline docs, "Schedulers" and "Predictor-corrector sampling")
+
+// ascending bitonic sort of 1024 keys in LDS by a workgroup of 1024 threads
+__device__ __forceinline__ void sort1024(uint64_t* keys) {
+  const int i = threadIdx.x;
+  __syncthreads();
+  for (int k = 2; k <= 1024; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = i ^ j;
+      if (p > i) {
+        const uint64_t x = keys[i], y = keys[p];
+        const bool up = (i & k) == 0;
+        if ((x > y) == up) {
+          keys[i] = y;
+          keys[p] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// p(v) of a row under softmax(z * inv_t) from its merged statistics (log2 units): one fp32 exp2
+__device__ __forceinline__ float row_prob(float zv, float c, const SoftStats& st) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(zv, c, -st.m)) / (1.0f + st.r);
+}
+
+// One workgroup of 1024 threads per canvas: stability, the adaptive stop and finalisation (the
+// pipeline's rule, as for the entropy bound), then which rows draw a token this step.
+//   block refinement: every uncommitted row (and, with editing, every committed row) draws a
+//     candidate; with temperature 0 the candidate is the argmax and nothing is drawn;
+//   DDIM predictor: every row draws from its posterior; corrector: the corrector_k rows with the
+//     lowest p(current token) (lower position first on ties); final step: finalise.
+__global__ __launch_bounds__(1024) void k_sched_prepare(EbArgs a) {
+  __shared__ uint64_t keys[1024];
+  __shared__ double dsum[1024];
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool live = i < a.C;
+  const size_t at = static_cast<size_t>(b) * a.C + i;
+  const int rb = map_b(a, b);
+  const size_t ra = static_cast<size_t>(rb) * a.C + i;
+  if (a.st.done[rb]) {  // a frozen canvas never changes
+    if (live) {
+      a.out.commit_now[ra] = 0;
+      a.need_cand[at] = 0;
+    }
+    return;
+  }
+  const float h = live ? a.out.entropy[ra] : 0.f;
+  const int am = live ? a.out.argmax[ra] : 0;
+  const bool committed = live ? (a.st.committed[ra] != 0) : true;
+  const int prev = live ? a.st.prev_argmax[ra] : 0;
+  const int bad = __syncthreads_or(live && !(fabsf(h) <= FLT_MAX));
+  if (bad) {  // non-finite logits: sticky status, the canvas is frozen unchanged
+    if (live) {
+      a.out.commit_now[ra] = 0;
+      a.need_cand[at] = 0;
+    }
+    if (i == 0) {
+      if (a.st.dev_status) atomicExch(a.st.dev_status, static_cast<int>(DG_ERR_NONFINITE));
+      a.st.done[rb] = 1;
+    }
+    return;
+  }
+  const int all_same = __syncthreads_and(!live || am == prev);
+  const int stable = (a.step >= 1 && all_same) ? a.st.stable_count[rb] + 1 : 0;
+  if (live) a.st.prev_argmax[ra] = am;
+  dsum[i] = live ? static_cast<double>(h) : 0.0;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (i < o) dsum[i] += dsum[i + o];
+    __syncthreads();
+  }
+  const double mean_h = dsum[0] / a.C;
+  const int any_unc = __syncthreads_or(live && !committed);
+  const bool stop = a.stop_entropy >= 0.0 && stable >= a.stability && mean_h < a.stop_entropy;
+  if (i == 0) a.st.stable_count[rb] = stable;
+  const bool ddim = a.kind == SCHED_DDIM;
+  if (stop || (ddim && a.phase == DDIM_FINAL) || (!ddim && !any_unc && !a.editing)) {
+    if (live) {  // finalise: every uncommitted position takes its argmax
+      a.need_cand[at] = 0;
+      a.out.commit_now[ra] = committed ? 0 : 1;
+      if (!committed) {
+        a.st.canvas[ra] = am;
+        a.st.committed[ra] = 1;
+      }
+    }
+    if (i == 0) a.st.done[rb] = 1;
+    return;
+  }
+  if (!ddim) {  // block refinement
+    if (live) {
+      a.need_cand[at] = (!a.greedy && (!committed || a.editing)) ? 1 : 0;
+      if (a.greedy) a.cand[at] = am;
+    }
+    return;
+  }
+  if (live) a.out.commit_now[ra] = 0;
+  if (a.phase == DDIM_PREDICT) {
+    if (live) a.need_cand[at] = 1;
+    return;
+  }
+  // corrector sweep: ascending (p(current token), position); probabilities are >= 0, so their
+  // binary32 patterns order like their values
+  float conf = 0.f;
+  if (live) {
+    const int x = a.st.canvas[ra];
+    const SoftStats st = a.row[at];
+    if (a.greedy) {
+      conf = (x == st.idx) ? 1.f : 0.f;
+    } else {
+      const float zx = bf2f(a.logits[ra * static_cast<size_t>(a.V) + min(max(x, 0), a.V - 1)]);
+      conf = row_prob(zx, a.inv_t_log2e, st);
+    }
+  }
+  keys[i] = live ? ((static_cast<uint64_t>(__float_as_uint(conf)) << 32) | static_cast<uint32_t>(i))
+                 : ~0ull;
+  sort1024(keys);
+  if (live) a.need_cand[at] = 0;
+  __syncthreads();
+  if (i < a.corrector_k && i < a.C) a.need_cand[static_cast<size_t>(b) * a.C +
+                                                static_cast<uint32_t>(keys[i])] = 1;
+}
+
+// DDIM draw for one vocabulary chunk of one row (predictor posterior or corrector conditional).
+// Both are affine in the model's probabilities: w_v = A + B p_v for v != j and A_j + B_j p_j at
+// the current token j (coefficients below, fp64).  The draw is argmax_v (ln w_v + g_v) with the
+// entropy-bound sampler's Gumbel noise g_v = -ln(-ln u_v); it is taken as argmax_v w_v / E_v with
+// E_v = -ln u_v, the same order (exp of the score), one logarithm per entry.
+__global__ __launch_bounds__(kCandThreads) void k_ddim_candidates(EbArgs a) {
+  const int row = blockIdx.x;
+  if (!a.need_cand[row]) return;
+  const int chunk = blockIdx.y;
+  const int b = row / a.C, pos = row % a.C;
+  const uint32_t cid = a.st.canvas_id[map_b(a, b)];
+  const uint32_t k0 = static_cast<uint32_t>(a.seed), k1 = static_cast<uint32_t>(a.seed >> 32);
+  const uint16_t* z = a.logits + map_row(a, row) * a.V;
+  const SoftStats st = a.row[row];
+  const float c = a.inv_t_log2e;
+  const int j = min(max(a.st.canvas[map_row(a, row)], 0), a.V - 1);
+  const double pj = a.greedy ? (j == st.idx ? 1.0 : 0.0)
+                             : static_cast<double>(row_prob(bf2f(z[j]), c, st));
+  const double V = static_cast<double>(a.V);
+  const double al = a.alpha_t;
+  const double d_same = al + (1.0 - al) / V, d_diff = (1.0 - al) / V;
+  const double s0 = pj / d_same + (1.0 - pj) / d_diff;
+  double A, B, Aj, Bj;
+  if (a.phase == DDIM_PREDICT) {
+    // sum_m p(m) q(x_next = v | x_t = j, x_0 = m): the one-step transition back to j times the
+    // forward transition to the next level applied to r(m) = p(m) / q(j | m)
+    const double bn = a.alpha_next, as = a.a_step;
+    const double step_same = as + (1.0 - as) / V, step_diff = (1.0 - as) / V;
+    A = step_diff * (1.0 - bn) * s0 / V;
+    B = step_diff * bn / d_diff;
+    Aj = step_same * (1.0 - bn) * s0 / V;
+    Bj = step_same * bn / d_same;
+  } else {
+    // alpha p_loo(v) + (1 - alpha) / V with p_loo(v) = p(v) / (q(j | v) s0)
+    A = Aj = (1.0 - al) / V;
+    B = al / (d_diff * s0);
+    Bj = al / (d_same * s0);
+  }
+  const int v0 = chunk * kCandChunk;
+  const int v1 = min(a.V, v0 + kCandChunk);
+  double best = -1.0;
+  int best_v = 0x7fffffff;
+  for (int v = v0 + threadIdx.x * 8; v < v1; v += kCandThreads * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(z + v);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const Philox4 r0 = philox10(static_cast<uint32_t>(v >> 2), pos, a.step, (cid << 1) | 1u, k0, k1);
+    const Philox4 r1 = philox10(static_cast<uint32_t>((v >> 2) + 1), pos, a.step, (cid << 1) | 1u,
+                                k0, k1);
+    const uint32_t x[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int vk = v + k;
+      const float zf = __uint_as_float(k & 1 ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+      const double p = a.greedy ? (vk == st.idx ? 1.0 : 0.0)
+                                : static_cast<double>(row_prob(zf, c, st));
+      const double wv = (vk == j) ? Aj + Bj * p : A + B * p;
+      const double u = (static_cast<double>(x[k]) + 0.5) * 0x1p-32;
+      const double sc = wv / (-log(u));
+      if (sc > best) {
+        best = sc;
+        best_v = vk;
+      }
+    }
+  }
+  __shared__ double rs[kCandThreads / 64];
+  __shared__ int ri[kCandThreads / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ob = __shfl_xor(best, o, 64);
+    const int ov = __shfl_xor(best_v, o, 64);
+    if (ob > best || (ob == best && ov < best_v)) {
+      best = ob;
+      best_v = ov;
+    }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    rs[wv] = best;
+    ri[wv] = best_v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kCandThreads / 64; ++k) {
+      if (rs[k] > best || (rs[k] == best && ri[k] < best_v)) {
+        best = rs[k];
+        best_v = ri[k];
+      }
+    }
+    // the score kept by the merge is ln(w / E), the Gumbel score itself
+    a.cand_score[static_cast<size_t>(row) * a.n_cand_chunks + chunk] = log(best);
+    a.cand_idx[static_cast<size_t>(row) * a.n_cand_chunks + chunk] = best_v;
+  }
+}
+
+// Block refinement commit, one workgroup of 1024 threads per canvas (canvases finalised or
+// frozen by k_sched_prepare are done and skipped): confidence = p(candidate); the uncommitted
+// positions in descending (confidence, then ascending position) order; the step commits every
+// one above the threshold plus `quota` more (every remaining one at the last step); with editing,
+// committed positions take a different candidate whose confidence is above edit_threshold; the
+// other uncommitted positions are renoised.
+__global__ __launch_bounds__(1024) void k_br_commit(EbArgs a) {
+  __shared__ uint64_t keys[1024];
+  __shared__ uint8_t sel[1024];
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int rb = map_b(a, b);
+  if (a.st.done[rb]) return;
+  const bool live = i < a.C;
+  const size_t at = static_cast<size_t>(b) * a.C + i;
+  const size_t ra = static_cast<size_t>(rb) * a.C + i;
+  const bool committed = live ? (a.st.committed[ra] != 0) : true;
+  const bool needs = live && (!committed || a.editing);
+  int cand = 0;
+  float conf = 0.f;
+  if (needs) {
+    cand = min(max(a.cand[at], 0), a.V - 1);
+    const float zc = bf2f(a.logits[ra * static_cast<size_t>(a.V) + cand]);
+    conf = row_prob(zc, a.inv_t_log2e, a.row[at]);
+  }
+  const bool unc = live && !committed;
+  keys[i] = unc ? ((static_cast<uint64_t>(~__float_as_uint(conf)) << 32) | static_cast<uint32_t>(i))
+                : ~0ull;
+  sel[i] = 0;
+  const bool above = unc && static_cast<double>(conf) > a.threshold;
+  const int n_above = __syncthreads_count(above);
+  const int n_unc = __syncthreads_count(unc);
+  sort1024(keys);
+  const bool last = a.step == a.max_steps - 1;
+  const int n = last ? n_unc : min(n_unc, n_above + a.quota);
+  if (i < n) sel[static_cast<uint32_t>(keys[i])] = 1;
+  __syncthreads();
+  if (live) {
+    if (unc) {
+      if (sel[i]) {
+        a.st.canvas[ra] = cand;
+        a.st.committed[ra] = 1;
+        a.out.commit_now[ra] = 1;
+      } else {  // full renoise: a fresh uniform token
+        a.out.commit_now[ra] = 0;
+        a.st.canvas[ra] = uniform_token(a.seed, a.st.canvas_id[rb], static_cast<uint32_t>(a.step),
+                                        static_cast<uint32_t>(i), static_cast<uint32_t>(a.V));
+      }
+    } else {
+      a.out.commit_now[ra] = 0;
+      if (a.editing && cand != a.st.canvas[ra] && static_cast<double>(conf) > a.edit_threshold)
+        a.st.canvas[ra] = cand;
+    }
+  }
+  const int all_committed = __syncthreads_and(!live || committed || sel[i]);
+  if (i == 0 && (last || (all_committed && !a.editing))) a.st.done[rb] = 1;
 }
 
 __global__ __launch_bounds__(256) void k_canvas_init(uint64_t seed, dg_eb_state st, int B, int C,
@@ -424,6 +719,22 @@ hipError_t launch_candidates(const EbArgs& a, hipStream_t s) {
 
 hipError_t launch_cand_apply(const EbArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_cand_apply, dim3((a.B * a.C + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_prepare(const EbArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_sched_prepare, dim3(a.B), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ddim_candidates(const EbArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.C, a.n_cand_chunks);
+  hipLaunchKernelGGL(k_ddim_candidates, grid, dim3(kCandThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_br_commit(const EbArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_br_commit, dim3(a.B), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,14 +16,20 @@
 namespace dg {
 namespace {
 
+struct TokMap {
+  int C, n;        // n > 0: row t reads tokens[idx[t / C] * C + t % C]
+  int idx[64];
+};
+
 // token ids outside [0, vocab) are clamped into range (no out-of-bounds gather)
 __global__ __launch_bounds__(256) void k_embed(const int32_t* tokens, const uint16_t* embed,
-                                               float* h, int ntok, int d, int vocab) {
+                                               float* h, int ntok, int d, int vocab, TokMap mp) {
   const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   const int per = d / 8;
   if (idx >= static_cast<long long>(ntok) * per) return;
   const int t = static_cast<int>(idx / per), c = static_cast<int>(idx % per) * 8;
-  const int tok = min(max(tokens[t], 0), vocab - 1);
+  const long long src = mp.n > 0 ? static_cast<long long>(mp.idx[t / mp.C]) * mp.C + t % mp.C : t;
+  const int tok = min(max(tokens[src], 0), vocab - 1);
   const uint4 v = *reinterpret_cast<const uint4*>(embed + static_cast<long long>(tok) * d + c);
   float4* o = reinterpret_cast<float4*>(h + static_cast<long long>(t) * d + c);
   o[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
@@ -468,10 +474,14 @@ __global__ __launch_bounds__(256) void k_kv_write(KvWriteArgs a) {
 }  // namespace
 
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, float* h, int ntok, int d,
-                        int vocab, hipStream_t s) {
+                        int vocab, hipStream_t s, int C, int n_map, const int* map) {
+  TokMap mp;
+  mp.C = C;
+  mp.n = n_map > 0 ? n_map : 0;
+  for (int i = 0; i < mp.n && i < 64; ++i) mp.idx[i] = map[i];
   const long long n = static_cast<long long>(ntok) * (d / 8);
   hipLaunchKernelGGL(k_embed, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                     tokens, embed, h, ntok, d, vocab);
+                     tokens, embed, h, ntok, d, vocab, mp);
   return hipGetLastError();
 }
 

@@ -98,6 +98,48 @@ def eb_sample(logits, step, params, state, out, ws=None, stream=None):
     return ws
 
 
+SCHED_KINDS = {"entropy_bound": _lib.DG_SCHED_ENTROPY_BOUND,
+               "block_refinement": _lib.DG_SCHED_BLOCK_REFINEMENT,
+               "discrete_ddim": _lib.DG_SCHED_DISCRETE_DDIM}
+
+
+def sched_params(kind, max_steps=48, seed=2, temperature=0.0, threshold=0.9,
+                 editing_threshold=-1.0, top_k=0, corrector_steps=0, corrector_k=0,
+                 stop_entropy=0.005, stability=1, t_max=0.8, t_min=0.4, entropy_bound=0.1):
+    """Parameters of one of the pipeline's schedulers (dg_sched_params)."""
+    return _lib.dg_sched_params(SCHED_KINDS[kind], max_steps, t_max, t_min, entropy_bound,
+                                temperature, threshold, editing_threshold, top_k,
+                                corrector_steps, corrector_k, stop_entropy, stability, seed)
+
+
+def sched_params_from_dict(p, seed):
+    """dg_sched_params from an oracle-style parameter dict (oracle.schedulers.default_params)."""
+    keys = ("max_steps", "temperature", "threshold", "editing_threshold", "corrector_steps",
+            "corrector_k", "stop_entropy", "stability")
+    return sched_params(p["kind"], seed=seed, **{k: p[k] for k in keys if k in p})
+
+
+def sample(logits, step, params, state, out, ws=None, stream=None):
+    """Any scheduler's step on given bf16 logits [B, C, V] (dg_sample)."""
+    lib = _lib.load()
+    b, c, v = logits.shape
+    need = lib.dg_eb_workspace_bytes(b, c, v)
+    if ws is None:
+        ws = workspace(need, logits.device)
+    st, o = state.struct(), out.struct()
+    check(lib.dg_sample(ptr(logits), b, c, v, step, ctypes.byref(params), ctypes.byref(st),
+                        ctypes.byref(o), ptr(ws), ws.numel(), stream_ptr(stream)), "dg_sample")
+    return ws
+
+
+def decoder_step_sched(model, kv, step, params, state, out, ws, stream=None):
+    lib = _lib.load()
+    kvs, st, o = kv.struct(), state.struct(), out.struct()
+    check(lib.dg_decoder_step_sched(model.handle, ctypes.byref(kvs), step, ctypes.byref(params),
+                                    ctypes.byref(st), ctypes.byref(o), ptr(ws), ws.numel(),
+                                    stream_ptr(stream)), "dg_decoder_step_sched")
+
+
 def dims_struct(d):
     wd = _lib.DG_FP8_E4M3 if d.get("wdtype", "bf16") in ("e4m3", "fp8") else _lib.DG_BF16
     return _lib.dg_dims(d["n_layers"], d["d"], d["hq"], d["hkv"], d["dh"], d["E"], d["top_k"],
@@ -224,9 +266,10 @@ def kv_append_tokens(model, kv, tokens, ws, stream=None):
 
 
 def generate(model, kv, params, state, out, gen_length, eos_token_id=-1, eos_early_stop=True,
-             ws=None, stream=None):
+             ws=None, stream=None, compact_frozen=False):
     """The canvas loop on a cache that holds the prompt: returns (tokens [B, n*C] int32 device,
-    canvases generated, decoder steps per canvas)."""
+    canvases generated, decoder steps per canvas).  params: dg_eb_params (the entropy bound) or
+    dg_sched_params (any scheduler, dg_generate_sched)."""
     lib = _lib.load()
     c = state.C
     n = -(-int(gen_length) // c)
@@ -234,16 +277,28 @@ def generate(model, kv, params, state, out, gen_length, eos_token_id=-1, eos_ear
     if ws is None:
         ws = workspace(lib.dg_generate_workspace_bytes(model.handle, state.B),
                        state.canvas.device)
-    gen = _lib.dg_gen_params(int(gen_length), int(eos_token_id), 1 if eos_early_stop else 0)
+    gen = _lib.dg_gen_params(int(gen_length), int(eos_token_id), 1 if eos_early_stop else 0,
+                             1 if compact_frozen else 0)
     kvs, st, o = kv.struct(), state.struct(), out.struct()
     done = ctypes.c_int32(0)
     steps = (ctypes.c_int32 * n)()
-    check(lib.dg_generate(model.handle, ctypes.byref(kvs), ctypes.byref(gen), ctypes.byref(params),
-                          ctypes.byref(st), ctypes.byref(o), ptr(tokens), ctypes.byref(done),
-                          ctypes.cast(steps, ctypes.c_void_p), ptr(ws), ws.numel(),
-                          stream_ptr(stream)), "dg_generate")
+    fn = lib.dg_generate_sched if isinstance(params, _lib.dg_sched_params) else lib.dg_generate
+    check(fn(model.handle, ctypes.byref(kvs), ctypes.byref(gen), ctypes.byref(params),
+             ctypes.byref(st), ctypes.byref(o), ptr(tokens), ctypes.byref(done),
+             ctypes.cast(steps, ctypes.c_void_p), ptr(ws), ws.numel(), stream_ptr(stream)),
+          "dg_generate")
     k = done.value
     return tokens[:, :k * c], k, [steps[i] for i in range(k)]
+
+
+def decoder_step_live(model, kv, step, params, state, out, live, ws, stream=None):
+    """dg_decoder_step_live: the step over the canvases in `live` only (dg_sched_params)."""
+    lib = _lib.load()
+    kvs, st, o = kv.struct(), state.struct(), out.struct()
+    arr = (ctypes.c_int32 * len(live))(*[int(x) for x in live])
+    check(lib.dg_decoder_step_live(model.handle, ctypes.byref(kvs), step, ctypes.byref(params),
+                                   ctypes.byref(st), ctypes.byref(o), len(live), arr, ptr(ws),
+                                   ws.numel(), stream_ptr(stream)), "dg_decoder_step_live")
 
 
 def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=None,
@@ -253,6 +308,17 @@ def layer_forward(model, kv, layer, causal, h, ws, router_logits=None, topk_idx=
     check(lib.dg_layer_forward(model.handle, ctypes.byref(kvs), layer, int(causal), ptr(h),
                                ptr(router_logits), ptr(topk_idx), ptr(gates), ptr(ws),
                                ws.numel(), stream_ptr(stream)), "dg_layer_forward")
+
+
+def layer_forward_tokens(model, kv, layer, h, ws, router_logits=None, topk_idx=None, gates=None,
+                         stream=None):
+    """One encoder layer over n = h.shape[0] / B new tokens per canvas (dg_layer_forward_tokens)."""
+    lib = _lib.load()
+    kvs = kv.struct()
+    n = h.shape[0] // kv.batch
+    check(lib.dg_layer_forward_tokens(model.handle, ctypes.byref(kvs), layer, n, ptr(h),
+                                      ptr(router_logits), ptr(topk_idx), ptr(gates), ptr(ws),
+                                      ws.numel(), stream_ptr(stream)), "dg_layer_forward_tokens")
 
 
 def pack_weight(src, dst, stream=None):

@@ -140,6 +140,48 @@ typedef struct {
   int32_t* dev_status;    /* [1] sticky; set to DG_ERR_NONFINITE on a non-finite logit row    */
 } dg_eb_state;
 
+/* The pipeline's interchangeable samplers (diffusers DiffusionGemmaPipeline docs, "Schedulers"
+ * and "Predictor-corrector sampling"): only the commit / renoise rule changes; the statistics,
+ * the adaptive stop (stop_entropy, stability) and the Philox streams are shared.
+ *   DG_SCHED_ENTROPY_BOUND: the model card's sampler (t_max, t_min, entropy_bound), as
+ *     dg_eb_params describes it.
+ *   DG_SCHED_BLOCK_REFINEMENT: at the fixed `temperature` (0 = greedy: the candidate is the
+ *     argmax; else a Gumbel-max draw from softmax(logits / temperature)), confidence =
+ *     p(candidate) under softmax(logits / T_eff) (T_eff = temperature, or 1 when greedy); each
+ *     step commits, among the uncommitted positions, every one with confidence > threshold plus
+ *     the step's even share of the canvas, floor((s+1) C / S) - floor(s C / S), of the most
+ *     confident others (lower position first on ties); the last step commits everything left;
+ *     editing_threshold >= 0 lets a committed position take a different candidate whose
+ *     confidence is above it; the rest is renoised uniformly.  top_k (a vocabulary filter of the
+ *     draw) must be 0: the filter is not built.
+ *   DG_SCHED_DISCRETE_DDIM: uniform (D3PM) corruption with alpha(t) = 1 - t; with
+ *     P = max_steps - corrector_steps, call step s < P - 1 draws every position from the exact
+ *     posterior sum_m p(m) q(x_{t_{s+1}} | x_{t_s}, x_0 = m), t_s = 1 - s / P; call steps
+ *     P - 1 .. max_steps - 2 are leave-one-out corrector sweeps at t = 1 / P, each redrawing the
+ *     corrector_k positions of lowest p(current token) from alpha p_loo + (1 - alpha) / V with
+ *     p_loo proportional to p(m) / q(current | m); the last call step sets every position to its
+ *     argmax and commits the canvas.  Nothing is committed before that.
+ * Every scheduler finalises a canvas (uncommitted positions take the argmax) when the adaptive
+ * stop holds: argmax unchanged over stability + 1 consecutive steps and mean entropy of
+ * softmax(logits / T) below stop_entropy (T = T_s for the entropy bound, T_eff otherwise). */
+enum { DG_SCHED_ENTROPY_BOUND = 0, DG_SCHED_BLOCK_REFINEMENT = 1, DG_SCHED_DISCRETE_DDIM = 2 };
+
+typedef struct {
+  int32_t kind;               /* DG_SCHED_*                                                    */
+  int32_t max_steps;          /* num_inference_steps (48)                                      */
+  double t_max, t_min;        /* entropy bound: 0.8 -> 0.4                                     */
+  double entropy_bound;       /* entropy bound: 0.1                                            */
+  double temperature;         /* block refinement, DDIM: >= 0, 0 = greedy                      */
+  double threshold;           /* block refinement: 0.9                                         */
+  double editing_threshold;   /* block refinement: < 0 disables editing                        */
+  int32_t top_k;              /* block refinement: 0                                           */
+  int32_t corrector_steps;    /* DDIM: 0 <= corrector_steps <= max_steps - 1                   */
+  int32_t corrector_k;        /* DDIM: positions per corrector sweep, >= 0                     */
+  double stop_entropy;        /* 0.005; negative disables the adaptive stop                    */
+  int32_t stability;          /* 1                                                             */
+  uint64_t seed;              /* Philox4x32-10 key                                             */
+} dg_sched_params;
+
 /* Per-step outputs (device, caller-owned). */
 typedef struct {
   float* entropy;         /* [B, C] entropy (nats) of softmax(logits / T_s)                   */
@@ -169,6 +211,29 @@ dg_status dg_decoder_step(const dg_model* model, const dg_kv* kv, int32_t step,
 dg_status dg_eb_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len, int32_t vocab,
                        int32_t step, const dg_eb_params* params, dg_eb_state* state,
                        dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
+
+/* dg_decoder_step and dg_eb_sample with any of the pipeline's schedulers (dg_sched_params).
+ * Same layouts, workspaces and errors; DG_ERR_STATE also for an unknown kind, a negative
+ * temperature or a corrector_steps outside [0, max_steps - 1], DG_ERR_UNSUPPORTED for
+ * top_k != 0.  The state carries the same fields across calls. */
+dg_status dg_decoder_step_sched(const dg_model* model, const dg_kv* kv, int32_t step,
+                                const dg_sched_params* params, dg_eb_state* state,
+                                dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
+/* Frozen-canvas compaction (diffusers docs, "Adaptive stopping": each sample of a batch freezes
+ * on its own).  dg_decoder_step_sched over only the canvases live[0 .. n_live) of the batch
+ * (host array of distinct indices in [0, kv->batch)): their cache rows, state rows and output
+ * rows are read and written in place; the other canvases' state and outputs are not touched, and
+ * the step does no work for them.  Every live canvas's results are bit-identical to the full
+ * step's (the attention key split is chosen for the whole batch).  Workspace as for the full
+ * step.  Errors: those of dg_decoder_step_sched; DG_ERR_SHAPE for n_live outside [1, batch] or
+ * a repeated or out-of-range index. */
+dg_status dg_decoder_step_live(const dg_model* model, const dg_kv* kv, int32_t step,
+                               const dg_sched_params* params, dg_eb_state* state,
+                               dg_step_out* out, int32_t n_live, const int32_t* live, void* ws,
+                               size_t ws_bytes, void* stream);
+dg_status dg_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len, int32_t vocab,
+                    int32_t step, const dg_sched_params* params, dg_eb_state* state,
+                    dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Encoder pass over finished canvases tokens [B, C] (causal inside the canvas, sees the cache);
  * every layer writes its keys/values at [len[b], len[b] + C).  On DG_OK the HOST array kv->len
@@ -208,6 +273,9 @@ typedef struct {
   int32_t eos_token_id;     /* < 0: no EOS check                                              */
   int32_t eos_early_stop;   /* nonzero: start no further canvas once every sequence has
                                produced eos_token_id (at any position of a finished canvas)   */
+  int32_t compact_frozen;   /* nonzero: once a sample of the batch is frozen (adaptive stop),
+                               the canvas's later steps run only the samples still live
+                               (dg_decoder_step_live): same tokens, less work               */
 } dg_gen_params;
 
 /* Workspace of dg_generate: dg_workspace_bytes(model, batch) + 512 (0 on invalid arguments). */
@@ -231,6 +299,13 @@ dg_status dg_generate(const dg_model* model, dg_kv* kv, const dg_gen_params* gen
                       int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* dg_generate with any of the pipeline's schedulers (dg_sched_params); dg_generate is this call
+ * with the entropy-bound scheduler. */
+dg_status dg_generate_sched(const dg_model* model, dg_kv* kv, const dg_gen_params* gen,
+                            const dg_sched_params* params, dg_eb_state* state, dg_step_out* out,
+                            int32_t* tokens, int32_t* canvases, int32_t* steps, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* dg_last_error(void);
 
@@ -242,6 +317,17 @@ const char* dg_last_error(void);
 dg_status dg_layer_forward(const dg_model* model, const dg_kv* kv, int32_t layer, int32_t causal,
                            float* h, float* router_logits, int32_t* topk_idx, float* gates,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* One encoder layer over n_tokens new tokens per canvas, exactly as dg_kv_append_tokens runs it
+ * (same kernels and launch shapes for the same n_tokens): h [B * n_tokens, d] fp32 is the layer's
+ * input residual stream, updated in place; the layer writes the new tokens' keys/values at
+ * [len[b], len[b] + n_tokens) of its cache slice (kv->len is not advanced).  Trace outputs as for
+ * dg_layer_forward.  ws: at least dg_append_workspace_bytes(model, B, n_tokens).  Errors as for
+ * dg_kv_append_tokens, plus DG_ERR_SHAPE for a layer out of range. */
+dg_status dg_layer_forward_tokens(const dg_model* model, const dg_kv* kv, int32_t layer,
+                                  int32_t n_tokens, float* h, float* router_logits,
+                                  int32_t* topk_idx, float* gates, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Packs a row-major bf16 matrix [rows][cols] (rows % 16 == 0, cols % 32 == 0; an [E][N][K]
  * expert tensor is passed as rows = E N) into the fragment-major layout the expert kernels

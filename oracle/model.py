@@ -115,8 +115,12 @@ def swiglu_ffn(u, w_gate_up, w_down, s_gate_up=None, s_down=None):
     return linear(silu(gu[..., :f]) * gu[..., f:], w_down, s_down)
 
 
-def route(u, w_router, top_k):
-    """Router: logits, top-k expert ids (descending logit, lowest id on ties) and gates."""
+def route(u, w_router, top_k, force_idx=None):
+    """Router: logits, top-k expert ids (descending logit, lowest id on ties) and gates.
+
+    force_idx [T, k]: use these expert ids instead of the top-k (gates are still the softmax
+    weights renormalised over the chosen experts).  The parity tests pass the GPU's choice here
+    for rows whose k-th and (k+1)-th logits are a near-tie, where either choice is correct."""
     r = u @ w_router.T                                                # [T, E]
     pi = softmax(r, axis=-1)
     ntok, n_exp = r.shape
@@ -124,14 +128,17 @@ def route(u, w_router, top_k):
     for t in range(ntok):
         order = sorted(range(n_exp), key=lambda e: (-r[t, e], e))
         idx[t] = order[:top_k]
+    if force_idx is not None:
+        idx = np.asarray(force_idx, dtype=np.int64).reshape(ntok, top_k).copy()
     sel = np.take_along_axis(pi, idx, axis=1)
     gates = sel / sel.sum(axis=1, keepdims=True)
     return r, idx, gates
 
 
-def moe(u, lw, top_k):
-    """Sparse MoE FFN: sum over the top-k experts of gate * FFN_e(u), plus the shared expert."""
-    r, idx, gates = route(u, lw["w_router"], top_k)
+def moe(u, lw, top_k, force_idx=None):
+    """Sparse MoE FFN: sum over the top-k experts of gate * FFN_e(u), plus the shared expert
+    (force_idx: see ``route``)."""
+    r, idx, gates = route(u, lw["w_router"], top_k, force_idx)
     ntok, d = u.shape
     n_exp = lw["w_router"].shape[0]
     y = np.zeros((ntok, top_k, d))
@@ -156,15 +163,37 @@ def split_qkv(qkv, dims):
     return q, k, v
 
 
+def kv_fp8(dims):
+    """Is the KV cache of this model stored in e4m3 (the fp8 KV configuration)?"""
+    return dims.get("kv_dtype", "bf16") in ("e4m3", "fp8")
+
+
+def quantize_dequantize_rows(x):
+    """x as its per-row e4m3 codes times the row scale (numerics.quantize_rows_e4m3 along the
+    last axis), as float64: the value an e4m3 row with an fp32 scale represents."""
+    q, s = quantize_rows_e4m3(x)
+    return q * s[..., None]
+
+
 def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
     """First half of a layer: h + O-projection of the joint attention over RMSNorm(h).
 
     h [B, C, d]; k_cache, v_cache [B, Hkv, cap, dh] (this layer); cache_len [B].
-    Returns (h after attention, k [B, C, Hkv, dh], v) -- k, v are the canvas keys/values."""
+    Returns (h after attention, k [B, C, Hkv, dh], v) -- k, v are the canvas keys/values.
+
+    fp8 KV configuration (reading; the pages only quote FP8 speed): the QKV product is taken in
+    its bf16 storage form, and every query, key and value row of dh values (one token, one head)
+    is replaced by its per-row e4m3 quantisation (codes times fp32 scale) before the attention;
+    the cache holds such rows.  The returned k, v are the quantised canvas rows."""
     eps = dims["eps"]
     bsz, clen, d = h.shape
     u = rms_norm(h, lw["attn_norm"], eps)
-    q, k, v = split_qkv(u @ lw["w_qkv"].T, dims)
+    qkv = u @ lw["w_qkv"].T
+    if kv_fp8(dims):
+        qkv = round_bf16(qkv)
+    q, k, v = split_qkv(qkv, dims)
+    if kv_fp8(dims):
+        q, k, v = (quantize_dequantize_rows(x) for x in (q, k, v))
     window = 0 if layer_is_global(layer, dims) else dims["window"]
     o = np.zeros_like(q)
     for b in range(bsz):
@@ -174,47 +203,52 @@ def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
     return h + o.reshape(bsz, clen, -1) @ lw["w_o"].T, k, v
 
 
-def ffn_block(h, lw, dims):
-    """Second half of a layer: h + MoE(RMSNorm(h)).  Returns (new h, routing info)."""
+def ffn_block(h, lw, dims, force_idx=None):
+    """Second half of a layer: h + MoE(RMSNorm(h)).  Returns (new h, routing info).
+    force_idx [B, C, k] or None (see ``route``)."""
     bsz, clen, d = h.shape
     u = rms_norm(h, lw["ffn_norm"], dims["eps"])
-    f, info = moe(u.reshape(bsz * clen, d), lw, dims["top_k"])
+    f, info = moe(u.reshape(bsz * clen, d), lw, dims["top_k"], force_idx)
     return h + f.reshape(bsz, clen, d), info
 
 
-def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
+def layer_forward(h, lw, dims, layer, k_cache, v_cache, cache_len, causal, force_idx=None):
     """One transformer layer over a batch of canvases.
 
     h [B, C, d] residual stream; k_cache, v_cache [B, Hkv, cap, dh] (this layer);
-    cache_len [B].  Returns (new h, k [B, C, Hkv, dh], v, routing info).
+    cache_len [B]; force_idx [B, C, k] or None (see ``route``).
+    Returns (new h, k [B, C, Hkv, dh], v, routing info).
     """
     h, k, v = attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal)
-    h, info = ffn_block(h, lw, dims)
+    h, info = ffn_block(h, lw, dims, force_idx)
     return h, k, v, info
 
 
-def decoder_forward(canvas, model, cache):
+def decoder_forward(canvas, model, cache, force_idx=None):
     """Decoder pass over canvases [B, C] -> logits [B, C, V] (bf16-rounded, as float64).
 
     cache: dict(k, v: lists over layers of [B, Hkv, cap, dh], len [B]).
+    force_idx: None, or a list over layers of [B, C, k] expert ids (see ``route``).
     Also returns the fp64 logits before rounding and per-layer routing info.
     """
     dims = model["dims"]
     h = model["embed"][np.asarray(canvas)]
     infos = []
     for layer, lw in enumerate(model["layers"]):
+        fi = None if force_idx is None else force_idx[layer]
         h, _, _, info = layer_forward(h, lw, dims, layer, cache["k"][layer], cache["v"][layer],
-                                      cache["len"], causal=False)
+                                      cache["len"], causal=False, force_idx=fi)
         infos.append(info)
     z = linear(rms_norm(h, model["final_norm"], dims["eps"]), model["w_lm"], model.get("s_lm"))
     return round_bf16(z), z, infos
 
 
-def encoder_append(tokens, model, cache, round_stored=True):
+def encoder_append(tokens, model, cache, round_stored=True, force_idx=None):
     """Encoder pass over finished canvases [B, C]: causal inside the canvas, sees the cache.
 
     Each layer stores its keys and values at [len, len + C), rounded to bf16 (the cache's storage
     type) unless ``round_stored`` is False; len += C.  The cache dict is updated in place.
+    force_idx: None, or a list over layers of [B, C, k] expert ids (see ``route``).
     """
     dims = model["dims"]
     tokens = np.asarray(tokens)
@@ -224,10 +258,13 @@ def encoder_append(tokens, model, cache, round_stored=True):
         kc, vc = cache["k"][layer], cache["v"][layer]
         if np.any(cache["len"] + clen > kc.shape[2]):
             raise ValueError("cache capacity exceeded")
-        h, k, v, _ = layer_forward(h, lw, dims, layer, kc, vc, cache["len"], causal=True)
+        fi = None if force_idx is None else force_idx[layer]
+        h, k, v, _ = layer_forward(h, lw, dims, layer, kc, vc, cache["len"], causal=True,
+                                   force_idx=fi)
         for b in range(bsz):
             n = int(cache["len"][b])
-            store = round_bf16 if round_stored else np.asarray
+            # the layer's k, v are already e4m3 rows in the fp8 KV configuration (exact)
+            store = round_bf16 if round_stored and not kv_fp8(dims) else np.asarray
             kc[b, :, n:n + clen] = store(k[b].transpose(1, 0, 2))
             vc[b, :, n:n + clen] = store(v[b].transpose(1, 0, 2))
     cache["len"] = cache["len"] + clen

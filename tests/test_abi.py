@@ -154,6 +154,26 @@ def test_eb_sample_validation_before_launch():
     assert call(params=bad) == 6
 
 
+def test_layer_forward_tokens_validate():
+    lib = _lib.load()
+    st, h = _create(_tiny_dims())
+    lens = (ctypes.c_int32 * 1)(60)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens)
+    fake = ctypes.c_void_p(0x1000)
+    ws = lib.dg_append_workspace_bytes(h, 1, 4)
+
+    def call(layer=0, n=4, w=ws):
+        return lib.dg_layer_forward_tokens(h, ctypes.byref(kv), layer, n, fake, None, None, None,
+                                           fake, w, None)
+
+    assert call(layer=2) == 2                    # layer out of range
+    assert call(n=0) == 2
+    assert call(n=5, w=1 << 40) == 4             # 60 + 5 > cap 64
+    assert call(w=ws - 1) == 5                   # workspace sized below 4 tokens
+    assert lens[0] == 60
+    lib.dg_model_destroy(h)
+
+
 def test_decoder_calls_validate_kv_and_step():
     lib = _lib.load()
     st, h = _create(_tiny_dims())

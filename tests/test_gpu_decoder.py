@@ -15,7 +15,8 @@ import torch
 from block_diffusion_decoding_canvas_amd import driver, synth
 from oracle import model as om
 from oracle import sampler as osamp
-from tests.parity_util import assert_close_rel, compare_eb_step, routing_certified
+from tests.parity_util import (GpuChain, assert_close_rel, check_forced_routing,
+                               compare_eb_step)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -72,11 +73,11 @@ def test_tiny_prefill_and_8_step_lockstep(hot):
         gs.load_host(st)
         driver.decoder_step(model, kv, s, p, gs, out, ws)
         torch.cuda.synchronize()
-        zr, z64, _ = om.decoder_forward(st["canvas"], m64, ref_cache)
+        chain = GpuChain(dims, model, kv, ws, st["canvas"], mnp["embed"])
+        zr, z64, infos = om.decoder_forward(st["canvas"], m64, ref_cache, force_idx=chain.idx)
+        chain.check(infos, dims["top_k"], f"s={s}")
         zg = out.logits.float().cpu().numpy()
-        cert = routing_certified(dims, mnp, model, kv, ws, ref_cache, st["canvas"])[-1]
-        assert cert.sum() >= cert.size // 4
-        assert_close_rel(zg[0, cert], zr[0, cert], what=f"logits s={s} (certified rows)")
+        assert_close_rel(zg, zr, what=f"logits s={s} (all rows)")
         err = np.abs(zg - z64).max(axis=-1)
         before = copy.deepcopy(st)
         ref = osamp.eb_step(zr, s, params, st, seed, ids)
@@ -149,18 +150,19 @@ def test_full_width_layer(causal):
                 orders += 1
     print(f"router: {sets}/{T} sets and {orders}/{T} orders certified")
     assert sets >= T // 2
-    # outputs: all tokens in relative L2; element-wise on tokens whose expert set is certified
-    # (a near-tie at the k-th expert legitimately swaps one expert's contribution)
+    # outputs: every token at the stated tolerance, the oracle taking the GPU's expert set where
+    # the router logits sit at a k-th/(k+1)-th near-tie (checked for validity)
     hout = hg.cpu().numpy()
-    h_ref = h_ref.reshape(T, -1)
-    assert np.linalg.norm(hout - h_ref) <= 2e-2 * np.linalg.norm(h_ref)
-    cert = np.array([np.sort(r_ref[t])[::-1][k - 1] - np.sort(r_ref[t])[::-1][k] >
-                     2 * rerr[t] + 1e-7 for t in range(T)])
-    assert_close_rel(hout[cert], h_ref[cert], what="layer output (certified routing)")
+    swaps = check_forced_routing(r_ref, rg, tig, k, "full-width layer")
+    h_f, _, _, _ = om.layer_forward(h.astype(np.float64), lw, dims, 0, np.stack(
+        [c64["k"][0][b] for b in range(1)]), np.stack([c64["v"][0][b] for b in range(1)]),
+        c64["len"], causal=bool(causal), force_idx=tig.reshape(1, T, k))
+    h_f = h_f.reshape(T, -1)
+    print(f"near-tie expert swaps: {swaps}/{T}")
+    assert_close_rel(hout, h_f, what="layer output (all tokens)")
     # the layer's increment on its own (the residual input passes through unchanged)
     h_in = h.reshape(T, -1).astype(np.float64)
-    assert_close_rel(hout[cert] - h_in[cert], h_ref[cert] - h_in[cert],
-                     what="layer increment (certified routing)")
+    assert_close_rel(hout - h_in, h_f - h_in, what="layer increment (all tokens)")
     if causal:
         kgpu = kv.k[0].float().cpu().numpy()[0, :, 2048:2048 + T]
         vgpu = kv.v[0].float().cpu().numpy()[0, :, 2048:2048 + T]

@@ -2,8 +2,9 @@
 
 Integer decisions (the e4m3 codes, decided in binary32 from identical inputs) are compared
 bit-exactly; the stage outputs (FFN residual increment, logits, entropies) within the stated
-tolerance, on rows whose expert set is certified by the router-logit margin; the end-to-end
-decoder run (a batch of 4 ragged caches, sliding-window and global layers) like the bf16 runs.
+tolerance on every row, the oracle taking the GPU's expert set wherever the two sides' router
+logits sit at a near-tie (checked for validity first); the end-to-end decoder run (a batch of 4
+ragged caches, sliding-window and global layers) like the bf16 runs.
 """
 import copy
 
@@ -15,45 +16,35 @@ from block_diffusion_decoding_canvas_amd import driver, synth
 from oracle import model as om
 from oracle import sampler as osamp
 from oracle.numerics import e4m3_code, quantize_rows_e4m3, round_bf16
-from tests.parity_util import (FP8_CHAIN_ARRAY_TOL, FP8_CHAIN_TOL, argmax_certified,
+from tests.parity_util import (FP8_CHAIN_ARRAY_TOL, FP8_CHAIN_TOL, GpuChain, argmax_certified,
                                assert_close_rel, assert_entropy_close, compare_eb_step,
-                               entropy_sensitivity, entropy_tolerance, routing_certified)
+                               entropy_sensitivity, entropy_tolerance, ffn_forced)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _ffn_stages_on_oracle_states(dims, m64, c64, model, ws, canvas):
+def _ffn_stages_on_oracle_states(dims, m64, c64, model, ws, canvas, force):
+    """Every FFN (the quantised half of a layer) from the oracle's own post-attention state, on
+    every row, with the oracle taking the GPU's expert sets at near-ties.  force: the GPU chain's
+    expert sets per layer (the oracle's states follow the same choices)."""
     B, C = np.asarray(canvas).shape
-    T, k = B * C, dims["top_k"]
     h = m64["embed"][np.asarray(canvas)]
     for layer, lw in enumerate(m64["layers"]):
         h_mid, _, _ = om.attention_block(h, lw, dims, layer, c64["k"][layer], c64["v"][layer],
                                          c64["len"], causal=False)
-        h_out, info = om.ffn_block(h_mid, lw, dims)
-        hg = torch.from_numpy(h_mid.reshape(T, -1).astype(np.float32)).to(DEV)
-        rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device=DEV)
-        driver.ffn_forward(model, layer, B, hg, ws, rl)
-        torch.cuda.synchronize()
-        r_ref = info["router_logits"]
-        rerr = np.abs(rl.cpu().numpy() - r_ref).max()
-        srt = -np.sort(-r_ref, axis=1)
-        cert = (srt[:, k - 1] - srt[:, k]) > 4 * rerr + 1e-7
-        assert cert.sum() >= T // 4
-        h_in = h_mid.reshape(T, -1).astype(np.float32).astype(np.float64)
-        inc = hg.cpu().numpy().astype(np.float64) - h_in
-        assert_close_rel(inc[cert], (h_out.reshape(T, -1) - h_mid.reshape(T, -1))[cert],
-                         what=f"fp8 FFN increment, layer {layer}")
-        h = h_out
+        inc_g, inc_r, _ = ffn_forced(model, lw, dims, layer, B, h_mid, ws, f"fp8 FFN {layer}")
+        assert_close_rel(inc_g, inc_r, what=f"fp8 FFN increment, layer {layer}")
+        h, _ = om.ffn_block(h_mid, lw, dims, force[layer])
 
 
-def _oracle_final_hidden(canvas, m64, c64):
-    """The oracle's residual stream after the last decoder layer, [B * C, d]."""
+def _oracle_final_hidden(canvas, m64, c64, force):
+    """The oracle's residual stream after the last decoder layer, [B * C, d] (forced sets)."""
     dims = m64["dims"]
     h = m64["embed"][np.asarray(canvas)]
     for layer, lw in enumerate(m64["layers"]):
         h, _, _, _ = om.layer_forward(h, lw, dims, layer, c64["k"][layer], c64["v"][layer],
-                                      c64["len"], causal=False)
+                                      c64["len"], causal=False, force_idx=force[layer])
     return h.reshape(-1, dims["d"])
 
 
@@ -113,23 +104,11 @@ def _ffn_case(dims, wdtype, B, seed):
     h = synth.hidden_states(T, dims["d"], seed=seed + 1).astype(np.float64)
     for layer in range(dims["n_layers"]):
         lw = ref_model["layers"][layer]
-        u = om.rms_norm(h, lw["ffn_norm"], dims["eps"])
-        f, info = om.moe(u, lw, dims["top_k"])
-        hg = torch.from_numpy(h.astype(np.float32)).to(DEV)
-        rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device=DEV)
-        driver.ffn_forward(model, layer, B, hg, ws, rl)
-        torch.cuda.synchronize()
-        r_ref = info["router_logits"]
-        rerr = np.abs(rl.cpu().numpy() - r_ref).max()
-        srt = -np.sort(-r_ref, axis=1)
-        k = dims["top_k"]
-        cert = (srt[:, k - 1] - srt[:, k]) > 4 * rerr + 1e-7
-        assert cert.sum() >= T // 4
-        delta = hg.cpu().numpy().astype(np.float64) - h.astype(np.float32).astype(np.float64)
-        err = np.linalg.norm(delta[cert] - f[cert], axis=1) / np.linalg.norm(f[cert], axis=1)
+        delta, f, swaps = ffn_forced(model, lw, dims, layer, B, h, ws, f"{wdtype} FFN {layer}")
+        err = np.linalg.norm(delta - f, axis=1) / np.linalg.norm(f, axis=1)
         print(f"{wdtype} layer {layer}: FFN increment worst row rel err {err.max():.2e}, "
-              f"certified {cert.sum()}/{T}")
-        assert_close_rel(delta[cert], f[cert], what=f"{wdtype} FFN layer {layer}")
+              f"near-tie expert swaps {swaps}/{T}")
+        assert_close_rel(delta, f, what=f"{wdtype} FFN layer {layer}")
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "e4m3"])
@@ -219,16 +198,14 @@ def test_fp8_decoder_steps_batched_windowed():
         gs.load_host(st)
         driver.decoder_step(model, kv, s, p, gs, out, ws)
         torch.cuda.synchronize()
-        zr, z64, _ = om.decoder_forward(st["canvas"], m64, c64)
+        chain = GpuChain(dims, model, kv, ws, st["canvas"], mnp["embed"])
+        zr, z64, infos = om.decoder_forward(st["canvas"], m64, c64, force_idx=chain.idx)
+        chain.check(infos, dims["top_k"], f"fp8 s={s}")
         zg = out.logits.float().cpu().numpy()
-        cert = routing_certified(dims, mnp, model, kv, ws, c64, st["canvas"],
-                                 ref_model=m64)[-1].reshape(B, dims["C"])
-        assert cert.sum() >= cert.size // 4
-        # every FFN (the quantised half of a layer) from the oracle's own post-attention state:
-        # the increments at the stated tolerance on rows with a certified expert set
-        _ffn_stages_on_oracle_states(dims, m64, c64, model, ws, st["canvas"])
+        # every FFN (the quantised half of a layer) from the oracle's own post-attention state
+        _ffn_stages_on_oracle_states(dims, m64, c64, model, ws, st["canvas"], chain.idx)
         # the LM head from the oracle's final hidden state: logits at the stated tolerance
-        h_fin = _oracle_final_hidden(st["canvas"], m64, c64)
+        h_fin = _oracle_final_hidden(st["canvas"], m64, c64, chain.idx)
         lm = driver.StepOut(B, dims["C"], dims["V"], DEV)
         driver.lm_head_forward(model, B, torch.from_numpy(h_fin.astype(np.float32)).to(DEV), s,
                                p, lm, ws)
@@ -237,9 +214,9 @@ def test_fp8_decoder_steps_batched_windowed():
         # end to end: e4m3 codes flip where upstream float differences cross a rounding
         # boundary; FP8_CHAIN_TOL is the bound for chained fp8 stages
         rel = np.linalg.norm(zg - zr, axis=-1) / np.linalg.norm(zr, axis=-1)
-        print(f"fp8 step {s}: certified {cert.sum()}/{cert.size}, end-to-end logits worst row "
-              f"rel err {rel[cert].max():.2e}, median {np.median(rel[cert]):.2e}")
-        assert_close_rel(zg[cert], zr[cert], rel=FP8_CHAIN_TOL, what=f"fp8 logits s={s}")
+        print(f"fp8 step {s}: end-to-end logits worst row rel err {rel.max():.2e}, "
+              f"median {np.median(rel):.2e}")
+        assert_close_rel(zg, zr, rel=FP8_CHAIN_TOL, what=f"fp8 logits s={s}")
         assert np.linalg.norm(zg - zr) <= FP8_CHAIN_ARRAY_TOL * np.linalg.norm(zr)
         # the sampler on these logits: decisions robust to the observed logit error must match
         # exactly, the rest must be valid (the rule's choice on the GPU's own entropies); the

@@ -3,8 +3,10 @@
 Two full-width layers (d 2816, 16/8 heads of 256, 128 experts top-8 + shared, inner 704) with the
 262,144-entry vocabulary, a 256-token canvas and an 8,192-token N(0,1) cache: the same kernels,
 tile shapes, splits and grids the 30-layer benchmark launches, compared on every output the
-oracle computes (all logits, entropies, argmax, the sampler state), then the encoder append of
-the canvas into the cache.  Layers are independent, so the 30-layer step differs only in depth.
+oracle computes (every logit row, entropies, argmax, the sampler state), then the encoder append
+of the canvas into the cache.  Layers are independent, so the 30-layer step differs only in depth.
+Where the two sides' router logits sit at a k-th/(k+1)-th near-tie, either expert set is correct:
+the GPU's set is checked for validity and the oracle takes it, so that every row is compared.
 """
 import copy
 
@@ -15,7 +17,7 @@ import torch
 from block_diffusion_decoding_canvas_amd import driver, synth
 from oracle import model as om
 from oracle import sampler as osamp
-from tests.parity_util import assert_close_rel, compare_eb_step
+from tests.parity_util import GpuChain, assert_close_rel, compare_eb_step
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -37,41 +39,9 @@ def full():
     return dims, mnp, model, kv, ws, c64
 
 
-def _layers_on_oracle_inputs(dims, mnp, model, kv, ws, c64, canvas):
-    """Run each layer on the GPU from the oracle's own input to that layer (oracle -> GPU only);
-    return the oracle's per-layer routing info, the GPU router-logit error per layer and the
-    canvas rows whose expert set is certified in every layer."""
-    T, k = dims["C"], dims["top_k"]
-    h = mnp["embed"][np.asarray(canvas)].astype(np.float64)
-    cert = np.ones(T, dtype=bool)
-    for layer in range(dims["n_layers"]):
-        lw = mnp["layers"][layer]
-        h_next, _, _, info = om.layer_forward(h, lw, dims, layer, c64["k"][layer],
-                                              c64["v"][layer], c64["len"], causal=False)
-        hg = torch.from_numpy(h.reshape(T, -1).astype(np.float32)).to(DEV)
-        rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device=DEV)
-        ti = torch.zeros((T, k), dtype=torch.int32, device=DEV)
-        driver.layer_forward(model, kv, layer, 0, hg, ws, rl, ti, None)
-        torch.cuda.synchronize()
-        r_ref = info["router_logits"]
-        rerr = np.abs(rl.cpu().numpy() - r_ref).max()
-        srt = -np.sort(-r_ref, axis=1)
-        layer_cert = (srt[:, k - 1] - srt[:, k]) > 4 * rerr + 1e-7
-        tig = ti.cpu().numpy()
-        for t in np.nonzero(layer_cert)[0]:
-            assert set(tig[t]) == set(info["topk_idx"][t]), f"layer {layer} token {t} experts"
-        hout = hg.cpu().numpy().astype(np.float64)
-        h_in = h.reshape(T, -1).astype(np.float32).astype(np.float64)
-        assert_close_rel(hout[layer_cert] - h_in[layer_cert],
-                         h_next.reshape(T, -1)[layer_cert] - h_in[layer_cert],
-                         what=f"layer {layer} increment (certified routing)")
-        print(f"layer {layer}: router err {rerr:.2e}, certified {layer_cert.sum()}/{T}")
-        cert &= layer_cert
-        h = h_next
-    return cert
-
-
 def test_full_size_decoder_steps(full):
+    """Every logit row at the stated tolerance: the oracle takes the GPU's expert set wherever
+    the two sides' router logits sit at a k-th/(k+1)-th near-tie (checked for validity first)."""
     dims, mnp, model, kv, ws, c64 = full
     params = osamp.default_params()
     seed, ids = 2, [0]
@@ -79,64 +49,73 @@ def test_full_size_decoder_steps(full):
     st = osamp.new_state(osamp.init_canvas(seed, ids, dims["C"], dims["V"]))
     gs = driver.SamplerState(1, dims["C"], DEV)
     out = driver.StepOut(1, dims["C"], dims["V"], DEV)
+    out2 = driver.StepOut(1, dims["C"], dims["V"], DEV)
     for s in (0, 47):                        # first step, and the finalising last step
-        cert = _layers_on_oracle_inputs(dims, mnp, model, kv, ws, c64, st["canvas"])
+        chain = GpuChain(dims, model, kv, ws, st["canvas"], mnp["embed"])
         gs.load_host(st)
         driver.decoder_step(model, kv, s, p, gs, out, ws)
         torch.cuda.synchronize()
-        zr, z64, _ = om.decoder_forward(st["canvas"], mnp, c64)
+        # the step's logits and statistics are the chain's: same kernels and shapes, bitwise
+        driver.lm_head_forward(model, 1, chain.h, s, p, out2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.logits, out2.logits) and torch.equal(out.entropy, out2.entropy)
+        zr, z64, infos = om.decoder_forward(st["canvas"], mnp, c64, force_idx=chain.idx)
+        swaps = chain.check(infos, dims["top_k"], f"s={s}")
         zg = out.logits.float().cpu().numpy()
-        # rows whose experts are certified in every layer: the stated tolerance; rows with a
-        # near-tie expert swap differ by that expert's contribution: a loose sanity bound
-        assert_close_rel(zg[0, cert], zr[0, cert], what=f"logits s={s} (certified rows)")
-        assert np.linalg.norm(zg - zr) <= 0.1 * np.linalg.norm(zr)
+        assert_close_rel(zg, zr, what=f"logits s={s} (all rows)")
         err = np.abs(zg - z64).max(axis=-1)
         before = copy.deepcopy(st)
         ref = osamp.eb_step(zr, s, params, st, seed, ids)
         ok = compare_eb_step(f"full s={s}", params, seed, ids, before, st, ref, gs.host(), out,
                              z64, err)
-        print(f"step {s}: certified rows {cert.sum()}/{dims['C']}, mean H "
-              f"{ref['entropy'].mean():.4f}, commits {int(ref['commit_now'].sum())}, "
-              f"{'exact' if ok else 'near-tie'}")
-        assert cert.sum() >= dims["C"] // 4      # the certified comparison is not vacuous
+        rel = np.linalg.norm(zg - zr, axis=-1) / np.linalg.norm(zr, axis=-1)
+        print(f"step {s}: near-tie expert swaps per layer {swaps}, logits worst row rel err "
+              f"{rel.max():.2e}, median {np.median(rel):.2e}, mean H {ref['entropy'].mean():.4f}, "
+              f"commits {int(ref['commit_now'].sum())}, {'exact' if ok else 'near-tie'}")
         if s == 47:
             assert gs.host()["done"].all()
 
 
 def test_full_size_append(full):
+    """Every appended key and value at the stated tolerance (the oracle takes the GPU's expert
+    sets at near-ties); the append writes exactly what the encoder layer chain writes."""
     dims, mnp, model, kv, ws, c64 = full
-    T, k = dims["C"], dims["top_k"]
+    T = dims["C"]
     tokens = synth.prompt_ids(T, dims["V"], seed=7)[None]
-    # encoder routing certified per position, from each layer run on the oracle's own input
-    # (the layer writes its keys/values at [len, len + C); the append below rewrites them)
     kv.len[0] = CACHE
-    h = mnp["embed"][tokens].astype(np.float64)
-    cert_before = [np.ones(T, dtype=bool)]
-    for layer in range(dims["n_layers"] - 1):
-        h_next, _, _, info = om.layer_forward(h, mnp["layers"][layer], dims, layer,
-                                              c64["k"][layer], c64["v"][layer], c64["len"],
-                                              causal=True)
-        hg = torch.from_numpy(h.reshape(T, -1).astype(np.float32)).to(DEV)
-        rl = torch.zeros((T, dims["E"]), dtype=torch.float32, device=DEV)
-        driver.layer_forward(model, kv, layer, 1, hg, ws, rl, None, None)
-        torch.cuda.synchronize()
-        r_ref = info["router_logits"]
-        rerr = np.abs(rl.cpu().numpy() - r_ref).max()
-        srt = -np.sort(-r_ref, axis=1)
-        cert_before.append(cert_before[-1] & ((srt[:, k - 1] - srt[:, k]) > 4 * rerr + 1e-7))
-        h = h_next
+    chain = GpuChain(dims, model, kv, ws, tokens, mnp["embed"], causal=True)
+    chain_k = kv.k[:, 0, :, CACHE:CACHE + T].clone()
+    chain_v = kv.v[:, 0, :, CACHE:CACHE + T].clone()
     driver.kv_append_canvas(model, kv, torch.tensor(tokens, dtype=torch.int32, device=DEV), ws)
     torch.cuda.synchronize()
-    ref = dict(k=[a.copy() for a in c64["k"]], v=[a.copy() for a in c64["v"]],
-               len=np.array(c64["len"]))
-    om.encoder_append(tokens, mnp, ref)
-    assert kv.lengths() == [CACHE + T]
-    for layer in range(dims["n_layers"]):
-        cert = cert_before[layer]
-        print(f"append layer {layer}: certified positions {cert.sum()}/{T}")
-        assert cert.sum() >= T // 4
-        kg = kv.k[layer, 0, :, CACHE:].float().cpu().numpy()[:, cert]
-        vg = kv.v[layer, 0, :, CACHE:].float().cpu().numpy()[:, cert]
-        assert_close_rel(kg, ref["k"][layer][0, :, CACHE:][:, cert], what=f"appended K {layer}")
-        assert_close_rel(vg, ref["v"][layer][0, :, CACHE:][:, cert], what=f"appended V {layer}")
-    kv.len[0] = CACHE
+    try:
+        assert kv.lengths() == [CACHE + T]
+        assert torch.equal(kv.k[:, 0, :, CACHE:CACHE + T], chain_k)
+        assert torch.equal(kv.v[:, 0, :, CACHE:CACHE + T], chain_v)
+        ref = dict(k=[a.copy() for a in c64["k"]], v=[a.copy() for a in c64["v"]],
+                   len=np.array(c64["len"]))
+        # the last layer's FFN does not reach the cache: its routing is not forced or checked
+        force = chain.idx[:-1] + [None]
+        infos = _encoder_infos(tokens, mnp, c64, force)
+        swaps = chain.check(infos[:-1], dims["top_k"], "append")
+        om.encoder_append(tokens, mnp, ref, force_idx=force)
+        for layer in range(dims["n_layers"]):
+            kg = kv.k[layer, 0, :, CACHE:].float().cpu().numpy()
+            vg = kv.v[layer, 0, :, CACHE:].float().cpu().numpy()
+            assert_close_rel(kg, ref["k"][layer][0, :, CACHE:], what=f"appended K {layer}")
+            assert_close_rel(vg, ref["v"][layer][0, :, CACHE:], what=f"appended V {layer}")
+        print(f"append: near-tie expert swaps per layer {swaps}")
+    finally:
+        kv.len[0] = CACHE
+
+
+def _encoder_infos(tokens, mnp, c64, force):
+    """The oracle's routing infos of the encoder pass (forced sets as given), layer by layer."""
+    dims = mnp["dims"]
+    h = mnp["embed"][np.asarray(tokens)].astype(np.float64)
+    infos = []
+    for layer, lw in enumerate(mnp["layers"]):
+        h, _, _, info = om.layer_forward(h, lw, dims, layer, c64["k"][layer], c64["v"][layer],
+                                         c64["len"], causal=True, force_idx=force[layer])
+        infos.append(info)
+    return infos

@@ -157,3 +157,76 @@ def test_fp8_moe_with_all_experts_is_dense_mixture(top_k):
     dense = om.swiglu_ffn(u, lw["ws_gate_up"], lw["ws_down"])
     q = om.swiglu_ffn(u, qlw["ws_gate_up"], qlw["ws_down"], qlw["ss_gate_up"], qlw["ss_down"])
     assert np.linalg.norm(q - dense) <= 0.1 * np.linalg.norm(dense)
+
+
+# ---- fp8 KV cache configuration ----------------------------------------------------------------
+
+def _torch_qdq(x):
+    """Per-row e4m3 quantise-dequantise with torch: fp32 amax / 448 scale, fp32 division, the
+    float8_e4m3fn cast (nearest even), times the scale."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = t.abs().amax(dim=-1, keepdim=True)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    return ((t / s).clamp(-448, 448).to(torch.float8_e4m3fn).float().double() * s.double()).numpy()
+
+
+def test_quantize_dequantize_rows_matches_torch():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((40, 6, 64)) * np.exp2(rng.uniform(-8, 8, (40, 6, 1)))
+    x[3, 2] = 0.0
+    got = om.quantize_dequantize_rows(x)
+    assert np.array_equal(got, _torch_qdq(x))
+    assert np.array_equal(got[3, 2], np.zeros(64))
+    # idempotent: a stored row re-quantises to itself
+    assert np.array_equal(om.quantize_dequantize_rows(got), got)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_kv_attention_block_is_sdpa_on_quantised_rows(causal):
+    """The fp8 KV attention half-layer equals torch SDPA (GQA by repeated KV heads, with the
+    visibility mask) over the e4m3 quantise-dequantised rows of the bf16 QKV product, then the O
+    projection."""
+    from block_diffusion_decoding_canvas_amd import synth
+    import torch.nn.functional as F
+    dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=32, E=4, top_k=2, F=32, Fs=32, V=50, C=8,
+                window=0, global_every=1, eps=1e-6, kv_dtype="e4m3")
+    m = synth.model_to_f64(synth.make_model(dims, seed=13, norm_gain_std=0.1))
+    lw = m["layers"][0]
+    lw["w_qkv"] = lw["w_qkv"] * 20
+    rng = np.random.default_rng(14)
+    n, C = 11, dims["C"]
+    h = rng.standard_normal((1, C, 64))
+    kc = _torch_qdq(rng.standard_normal((1, 2, 16, 32)))      # a cache of stored e4m3 rows
+    vc = _torch_qdq(rng.standard_normal((1, 2, 16, 32)))
+    out, k, v = om.attention_block(h, lw, dims, 0, kc, vc, np.array([n]), causal)
+    u = F.rms_norm(torch.from_numpy(h[0]), (64,), weight=torch.from_numpy(lw["attn_norm"]),
+                   eps=1e-6)
+    qkv = (u @ torch.from_numpy(lw["w_qkv"]).T).to(torch.bfloat16).double().numpy()
+    q = _torch_qdq(qkv[:, :128].reshape(C, 4, 32))
+    kn = _torch_qdq(qkv[:, 128:192].reshape(C, 2, 32))
+    vn = _torch_qdq(qkv[:, 192:].reshape(C, 2, 32))
+    assert np.array_equal(k[0], kn) and np.array_equal(v[0], vn)
+    keys = np.concatenate([kc[0][:, :n], kn.transpose(1, 0, 2)], axis=1).repeat(2, axis=0)
+    vals = np.concatenate([vc[0][:, :n], vn.transpose(1, 0, 2)], axis=1).repeat(2, axis=0)
+    mask = np.ones((C, n + C), bool)
+    if causal:
+        mask[:, n:] = np.tril(np.ones((C, C), bool))
+    o = F.scaled_dot_product_attention(torch.from_numpy(q.transpose(1, 0, 2)),
+                                       torch.from_numpy(keys), torch.from_numpy(vals),
+                                       attn_mask=torch.from_numpy(mask)).numpy()
+    ref = h[0] + o.transpose(1, 0, 2).reshape(C, -1) @ lw["w_o"].T
+    assert np.allclose(out[0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_fp8_kv_append_stores_quantised_rows():
+    from block_diffusion_decoding_canvas_amd import synth
+    dims = dict(synth.dims_tiny(), kv_dtype="e4m3")
+    m = synth.model_to_f64(synth.make_model(dims, seed=15))
+    c = synth.empty_cache(dims, 1, 40)
+    c = dict(k=[a.astype(np.float64) for a in c["k"]], v=[a.astype(np.float64) for a in c["v"]],
+             len=c["len"])
+    om.encoder_append(synth.prompt_ids(16, dims["V"])[None], m, c)
+    for layer in range(dims["n_layers"]):
+        for x in (c["k"][layer][0, :, :16], c["v"][layer][0, :, :16]):
+            assert np.any(x != 0)
+            assert np.array_equal(om.quantize_dequantize_rows(x), x)   # whole e4m3 rows

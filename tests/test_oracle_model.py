@@ -155,8 +155,9 @@ def test_route_ties_lowest_index_descending_order():
     assert np.allclose(gates[0], [e4 / (e4 + 2 * e1), e1 / (e4 + 2 * e1), e1 / (e4 + 2 * e1)])
 
 
-def _torch_layer(h, lw, dims, kc, vc, n, causal, window=0):
-    """The same layer composed from torch library modules (Linear, rms_norm, SDPA, silu)."""
+def _torch_layer(h, lw, dims, kc, vc, n, causal, window=0, force_idx=None):
+    """The same layer composed from torch library modules (Linear, rms_norm, SDPA, silu, topk);
+    force_idx [C, k] replaces the router's top-k choice (gates renormalised over it)."""
     d, hq, hkv, dh = dims["d"], dims["hq"], dims["hkv"], dims["dh"]
     x = _t(h)
     u = F.rms_norm(x, (d,), weight=_t(lw["attn_norm"]), eps=dims["eps"])
@@ -168,6 +169,12 @@ def _torch_layer(h, lw, dims, kc, vc, n, causal, window=0):
     vals = torch.cat([_t(vc[:, :n]), v], 1).repeat_interleave(hq // hkv, 0)
     c = x.shape[0]
     mask = torch.ones(c, n + c, dtype=torch.bool)
+    if window > 0:
+        # brute-force window rule: canvas query i (absolute n + i) sees cache j iff its distance
+        # is below the window
+        for i in range(c):
+            for j in range(n):
+                mask[i, j] = (n + i) - j < window
     if causal:
         mask[:, n:] = torch.tril(torch.ones(c, c, dtype=torch.bool))
     o = F.scaled_dot_product_attention(q, keys, vals, attn_mask=mask)
@@ -178,9 +185,13 @@ def _torch_layer(h, lw, dims, kc, vc, n, causal, window=0):
     pi = torch.softmax(r, -1).gather(1, top.indices)
     gates = pi / pi.sum(1, keepdim=True)
     y = _t(_ffn_torch(u.numpy(), lw["ws_gate_up"], lw["ws_down"]))
+    idx = top.indices if force_idx is None else torch.as_tensor(force_idx)
+    if force_idx is not None:
+        pi = torch.softmax(r, -1).gather(1, idx)
+        gates = pi / pi.sum(1, keepdim=True)
     for t in range(c):
         for j in range(dims["top_k"]):
-            e = int(top.indices[t, j])
+            e = int(idx[t, j])
             y[t] += gates[t, j] * _t(_ffn_torch(u[t:t + 1].numpy(), lw["w_gate_up"][e],
                                                  lw["w_down"][e]))[0]
     return (x + y).numpy()
@@ -260,3 +271,99 @@ def test_attention_query_subset_equals_full_rows(causal):
     rows = np.array([0, 3, 7, 11])
     sub = om.attention(q[rows], kc, vc, kn, vn, mask[rows], causal, q_pos=rows)
     assert np.array_equal(sub, full[rows])
+
+
+def _torch_decoder(canvas, m, cache, force=None):
+    """The decoder pass composed from torch library routines: F.embedding, the layers above,
+    F.rms_norm with the final gain, F.linear with the LM head and the cast to torch.bfloat16.
+    force: per layer [B, C, k] expert ids replacing the router's choice (None: the router's)."""
+    dims = m["dims"]
+    out = []
+    for b in range(canvas.shape[0]):
+        h = F.embedding(torch.as_tensor(canvas[b]), _t(m["embed"])).numpy()
+        n = int(cache["len"][b])
+        for layer, lw in enumerate(m["layers"]):
+            window = 0 if dims["window"] == 0 or (layer + 1) % dims["global_every"] == 0 \
+                else dims["window"]
+            fi = None if force is None else force[layer][b]
+            h = _torch_layer(h, lw, dims, cache["k"][layer][b], cache["v"][layer][b], n,
+                             causal=False, window=window, force_idx=fi)
+        u = F.rms_norm(_t(h), (dims["d"],), weight=_t(m["final_norm"]), eps=dims["eps"])
+        out.append(F.linear(u, _t(m["w_lm"])))
+    z = torch.stack(out)
+    return z.to(torch.bfloat16).to(torch.float64).numpy(), z.numpy()
+
+
+def _decoder_case(window, batch, lens, seed=21):
+    dims = dict(n_layers=2, d=32, hq=4, hkv=2, dh=8, E=6, top_k=2, F=24, Fs=16, V=96, C=8,
+                window=window, global_every=2, eps=1e-6)
+    m = synth.model_to_f64(synth.make_model(dims, seed=seed, norm_gain_std=0.1, lm_std=0.5))
+    for lw in m["layers"]:
+        for k in ("w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down", "w_qkv", "w_o"):
+            lw[k] = lw[k] * 20                           # larger weights: non-trivial routing
+    cap = max(lens) + dims["C"]
+    c = synth.make_cache(dims, batch, cap, max(lens), seed=seed + 1)
+    cache = dict(k=[a.astype(np.float64) for a in c["k"]], v=[a.astype(np.float64) for a in c["v"]],
+                 len=np.array(lens))
+    canvas = np.random.default_rng(seed + 2).integers(0, dims["V"], size=(batch, dims["C"]))
+    return dims, m, cache, canvas
+
+
+@pytest.mark.parametrize("window,lens", [(0, [13]), (6, [13, 9])])
+def test_decoder_forward_matches_torch_composition(window, lens):
+    """The whole decoder pass, head included (embedding gather, the layers, the final RMSNorm with
+    its own gain, the LM head, the bf16 rounding of the logits), against the torch composition;
+    a global model and a windowed one (layer 0 windowed, layer 1 global) with two cache lengths."""
+    dims, m, cache, canvas = _decoder_case(window, len(lens), lens)
+    zr, z64, infos = om.decoder_forward(canvas, m, cache)
+    ref_r, ref64 = _torch_decoder(canvas, m, cache)
+    assert np.allclose(z64, ref64, rtol=1e-10, atol=1e-12)
+    assert np.array_equal(zr, ref_r)
+    # the rounding is not the identity on these logits, and the head's gain matters
+    assert not np.array_equal(zr, z64)
+    m1 = dict(m, final_norm=np.ones_like(m["final_norm"]))
+    assert not np.allclose(om.decoder_forward(canvas, m1, cache)[1], z64, rtol=1e-3)
+
+
+def test_decoder_forward_forced_routing():
+    """Forcing the router's own top-k sets reproduces the plain pass exactly; forcing other sets
+    (the second and third expert by logit) equals the torch composition with those sets."""
+    dims, m, cache, canvas = _decoder_case(6, 2, [13, 9], seed=31)
+    zr, z64, infos = om.decoder_forward(canvas, m, cache)
+    own = [info["topk_idx"].reshape(2, dims["C"], -1) for info in infos]
+    zr2, z642, _ = om.decoder_forward(canvas, m, cache, force_idx=own)
+    assert np.array_equal(z64, z642) and np.array_equal(zr, zr2)
+    alt = []
+    for info in infos:
+        r = info["router_logits"]
+        order = np.argsort(-r, axis=1, kind="stable")
+        alt.append(order[:, 1:1 + dims["top_k"]].reshape(2, dims["C"], -1))
+    za_r, za64, ainfos = om.decoder_forward(canvas, m, cache, force_idx=alt)
+    ref_r, ref64 = _torch_decoder(canvas, m, cache, force=alt)
+    assert np.allclose(za64, ref64, rtol=1e-10, atol=1e-12)
+    assert not np.allclose(za64, z64, rtol=1e-3)
+    for info, a in zip(ainfos, alt):
+        assert np.array_equal(info["topk_idx"], a.reshape(-1, dims["top_k"]))
+
+
+def test_fp8_head_matches_torch_float8_composition():
+    """The fp8 configuration's head: per-row e4m3 codes of the final-norm output (torch float32
+    division and float8_e4m3fn cast) times the e4m3 LM-head codes, scaled by both row scales."""
+    from oracle.numerics import quantize_rows_e4m3
+    dims, m, cache, canvas = _decoder_case(0, 1, [13], seed=41)
+    mq = dict(m)
+    mq["w_lm"], mq["s_lm"] = quantize_rows_e4m3(m["w_lm"])
+    zr, z64, _ = om.decoder_forward(canvas, mq, cache)
+    # the layers are untouched by the head's quantisation: recover the final hidden state from
+    # the bf16-weight pass by re-running the torch layers
+    h = F.embedding(torch.as_tensor(canvas[0]), _t(m["embed"])).numpy()
+    for layer, lw in enumerate(m["layers"]):
+        h = _torch_layer(h, lw, dims, cache["k"][layer][0], cache["v"][layer][0], 13, False)
+    u = F.rms_norm(_t(h), (dims["d"],), weight=_t(m["final_norm"]), eps=dims["eps"])
+    u32 = u.to(torch.float32)
+    amax = u32.abs().amax(dim=1, keepdim=True)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (u32 / s).to(torch.float8_e4m3fn).to(torch.float64)
+    ref = (codes @ _t(mq["w_lm"]).T) * s.to(torch.float64) * _t(mq["s_lm"])[None]
+    assert np.allclose(z64[0], ref.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.array_equal(zr[0], ref.to(torch.bfloat16).to(torch.float64).numpy())
