@@ -97,6 +97,9 @@ _SIGS = {
     "dg_generate_sched": (i32, [c_void_p, P(dg_kv), P(dg_gen_params), P(dg_sched_params),
                                 P(dg_eb_state), P(dg_step_out), c_void_p, P(i32), c_void_p,
                                 c_void_p, ctypes.c_size_t, c_void_p]),
+    "dg_eb_sample_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "dg_eb_sample_noalloc": (i32, [c_void_p, i32, i32, i32, i32, P(dg_eb_params), P(dg_eb_state),
+                                   P(dg_step_out), c_void_p]),
     "dg_kv_append_canvas": (i32, [c_void_p, P(dg_kv), c_void_p, c_void_p, ctypes.c_size_t,
                                   c_void_p]),
     "dg_append_workspace_bytes": (ctypes.c_size_t, [c_void_p, i32, i32]),

@@ -447,6 +447,64 @@ dg_status dg_eb_sample(const uint16_t* logits, int32_t B, int32_t C, int32_t V, 
   return dg_sample(logits, B, C, V, step, &q, st, out, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---- the sampler without a caller workspace ------------------------------------------------
+// Its scratch (chunk statistics, candidate flags and candidate partials) lives in this
+// file-scope device array, one copy per GPU, held until the process ends.  In host code the
+// array's name is only a host-side stand-in: its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is passed to kernels.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dg_status scratch_ptr(void** out) {
+  int dev = -1;
+  DG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DG_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dg_eb_sample_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+dg_status dg_eb_sample_noalloc(const uint16_t* logits, int32_t B, int32_t C, int32_t V,
+                               int32_t step, const dg_eb_params* p, dg_eb_state* st,
+                               dg_step_out* out, void* stream) {
+  if (!logits) return fail(DG_ERR_NULL, "logits is NULL");
+  if (B < 1 || C < 1 || C > 1024 || V < 256 || V % 256)
+    return fail(DG_ERR_SHAPE, "need B >= 1, 1 <= C <= 1024, V a multiple of 256");
+  const size_t need = dg_eb_workspace_bytes(B, C, V);
+  if (need > kNoAllocScratchBytes)
+    return fail(DG_ERR_WORKSPACE, "B = %d, C = %d, V = %d need %zu bytes of scratch; the "
+                "built-in scratch holds %zu", B, C, V, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  dg_status s = scratch_ptr(&ws);
+  if (s != DG_OK) return s;
+  // every scratch entry a kernel reads is written earlier in the same call: nothing to clear
+  return dg_eb_sample(logits, B, C, V, step, p, st, out, ws, kNoAllocScratchBytes, stream);
+}
+
 dg_status dg_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* stream) {
   if (!src || !dst) return fail(DG_ERR_NULL, "NULL pointer");
   if (rows < 16 || cols < 32 || rows % 16 || cols % 32)

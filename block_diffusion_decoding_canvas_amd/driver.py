@@ -140,6 +140,16 @@ def decoder_step_sched(model, kv, step, params, state, out, ws, stream=None):
                                     stream_ptr(stream)), "dg_decoder_step_sched")
 
 
+def eb_sample_noalloc(logits, step, params, state, out, stream=None):
+    """The standalone EB sampler with the library's built-in scratch (dg_eb_sample_noalloc)."""
+    lib = _lib.load()
+    b, c, v = logits.shape
+    st, o = state.struct(), out.struct()
+    check(lib.dg_eb_sample_noalloc(ptr(logits), b, c, v, step, ctypes.byref(params),
+                                   ctypes.byref(st), ctypes.byref(o), stream_ptr(stream)),
+          "dg_eb_sample_noalloc")
+
+
 def dims_struct(d):
     wd = _lib.DG_FP8_E4M3 if d.get("wdtype", "bf16") in ("e4m3", "fp8") else _lib.DG_BF16
     return _lib.dg_dims(d["n_layers"], d["d"], d["hq"], d["hkv"], d["dh"], d["E"], d["top_k"],

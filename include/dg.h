@@ -212,6 +212,22 @@ dg_status dg_eb_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len
                        int32_t step, const dg_eb_params* params, dg_eb_state* state,
                        dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
 
+/* dg_eb_sample for callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and results,
+ * with the scratch in a fixed device array of dg_eb_sample_noalloc_max_bytes() bytes (8 MiB) that
+ * the library holds on each GPU it runs on until the process ends.  The device address of that
+ * array is looked up once per device on the first call there (with that device current); the call
+ * itself allocates nothing.  Errors: those of dg_eb_sample, and DG_ERR_WORKSPACE when
+ * dg_eb_workspace_bytes(B, C, V) exceeds the array (at V = 262,144 that is about 4,600 positions
+ * in all, e.g. B = 16 canvases of 256).  Every call on one GPU shares that GPU's array: calls
+ * that may overlap on one GPU (different streams, or host threads) race and must be ordered by
+ * the caller.  No entry needs clearing between calls: every scratch entry a kernel reads is
+ * written earlier in the same call. */
+size_t dg_eb_sample_noalloc_max_bytes(void);
+dg_status dg_eb_sample_noalloc(const uint16_t* logits, int32_t batch, int32_t canvas_len,
+                               int32_t vocab, int32_t step, const dg_eb_params* params,
+                               dg_eb_state* state, dg_step_out* out, void* stream);
+
 /* dg_decoder_step and dg_eb_sample with any of the pipeline's schedulers (dg_sched_params).
  * Same layouts, workspaces and errors; DG_ERR_STATE also for an unknown kind, a negative
  * temperature or a corrector_steps outside [0, max_steps - 1], DG_ERR_UNSUPPORTED for

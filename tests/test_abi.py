@@ -154,6 +154,30 @@ def test_eb_sample_validation_before_launch():
     assert call(params=bad) == 6
 
 
+def test_eb_sample_noalloc_validation_before_launch():
+    """The allocation-free sampler validates like dg_eb_sample and rejects inputs whose scratch
+    exceeds its fixed array, before any HIP call."""
+    lib = _lib.load()
+    cap = lib.dg_eb_sample_noalloc_max_bytes()
+    assert cap == 8 << 20
+    p = driver.eb_params()
+    fake = ctypes.c_void_p(0x1000)
+    state = _lib.dg_eb_state(*([0x1000] * 7))
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0)
+
+    def call(b=1, c=256, v=262144, logits=fake, step=0):
+        return lib.dg_eb_sample_noalloc(logits, b, c, v, step, ctypes.byref(p),
+                                        ctypes.byref(state), ctypes.byref(out), None)
+
+    assert call(logits=None) == 1                # DG_ERR_NULL
+    assert call(v=1000) == 2                     # DG_ERR_SHAPE
+    assert call(c=2048) == 2
+    assert lib.dg_eb_workspace_bytes(16, 256, 262144) <= cap
+    assert lib.dg_eb_workspace_bytes(32, 256, 262144) > cap
+    assert call(b=32) == 5                       # DG_ERR_WORKSPACE: beyond the fixed scratch
+    assert b"scratch" in lib.dg_last_error()
+
+
 def test_layer_forward_tokens_validate():
     lib = _lib.load()
     st, h = _create(_tiny_dims())
