@@ -36,6 +36,7 @@ def log(msg):
 HBM_PEAK_GBS = 8000.0
 GATEUP_SAMPLE_EVERY = 8
 MFMA_BF16_PEAK_TFS = 2500.0
+MFMA_FP8_PEAK_TFS = 5000.0
 
 
 def parse():
@@ -58,6 +59,8 @@ def parse():
                     help="run only the long-context batched fp8 workload (one JSON object)")
     ap.add_argument("--no-long-fp8", action="store_true",
                     help="skip the long-context batched fp8 line")
+    ap.add_argument("--long-kv", choices=("e4m3", "bf16"), default="e4m3",
+                    help="KV cache type of the long-context batched fp8 line")
     ap.add_argument("--decoder-only", action="store_true",
                     help="only the decoder steps and appends (for hardware-counter runs: no "
                          "prefill, generation loop, standalone sampler, ceilings or CPU oracle)")
@@ -309,21 +312,30 @@ def attention_flops_windowed(dims, cache_len, window, causal):
 
 
 def long_fp8_measure(driver, dev, layers=30, batch=4, cache=131072, steps=1, warmup=1,
-                     cpu=True):
+                     cpu=True, kv_dtype="e4m3"):
     """The long-context batched fp8 workload: the full-width decoder with e4m3 expert and LM-head
-    weights (per-row fp32 scales), 4 canvases of 256 tokens each on its own 131,072-token N(0,1)
-    cache, 5 sliding-window (1,024) layers to 1 global; one bench step = every canvas's EB steps
-    (48, adaptive stop on) + the append of the 4 canvases.  Returns one JSON-able dict."""
+    weights (per-row fp32 scales), 4 canvases of 256 tokens each on its own 131,072-token cache
+    (kv_dtype "e4m3": e4m3 rows with fp32 row scales, QK^T on the e4m3 MFMA and P V on the bf16
+    one; "bf16": N(0,1) bf16 rows), 5 sliding-window (1,024) layers to 1 global; one bench step =
+    every canvas's EB steps (48, adaptive stop on) + the append of the 4 canvases.  Returns one
+    JSON-able dict."""
     import torch
     from block_diffusion_decoding_canvas_amd import synth
     dims = synth.dims_long(n_layers=layers)
+    kv8 = kv_dtype == "e4m3"
+    if kv8:
+        dims["kv_dtype"] = "e4m3"
     B, C, V = batch, dims["C"], dims["V"]
-    log(f"long fp8: drawing the model and {batch} x {cache}-token caches")
+    log(f"long fp8: drawing the model and {batch} x {cache}-token {kv_dtype} caches")
     w = synth.make_model_device(dims, dev, seed=0)
     model = driver.Model(w, wdtype="e4m3")
     cap = cache + C
-    kc, vc = synth.make_cache_device(dims, B, cap, cache, dev, seed=1)
-    kv = driver.KVCache(dims, B, cap, dev, kc, vc, [cache] * B)
+    if kv8:
+        kc, vc, ks, vs = synth.make_cache_fp8_device(dims, B, cap, cache, dev, seed=1)
+        kv = driver.KVCache(dims, B, cap, dev, kc, vc, [cache] * B, ks, vs)
+    else:
+        kc, vc = synth.make_cache_device(dims, B, cap, cache, dev, seed=1)
+        kv = driver.KVCache(dims, B, cap, dev, kc, vc, [cache] * B)
     ws = driver.workspace(model.workspace_bytes(B), dev)
     params = driver.eb_params()
     state = driver.SamplerState(B, C, dev)
@@ -376,15 +388,21 @@ def long_fp8_measure(driver, dev, layers=30, batch=4, cache=131072, steps=1, war
     gu_bytes = (dims["E"] * 2 * f * d + 2 * fs * d) + T * d + (T * k * f + T * fs) * 4
     gu_t = ms_gu / max(n_gu, 1) * 1e-3
     gu_gbs = gu_bytes / gu_t / 1e9
+    # attention peak: bf16 MFMA; with the e4m3 cache, half the flops (QK^T) run on the e4m3
+    # MFMA at twice the rate, so the attainable peak is the harmonic mix 2 / (1/5.0 + 1/2.5) PF/s
+    at_peak = (2.0 / (1.0 / MFMA_FP8_PEAK_TFS + 1.0 / MFMA_BF16_PEAK_TFS) if kv8
+               else MFMA_BF16_PEAK_TFS)
     res = dict(
         workload=(f"{layers}-layer full-width decoder, e4m3 experts + LM head, {B} x 256-token "
-                  f"canvases on {cache}-token caches each, 5 sliding-window (1024) : 1 global "
-                  f"layers, 48 EB steps max (adaptive stop) + append per bench step"),
+                  f"canvases on {cache}-token {kv_dtype} KV caches each, 5 sliding-window (1024) "
+                  f": 1 global layers, 48 EB steps max (adaptive stop) + append per bench step"),
         steps_per_s=round(n_steps / elapsed, 3), tokens_per_s=round(B * C * steps / elapsed, 2),
         ms_per_bench_step=round(elapsed / steps * 1e3, 1), decoder_steps=n_steps,
-        bench_steps=steps, warmup=warmup, dtype="e4m3 experts and LM head, bf16 attention",
-        roofline=dict(bound="mfma", achieved=round(at_tf, 1), peak=MFMA_BF16_PEAK_TFS,
-                      unit="TFLOP/s", frac=round(at_tf / MFMA_BF16_PEAK_TFS, 4),
+        bench_steps=steps, warmup=warmup, kv_cache=kv_dtype,
+        dtype=("e4m3 experts, LM head and KV cache (QK^T e4m3, P V bf16)" if kv8 else
+               "e4m3 experts and LM head, bf16 attention"),
+        roofline=dict(bound="mfma", achieved=round(at_tf, 1), peak=round(at_peak, 1),
+                      unit="TFLOP/s", frac=round(at_tf / at_peak, 4),
                       kernel="attention (+ split merge): global and windowed layers",
                       launches=n_at, ms_per_pass=round(ms_at, 2)),
         moe_gateup_fp8=dict(bound="hbm", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
@@ -392,6 +410,8 @@ def long_fp8_measure(driver, dev, layers=30, batch=4, cache=131072, steps=1, war
                             bytes_per_launch=gu_bytes, avg_launch_us=round(gu_t * 1e6, 2),
                             launches=n_gu))
     del model, w, kv, kc, vc, ws, out
+    if kv8:
+        del ks, vs
     torch.cuda.empty_cache()
     if cpu:
         res["cpu_baseline"] = cpu_baseline_long(dims, B, cache)
@@ -512,7 +532,7 @@ def main():
         return
     if args.long_fp8_only:
         print(json.dumps(long_fp8_measure(driver, dev, layers=args.layers,
-                                          cpu=not args.no_cpu_baseline)))
+                                          cpu=not args.no_cpu_baseline, kv_dtype=args.long_kv)))
         return
     C, B = dims["C"], 1
     cap = args.cache + C * args.canvases
@@ -650,7 +670,7 @@ def main():
         del model, weights, kv, kc, vc, ws, out, state
         torch.cuda.empty_cache()
         long_fp8 = long_fp8_measure(driver, dev, layers=args.layers,
-                                    cpu=not args.no_cpu_baseline)
+                                    cpu=not args.no_cpu_baseline, kv_dtype=args.long_kv)
 
     cpu = None
     if not (args.no_cpu_baseline or args.decoder_only):

@@ -36,7 +36,8 @@ class dg_layer_w(ctypes.Structure):
 
 class dg_kv(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("batch", i32), ("cap", i32),
-                ("len", ctypes.POINTER(i32))]
+                ("len", ctypes.POINTER(i32)), ("dtype", i32), ("k_scale", c_void_p),
+                ("v_scale", c_void_p)]
 
 
 class dg_eb_params(ctypes.Structure):

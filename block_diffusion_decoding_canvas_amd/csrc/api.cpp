@@ -611,6 +611,10 @@ struct DecWs {
   uint8_t* act8;      // its e4m3 codes
   float* act8s;       // [T k + T] row scales
   uint8_t* hot;       // 1 KiB read by the streaming kernels' past-the-end loads (never used)
+  uint8_t* kq;        // [T][Hkv][dh] e4m3 canvas keys (fp8 KV cache)
+  uint8_t* vq;        // values
+  float* kqs;         // [T][Hkv] their row scales
+  float* vqs;
 };
 
 int attn_base_blocks(const dg_dims& d, int B, int C) {
@@ -651,6 +655,12 @@ DecWs carve_dec(Carver& c, const dg_dims& d, int B, int C) {
   w.y = c.take<uint16_t>(rows * d.d_model);
   w.eb = carve_eb(c, static_cast<int>(T), d.vocab / dg::gemm_lmhead_rows_per_block(), d.vocab);
   w.hot = c.take<uint8_t>(1024);
+  // e4m3 canvas key and value rows (used with an fp8 KV cache; small, so always carved)
+  const size_t kvrows = T * d.n_kv_heads;
+  w.kq = c.take<uint8_t>(kvrows * d.head_dim);
+  w.vq = c.take<uint8_t>(kvrows * d.head_dim);
+  w.kqs = c.take<float>(kvrows);
+  w.vqs = c.take<float>(kvrows);
   w.u8 = nullptr; w.u8s = nullptr; w.act32 = nullptr; w.act8 = nullptr; w.act8s = nullptr;
   if (d.wdtype == DG_FP8_E4M3) {
     w.u8 = c.take<uint8_t>(T * d.d_model);
@@ -673,6 +683,14 @@ size_t kv_layer_elems(const dg_dims& d, const dg_kv* kv) {
 // need_room: the call appends C tokens per canvas
 dg_status check_kv(const dg_model* m, const dg_kv* kv, bool need_room, int C = 0) {
   if (!kv || !kv->k || !kv->v || !kv->len) return fail(DG_ERR_NULL, "kv or a kv pointer is NULL");
+  if (kv->dtype != DG_BF16 && kv->dtype != DG_FP8_E4M3)
+    return fail(DG_ERR_SHAPE, "kv dtype %d is neither DG_BF16 nor DG_FP8_E4M3", kv->dtype);
+  if (kv->dtype == DG_FP8_E4M3) {
+    if (!kv->k_scale || !kv->v_scale) return fail(DG_ERR_NULL, "fp8 kv scale pointer is NULL");
+    if (m->dims.head_dim != 128 && m->dims.head_dim != 256)
+      return fail(DG_ERR_SHAPE, "an fp8 kv cache needs head_dim 128 or 256 (got %d)",
+                  m->dims.head_dim);
+  }
   if (kv->batch < 1 || kv->batch > 64) return fail(DG_ERR_SHAPE, "kv batch must be in [1, 64]");
   if (kv->cap < 1) return fail(DG_ERR_SHAPE, "kv capacity must be >= 1");
   for (int b = 0; b < kv->batch; ++b) {
@@ -711,8 +729,13 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causa
   const int B = mapped ? bm->n : kv->batch, T = B * C;
   const int dq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const size_t kvl = kv_layer_elems(d, kv);
-  uint16_t* kc = static_cast<uint16_t*>(kv->k) + kvl * l;
-  uint16_t* vc = static_cast<uint16_t*>(kv->v) + kvl * l;
+  const bool f8 = kv->dtype == DG_FP8_E4M3;
+  const size_t esz = f8 ? 1 : 2;      // bytes per cached element
+  uint8_t* kc = static_cast<uint8_t*>(kv->k) + kvl * esz * l;
+  uint8_t* vc = static_cast<uint8_t*>(kv->v) + kvl * esz * l;
+  const size_t kvr = kvl / d.head_dim;  // rows (one scale each) per layer
+  float* ksc = f8 ? kv->k_scale + kvr * l : nullptr;
+  float* vsc = f8 ? kv->v_scale + kvr * l : nullptr;
 
   dg::WGemmArgs g;
   memset(&g, 0, sizeof(g));
@@ -725,7 +748,9 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causa
   // attention over [visible cache ; canvas]
   dg::AttnArgs at;
   memset(&at, 0, sizeof(at));
-  at.qkv = w.qkv; at.kc = kc; at.vc = vc; at.cap = kv->cap;
+  at.qkv = w.qkv; at.cap = kv->cap;
+  at.kc = reinterpret_cast<const uint16_t*>(kc);
+  at.vc = reinterpret_cast<const uint16_t*>(vc);
   at.B = B; at.C = C; at.Hq = d.n_q_heads; at.Hkv = d.n_kv_heads; at.dh = d.head_dim;
   at.window = layer_global(d, l) ? 0 : d.window;
   at.causal = causal ? 1 : 0;
@@ -744,10 +769,23 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causa
   at.n_split = std::min(w.max_split, dg::attention_pick_split(kv->batch, C, d.n_q_heads,
                                                               d.n_kv_heads, max_keys));
   at.o_part = w.o_part; at.ml_part = w.ml_part; at.out = w.attn;
+  if (f8) {
+    // e4m3 rows of the canvas keys and values (an encoder pass also stores them in the cache at
+    // len + i: rows the attention does not read from the cache)
+    at.f8 = 1;
+    at.ksc = ksc; at.vsc = vsc;
+    at.kq = w.kq; at.vq = w.vq; at.kqs = w.kqs; at.vqs = w.vqs;
+    DG_LAUNCH(PC_QUANT, s, dg::launch_kv_quant(at, w.kq, w.vq, w.kqs, w.vqs,
+                                                  causal ? kc : nullptr, causal ? vc : nullptr,
+                                                  causal ? ksc : nullptr, causal ? vsc : nullptr,
+                                                  s));
+  }
   DG_LAUNCH(PC_ATTENTION, s, dg::launch_attention(at, s));
-  if (causal) {
-    DG_LAUNCH(PC_KV_WRITE, s, dg::launch_kv_write(w.qkv, kc, vc, B, C, d.n_q_heads, d.n_kv_heads,
-                                                  d.head_dim, kv->cap, kv->len, s));
+  if (causal && !f8) {
+    DG_LAUNCH(PC_KV_WRITE, s, dg::launch_kv_write(w.qkv, reinterpret_cast<uint16_t*>(kc),
+                                                  reinterpret_cast<uint16_t*>(vc), B, C,
+                                                  d.n_q_heads, d.n_kv_heads, d.head_dim,
+                                                  kv->cap, kv->len, s));
   }
   if (skip_ffn) return DG_OK;
 
@@ -786,8 +824,8 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   float* gates = trace_gates ? trace_gates : w.gates;
   DG_LAUNCH(PC_TOPK, s, dg::launch_topk(w.router_part, kRouterSplit, T, d.n_experts, d.top_k, idx,
                                         gates, trace_logits, s));
-  // expert tiles: wide ones for long prefill chunks (bf16 weights)
-  const int tile_rows = fp8 ? dg::moe_tile_rows_min() : dg::moe_tile_rows(T);
+  // expert tiles: wide ones for long prefill chunks and large batches (bf16 and e4m3 weights)
+  const int tile_rows = dg::moe_tile_rows(T);
   DG_LAUNCH(PC_PERMUTE, s, dg::launch_permute(idx, T, d.top_k, d.n_experts,
                                               tile_rows, w.perm, w.inv, w.chunks,
                                               w.n_chunks, w.max_chunks, s));
@@ -809,7 +847,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
     g.X = reinterpret_cast<const uint16_t*>(w.u8); g.x_scale = w.u8s;
     g.w_scale = lw.s_gate_up; g.wsc_estride = 2LL * d.ffn_inner; g.w_scale_sh = lw.ss_gate_up;
     g.out = w.act32;
-    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup_fp8(g, s));
+    DG_LAUNCH(PC_MOE_GATEUP, s, dg::launch_moe_gateup_fp8(g, tile_rows, s));
     DG_LAUNCH(PC_QUANT, s, dg::launch_quant_rows(w.act32, true, fmax, w.act8, fmax, w.act8s, rows,
                                                  static_cast<long long>(T) * d.top_k,
                                                  d.ffn_inner, d.shared_inner, s));
@@ -828,7 +866,7 @@ dg_status run_ffn(const dg_model* m, int l, int T, DecWs& w, const uint16_t* nex
   if (fp8) {
     g.X = reinterpret_cast<const uint16_t*>(w.act8); g.x_scale = w.act8s;
     g.w_scale = lw.s_down; g.wsc_estride = d.d_model; g.w_scale_sh = lw.ss_down;
-    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down_fp8(g, s));
+    DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down_fp8(g, tile_rows, s));
   } else {
     DG_LAUNCH(PC_MOE_DOWN, s, dg::launch_moe_down(g, tile_rows, s));
   }

@@ -215,8 +215,8 @@ hipError_t launch_gemm_dense_f32(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s);       // logits + stats
 int gemm_lmhead_rows_per_block();
 // expert products over fragment-major ("packed") weights, in tiles of tile_rows gathered rows:
-// moe_tile_rows(ntok) for bf16 weights (32, or 128 once a call routes ntok >= 1,024 tokens,
-// about 64 rows per expert and more), moe_tile_rows_min() for e4m3 weights and for sizing
+// moe_tile_rows(ntok) (32, or 128 once a call routes ntok >= 1,024 tokens, about 64 rows per
+// expert and more), moe_tile_rows_min() for sizing
 hipError_t launch_moe_gateup(const WGemmArgs& a, int tile_rows, hipStream_t s);  // SwiGLU act
 hipError_t launch_moe_down(const WGemmArgs& a, int tile_rows, hipStream_t s);    // Y rows bf16
 int moe_tile_rows(int ntok);
@@ -226,8 +226,8 @@ hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s);
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s);
 // e4m3 variants (X and W e4m3 codes, per-row scales); gate/up writes the fp32 SwiGLU output
-hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s);      // fp32 act
-hipError_t launch_moe_down_fp8(const WGemmArgs& a, hipStream_t s);        // Y rows bf16
+hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, int tile_rows, hipStream_t s);  // fp32 act
+hipError_t launch_moe_down_fp8(const WGemmArgs& a, int tile_rows, hipStream_t s);    // Y rows bf16
 hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s);   // logits + stats
 hipError_t launch_pack_fp8(const void* src, void* dst, long long rows, long long cols,
                            hipStream_t s);
@@ -251,8 +251,23 @@ struct AttnArgs {
   uint16_t* o_part;       // [n_split][B][Hkv][R][dh] bf16 (R = Hq/Hkv * C)
   float* ml_part;         // [n_split][B][Hkv][R][2]
   uint16_t* out;          // [B*C][Hq*dh]
+  // fp8 KV cache: kc / vc hold e4m3 codes (bytes, same layout) with one fp32 scale per row in
+  // ksc / vsc [B][Hkv][cap]; the call's canvas keys and values are read as e4m3 rows too, from
+  // kq / vq [B*C][Hkv][dh] with scales kqs / vqs [B*C][Hkv]
+  int f8;
+  const float* ksc;
+  const float* vsc;
+  const uint8_t* kq;
+  const uint8_t* vq;
+  const float* kqs;
+  const float* vqs;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// e4m3 rows of the call's canvas keys and values (one scale per token and KV head) from the
+// bf16 QKV product into kq / vq (+ scales); with kc != NULL they are also written into the cache
+// at [len[b] + i] (kc/vc codes, ksc/vsc scales of this layer)
+hipError_t launch_kv_quant(const AttnArgs& a, uint8_t* kq, uint8_t* vq, float* kqs, float* vqs,
+                           uint8_t* kc, uint8_t* vc, float* ksc, float* vsc, hipStream_t s);
 int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys);
 
 // per-token kernels

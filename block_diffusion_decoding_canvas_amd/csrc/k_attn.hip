@@ -46,6 +46,40 @@ struct AttnCfg {
   static constexpr int RING = 8 / QT;  // fragment ring depth: 8 MFMAs of cover
 };
 
+// fp8 KV cache: K tiles are e4m3 bytes in LDS (S^T = K Q^T on the 16x16x128 e4m3 MFMA, Q
+// quantised per query row in the prologue), V tiles are dequantised to bf16 as they are staged
+// (P V stays on the bf16 MFMA)
+template <int DH>
+struct AttnF8Cfg {
+  static constexpr int K8S = DH + 32;        // bytes per K row in LDS (stride / 16 = 2 mod 4)
+  static constexpr int NKB = DH / 128;       // 128-wide dh blocks of QK^T
+  static constexpr int PCH = DH / 16;        // 16-byte pieces (16 values) per key row
+  static constexpr int NPC = KT * PCH;       // pieces per tile
+  static constexpr int PIT = (NPC + AttnCfg<DH>::NTHR - 1) / AttnCfg<DH>::NTHR;
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// one 16x16x128 e4m3 MFMA: A and B hold 32 bytes per lane in the same k order
+__device__ __forceinline__ f32x4 mfma_f8_128(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+  const i32x8 a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z),
+                   static_cast<int>(a0.w), static_cast<int>(a1.x), static_cast<int>(a1.y),
+                   static_cast<int>(a1.z), static_cast<int>(a1.w)};
+  const i32x8 b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
+                   static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
+                   static_cast<int>(b1.z), static_cast<int>(b1.w)};
+  // format 0 for both operands: OCP e4m3; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// e4m3 code -> its value (exact in fp32): normals (8 + m) 2^(e - 10), subnormals m 2^-9
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                      : static_cast<float>(m) * 0.001953125f;
+  return (code & 0x80u) ? -mag : mag;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -75,11 +109,14 @@ __device__ __forceinline__ float lanes_sum4(float x) {
   return __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
 }
 
-template <int DH>
+template <int DH, bool F8>
 __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   using C = AttnCfg<DH>;
+  using C8 = AttnF8Cfg<DH>;
   constexpr int QT = C::QT, NTHR = C::NTHR;
-  __shared__ __align__(16) uint16_t ks[2][C::KBUF];
+  __shared__ __align__(16) uint16_t ks[2][F8 ? 8 : C::KBUF];
+  __shared__ __align__(16) uint8_t ks8[2][F8 ? KT * C8::K8S : 16];
+  __shared__ __align__(16) float sks[2][F8 ? KT : 4];
   __shared__ __align__(16) uint16_t vs[2][C::KBUF];
 
   // logical block -> (canvas, KV head, key split, query block); the query blocks that share a
@@ -133,10 +170,57 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     qrow[q] = static_cast<long long>(b) * a.C + qi[q];
     win_lo[q] = len + qi[q] - a.window + 1;   // first visible cache position (windowed layers)
     const uint16_t* qp = a.qkv + qrow[q] * ldqkv + h[q] * DH;
+    if constexpr (!F8) {
 #pragma unroll
-    for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
-      const int d0 = ks_ * 32 + lg * 8;
-      qf[ks_][q] = (d0 < DH) ? ld16(qp + d0) : zero4;
+      for (int ks_ = 0; ks_ < C::NKS; ++ks_) {
+        const int d0 = ks_ * 32 + lg * 8;
+        qf[ks_][q] = (d0 < DH) ? ld16(qp + d0) : zero4;
+      }
+    }
+  }
+  // fp8: the query row's e4m3 codes with its scale amax / 448 (decided in binary32); lane
+  // (r16, lg) holds dh [128 kb + 32 lg, + 32) of its row for every 128-wide block kb, the k order
+  // of the K fragments too
+  u32x4 qf8[F8 ? C8::NKB : 1][QT][2];
+  float sq[QT];
+  if constexpr (F8) {
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const uint16_t* qp = a.qkv + qrow[q] * ldqkv + h[q] * DH;
+      u32x4 raw[C8::NKB][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C8::NKB; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          raw[kb][m] = ld16(qp + 128 * kb + 32 * lg + 8 * m);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[kb][m][w] << 16)),
+                                     fabsf(__uint_as_float(raw[kb][m][w] & 0xffff0000u))));
+        }
+      amax = lanes_max4(amax);
+      sq[q] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+      for (int kb = 0; kb < C8::NKB; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // 8 bf16 -> 8 codes (2 dwords) of the 32-byte fragment
+          uint32_t c[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            c[w] = f2e4m3(__uint_as_float(raw[kb][m][w] << 16) / sq[q]) |
+                   (f2e4m3(__uint_as_float(raw[kb][m][w] & 0xffff0000u) / sq[q]) << 8);
+          const uint32_t lo = c[0] | (c[1] << 16), hi = c[2] | (c[3] << 16);
+          u32x4& dst = qf8[kb][q][m >> 1];
+          if (m & 1) {
+            dst.z = lo;
+            dst.w = hi;
+          } else {
+            dst.x = lo;
+            dst.y = hi;
+          }
+        }
     }
   }
 
@@ -187,34 +271,111 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
     return reinterpret_cast<const uint16_t*>((pc & m) | (pn & ~m));
   };
-  constexpr bool PFULL = C::NPC % NTHR == 0;   // every thread has all its pieces
-  int p_key[C::PIT], p_off[C::PIT];            // piece -> key in the tile, offset in a row
+  constexpr int PIT = F8 ? C8::PIT : C::PIT;
+  constexpr int NPC = F8 ? C8::NPC : C::NPC;
+  constexpr int PCH = F8 ? C8::PCH : C::KCH;   // pieces per key row
+  constexpr bool PFULL = NPC % NTHR == 0;      // every thread has all its pieces
+  // piece -> key in the tile and its first dh (a piece is 16 bytes: 8 bf16, or 16 e4m3 codes)
+  int p_key[PIT], p_off[PIT];
 #pragma unroll
-  for (int it = 0; it < C::PIT; ++it) {
-    const int pc = min(tid + it * NTHR, C::NPC - 1);
-    p_key[it] = pc / C::KCH;
-    p_off[it] = (pc % C::KCH) * 8;
+  for (int it = 0; it < PIT; ++it) {
+    const int pc = min(tid + it * NTHR, NPC - 1);
+    p_key[it] = pc / PCH;
+    p_off[it] = (pc % PCH) * (F8 ? 16 : 8);
   }
-  u32x4 pk[C::PIT], pv[C::PIT];
+  // fp8: rows of e4m3 codes (cache, or the call's quantised canvas rows) and their scales
+  const uint8_t* kcache8 = reinterpret_cast<const uint8_t*>(a.kc) +
+                           (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap * DH;
+  const uint8_t* vcache8 = reinterpret_cast<const uint8_t*>(a.vc) +
+                           (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap * DH;
+  const float* kcs = a.ksc + (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap;
+  const float* vcs = a.vsc + (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap;
+  const long long cq0 = static_cast<long long>(b) * a.C * a.Hkv + g;   // canvas row (i = 0)
+  auto kv_row8 = [&](int kk, const uint8_t* cache, const uint8_t* canvas) -> const uint8_t* {
+    const int kc = min(kk, nk - 1);
+    const uintptr_t pc = reinterpret_cast<uintptr_t>(
+        cache + static_cast<long long>(c_lo + max(min(kc, nc - 1), 0)) * DH);
+    const uintptr_t pn = reinterpret_cast<uintptr_t>(
+        canvas + (cq0 + static_cast<long long>(max(kc - nc, 0)) * a.Hkv) * DH);
+    const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
+    return reinterpret_cast<const uint8_t*>((pc & m) | (pn & ~m));
+  };
+  auto row_scale = [&](int kk, const float* cache, const float* canvas) -> float {
+    const int kc = min(kk, nk - 1);
+    const uintptr_t pc = reinterpret_cast<uintptr_t>(cache + c_lo + max(min(kc, nc - 1), 0));
+    const uintptr_t pn = reinterpret_cast<uintptr_t>(
+        canvas + cq0 + static_cast<long long>(max(kc - nc, 0)) * a.Hkv);
+    const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
+    return *reinterpret_cast<const float*>((pc & m) | (pn & ~m));
+  };
+  u32x4 pk[PIT], pv[PIT];
+  float pvs[F8 ? PIT : 1];
+  float pks = 0.f;                             // fp8: thread t < KT stages key t's scale
   auto fetch_k = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < C::PIT; ++it)
-      pk[it] = ld16(kv_row(tt * KT + p_key[it], kcache, kcanvas) + p_off[it]);
+    for (int it = 0; it < PIT; ++it) {
+      if constexpr (F8)
+        pk[it] = ld16(kv_row8(tt * KT + p_key[it], kcache8, a.kq) + p_off[it]);
+      else
+        pk[it] = ld16(kv_row(tt * KT + p_key[it], kcache, kcanvas) + p_off[it]);
+    }
+    if constexpr (F8) {
+      if (tid < KT) pks = row_scale(tt * KT + tid, kcs, a.kqs);
+    }
   };
   auto fetch_v = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < C::PIT; ++it)
-      pv[it] = ld16(kv_row(tt * KT + p_key[it], vcache, vcanvas) + p_off[it]);
+    for (int it = 0; it < PIT; ++it) {
+      if constexpr (F8) {
+        pv[it] = ld16(kv_row8(tt * KT + p_key[it], vcache8, a.vq) + p_off[it]);
+        pvs[it] = row_scale(tt * KT + p_key[it], vcs, a.vqs);
+      } else {
+        pv[it] = ld16(kv_row(tt * KT + p_key[it], vcache, vcanvas) + p_off[it]);
+      }
+    }
   };
-  auto stage = [&](uint16_t* dst, const u32x4 (&pr)[C::PIT]) __attribute__((always_inline)) {
+  auto stage = [&](uint16_t* dst, const u32x4 (&pr)[PIT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < C::PIT; ++it) {
-      if (!PFULL && tid + it * NTHR >= C::NPC) continue;
+    for (int it = 0; it < PIT; ++it) {
+      if (!PFULL && tid + it * NTHR >= NPC) continue;
       st16(dst + p_key[it] * C::KS_STRIDE + p_off[it], pr[it]);
     }
   };
-  auto stage_k = [&](int buf) __attribute__((always_inline)) { stage(ks[buf], pk); };
-  auto stage_v = [&](int buf) __attribute__((always_inline)) { stage(vs[buf], pv); };
+  auto stage_k = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int it = 0; it < PIT; ++it) {
+        if (!PFULL && tid + it * NTHR >= NPC) continue;
+        st16(&ks8[buf][p_key[it] * C8::K8S + p_off[it]], pk[it]);
+      }
+      if (tid < KT) sks[buf][tid] = pks;
+    } else {
+      stage(ks[buf], pk);
+    }
+  };
+  auto stage_v = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      // 16 codes of one key row -> their values times the row scale, rounded to bf16
+#pragma unroll
+      for (int it = 0; it < PIT; ++it) {
+        if (!PFULL && tid + it * NTHR >= NPC) continue;
+        uint32_t w[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t x = pv[it][q4];
+          w[2 * q4] = cvt_pk_bf16(e4m3_to_f32(x & 0xffu) * pvs[it],
+                                  e4m3_to_f32((x >> 8) & 0xffu) * pvs[it]);
+          w[2 * q4 + 1] = cvt_pk_bf16(e4m3_to_f32((x >> 16) & 0xffu) * pvs[it],
+                                      e4m3_to_f32(x >> 24) * pvs[it]);
+        }
+        uint16_t* d = vs[buf] + p_key[it] * C::KS_STRIDE + p_off[it];
+        st16(d, u32x4{w[0], w[1], w[2], w[3]});
+        st16(d + 8, u32x4{w[4], w[5], w[6], w[7]});
+      }
+    } else {
+      stage(vs[buf], pv);
+    }
+  };
 
   const float sc = a.scale_log2e;
   if (t_beg < t_end) {
@@ -227,9 +388,18 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   // issued, so that all of them overlap): they stay in registers for the whole key range instead
   // of being re-loaded in every tile
 #pragma unroll
-  for (int q = 0; q < QT; ++q)
+  for (int q = 0; q < QT; ++q) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int ks_ = 0; ks_ < C::NKS; ++ks_) asm volatile("" : "+v"(qf[ks_][q]));
+      for (int kb = 0; kb < C8::NKB; ++kb) {
+        asm volatile("" : "+v"(qf8[kb][q][0]));
+        asm volatile("" : "+v"(qf8[kb][q][1]));
+      }
+    } else {
+#pragma unroll
+      for (int ks_ = 0; ks_ < C::NKS; ++ks_) asm volatile("" : "+v"(qf[ks_][q]));
+    }
+  }
   __syncthreads();
   // one key tile; STAGE: also stage tile tt + 1 into the other buffers.  Every tile but the last
   // stages, so the loop body is straight-line code (a branch around the staging would make the
@@ -245,31 +415,66 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     // S^T[key][q] for 4 sub-tiles of 16 keys and the wave's query tiles (raw dot products).  The
     // K fragments run ks-major through a ring read from LDS RING fragments ahead of use (pinned
     // by scheduling barriers); each fragment feeds the MFMAs of every query tile
-    constexpr int NS = 4 * C::NKS;
-    auto kfrag = [&](int i) -> u32x4 {
-      const int d0 = (i / 4) * 32 + lg * 8;
-      return (d0 < DH) ? ld16(ksb + ((i % 4) * 16 + r16) * C::KS_STRIDE + d0) : zero4;
-    };
     f32x4 s[QT][4];
 #pragma unroll
     for (int q = 0; q < QT; ++q)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) s[q][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KR = C::RING < NS ? C::RING : NS;
-    u32x4 kr[KR];
+    if constexpr (F8) {
+      // S^T on the 16x16x128 e4m3 MFMA: fragment i = (dh block i / 4, key sub-tile i % 4), 32
+      // bytes per lane from two 16-byte LDS reads; then each raw product is scaled by its key's
+      // row scale (the query's scale is folded into the softmax multiplier below)
+      constexpr int NS8 = 4 * C8::NKB;
+      const uint8_t* k8b = ks8[cur] + r16 * C8::K8S + 32 * lg;
+      u32x4 kr8[NS8][2];
 #pragma unroll
-    for (int i = 0; i < KR; ++i) kr[i] = kfrag(i);
-    // a wave in an MFMA loop takes issue priority over the wave sharing its SIMD, which is then
-    // left to its softmax (measured: 2% faster at head_dim 256)
-    __builtin_amdgcn_s_setprio(1);
+      for (int i = 0; i < NS8; ++i) {
+        const uint8_t* p = k8b + (i % 4) * 16 * C8::K8S + (i / 4) * 128;
+        kr8[i][0] = ld16(p);
+        kr8[i][1] = ld16(p + 16);
+      }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+      for (int i = 0; i < NS8; ++i)
 #pragma unroll
-      for (int q = 0; q < QT; ++q) s[q][i % 4] = mfma16x16x32(kr[i % KR], qf[i / 4][q], s[q][i % 4]);
-      if (i + KR < NS) kr[i % KR] = kfrag(i + KR);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < QT; ++q)
+          s[q][i % 4] = mfma_f8_128(kr8[i][0], kr8[i][1], qf8[i / 4][q][0], qf8[i / 4][q][1],
+                                    s[q][i % 4]);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float4 skv = *reinterpret_cast<const float4*>(&sks[cur][nt * 16 + 4 * lg]);
+#pragma unroll
+        for (int q = 0; q < QT; ++q) {
+          s[q][nt][0] *= skv.x;
+          s[q][nt][1] *= skv.y;
+          s[q][nt][2] *= skv.z;
+          s[q][nt][3] *= skv.w;
+        }
+      }
+    } else {
+      constexpr int NS = 4 * C::NKS;
+      auto kfrag = [&](int i) -> u32x4 {
+        const int d0 = (i / 4) * 32 + lg * 8;
+        return (d0 < DH) ? ld16(ksb + ((i % 4) * 16 + r16) * C::KS_STRIDE + d0) : zero4;
+      };
+      constexpr int KR = C::RING < NS ? C::RING : NS;
+      u32x4 kr[KR];
+#pragma unroll
+      for (int i = 0; i < KR; ++i) kr[i] = kfrag(i);
+      // a wave in an MFMA loop takes issue priority over the wave sharing its SIMD, which is
+      // then left to its softmax (measured: 2% faster at head_dim 256)
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int q = 0; q < QT; ++q)
+          s[q][i % 4] = mfma16x16x32(kr[i % KR], qf[i / 4][q], s[q][i % 4]);
+        if (i + KR < NS) kr[i % KR] = kfrag(i + KR);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
-    __builtin_amdgcn_s_setprio(0);
     if constexpr (STAGE) {
       stage_k(cur ^ 1);   // the other buffer was last read before the previous barrier
       fetch_v(tt + 1);
@@ -301,6 +506,9 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     u32x4 pb[QT][2];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
+      // fp8: the query row's scale joins the softmax multiplier (it is > 0, so the max commutes)
+      float scq = sc;
+      if constexpr (F8) scq = sc * sq[q];
       float tmax = -INFINITY;
       if (full) {
 #pragma unroll
@@ -325,7 +533,7 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       }
       tmax = lanes_max4(tmax);
       // running max in scaled (log2) units; the scale is > 0, so it commutes with the max
-      const float m_new = fmaxf(m_run[q], tmax * sc);
+      const float m_new = fmaxf(m_run[q], tmax * scq);
       const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[q] + neg_m);   // m_run = -inf: 0
       m_run[q] = m_new;
@@ -340,8 +548,8 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
         f32x4 lo, hi;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp][j], sc, neg_m));
-          hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp + 1][j], sc, neg_m));
+          lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp][j], scq, neg_m));
+          hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp + 1][j], scq, neg_m));
         }
         l_run[q] += (lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]);
         pb[q][kp] = u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
@@ -466,12 +674,50 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   *reinterpret_cast<uint2*>(op) = pk;
 }
 
-template <int DH>
+// e4m3 rows of the canvas keys and values: one wave per (token, KV head, K or V) row of dh <= 256
+// values, 4 per lane; scale amax / 448 and codes e4m3(x / s), decided in binary32
+__global__ __launch_bounds__(256) void k_kv_quant(AttnArgs a, uint8_t* kq, uint8_t* vq,
+                                                  float* kqs, float* vqs, uint8_t* kc,
+                                                  uint8_t* vc, float* ksc, float* vsc) {
+  const long long nrow = static_cast<long long>(a.B) * a.C * a.Hkv * 2;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrow) return;
+  const int lane = threadIdx.x & 63;
+  const int dh = a.dh;
+  const int kind = static_cast<int>(row & 1);          // 0: key, 1: value
+  const long long tg = row >> 1;                       // token * Hkv + g
+  const int g = static_cast<int>(tg % a.Hkv);
+  const long long t = tg / a.Hkv;
+  const uint16_t* src =
+      a.qkv + t * ((a.Hq + 2 * a.Hkv) * dh) + (a.Hq + kind * a.Hkv + g) * dh;
+  const int c = lane * 4;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < dh) {
+    const uint2 u = *reinterpret_cast<const uint2*>(src + c);
+    x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                    __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+  const float amax =
+      wave_max(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  const uint32_t codes = f2e4m3(x.x / sc) | (f2e4m3(x.y / sc) << 8) | (f2e4m3(x.z / sc) << 16) |
+                         (f2e4m3(x.w / sc) << 24);
+  if (c < dh) *reinterpret_cast<uint32_t*>((kind ? vq : kq) + tg * dh + c) = codes;
+  if (lane == 0) (kind ? vqs : kqs)[tg] = sc;
+  if (kc) {   // encoder pass: the row also goes into the cache at position len + i
+    const int b = static_cast<int>(t / a.C), i = static_cast<int>(t % a.C);
+    const long long crow = (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap + a.len[b] + i;
+    if (c < dh) *reinterpret_cast<uint32_t*>((kind ? vc : kc) + crow * dh + c) = codes;
+    if (lane == 0) (kind ? vsc : ksc)[crow] = sc;
+  }
+}
+
+template <int DH, bool F8>
 hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   const int R = (a.Hq / a.Hkv) * a.C;
   int grid = ((R + QB - 1) / QB) * a.Hkv * a.B * a.n_split;
   grid = (grid + 7) & ~7;
-  hipLaunchKernelGGL(k_attn<DH>, dim3(grid), dim3(AttnCfg<DH>::NTHR), 0, s, a);
+  hipLaunchKernelGGL((k_attn<DH, F8>), dim3(grid), dim3(AttnCfg<DH>::NTHR), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const long long n = static_cast<long long>(a.B) * a.Hkv * R * (DH / 4);
@@ -493,14 +739,31 @@ int attention_pick_split(int B, int C, int Hq, int Hkv, int max_keys) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.f8) {
+    switch (a.dh) {   // the e4m3 QK^T runs 128 dh per MFMA
+      case 128: return launch_dh<128, true>(a, s);
+      case 256: return launch_dh<256, true>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.dh) {
-    case 16: return launch_dh<16>(a, s);
-    case 32: return launch_dh<32>(a, s);
-    case 64: return launch_dh<64>(a, s);
-    case 128: return launch_dh<128>(a, s);
-    case 256: return launch_dh<256>(a, s);
+    case 16: return launch_dh<16, false>(a, s);
+    case 32: return launch_dh<32, false>(a, s);
+    case 64: return launch_dh<64, false>(a, s);
+    case 128: return launch_dh<128, false>(a, s);
+    case 256: return launch_dh<256, false>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_kv_quant(const AttnArgs& a, uint8_t* kq, uint8_t* vq, float* kqs, float* vqs,
+                           uint8_t* kc, uint8_t* vc, float* ksc, float* vsc, hipStream_t s) {
+  if (a.dh > 256 || a.dh % 4) return hipErrorInvalidValue;
+  const long long nrow = static_cast<long long>(a.B) * a.C * a.Hkv * 2;
+  if (nrow == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_kv_quant, dim3(static_cast<unsigned>((nrow + 3) / 4)), dim3(256), 0, s, a,
+                     kq, vq, kqs, vqs, kc, vc, ksc, vsc);
+  return hipGetLastError();
 }
 
 }  // namespace dg

@@ -555,10 +555,16 @@ hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
   return launch_stream<EPI_LMHEAD, 16, 128, 8, 4>(a, s);
 }
 
-hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, hipStream_t s) {
+// e4m3 expert products: 32-row tiles for a decoder step; 128-row tiles on 8 waves once a call
+// routes >= 1,024 tokens (a batch of 4 canvases: ~64 rows per expert), as for bf16 weights
+hipError_t launch_moe_gateup_fp8(const WGemmArgs& a, int tile_rows, hipStream_t s) {
+  if (tile_rows == 128) return launch_stream<EPI_SWIGLU, 8, 512, 8, 4, true>(a, s);
+  if (tile_rows != 32) return hipErrorInvalidValue;
   return launch_stream<EPI_SWIGLU, 2, 512, 4, 4, true>(a, s);
 }
-hipError_t launch_moe_down_fp8(const WGemmArgs& a, hipStream_t s) {
+hipError_t launch_moe_down_fp8(const WGemmArgs& a, int tile_rows, hipStream_t s) {
+  if (tile_rows == 128) return launch_stream<EPI_BF16, 8, 512, 8, 4, true>(a, s);
+  if (tile_rows != 32) return hipErrorInvalidValue;
   return launch_stream<EPI_BF16, 2, 512, 4, 4, true>(a, s);
 }
 hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s) {

@@ -226,26 +226,54 @@ class Model:
             pass
 
 
-class KVCache:
-    """Static KV cache: bf16 [n_layers][B][Hkv][cap][dh] K and V, host lengths."""
+def kv_is_fp8(dims):
+    return dims.get("kv_dtype", "bf16") in ("e4m3", "fp8")
 
-    def __init__(self, dims, batch, cap, device="cuda", k=None, v=None, lengths=None):
+
+class KVCache:
+    """Static KV cache [n_layers][B][Hkv][cap][dh] K and V with host lengths: bf16, or (dims
+    kv_dtype "e4m3") e4m3 codes (uint8) with fp32 row scales [n_layers][B][Hkv][cap]."""
+
+    def __init__(self, dims, batch, cap, device="cuda", k=None, v=None, lengths=None,
+                 k_scale=None, v_scale=None):
         shape = (dims["n_layers"], batch, dims["hkv"], cap, dims["dh"])
-        self.k = k if k is not None else torch.zeros(shape, dtype=torch.bfloat16, device=device)
-        self.v = v if v is not None else torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.fp8 = kv_is_fp8(dims)
+        dt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.k = k if k is not None else torch.zeros(shape, dtype=dt, device=device)
+        self.v = v if v is not None else torch.zeros(shape, dtype=dt, device=device)
         assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
+        assert self.k.dtype == dt and self.v.dtype == dt
+        if self.fp8:
+            sshape = shape[:-1]
+            self.k_scale = (k_scale if k_scale is not None else
+                            torch.ones(sshape, dtype=torch.float32, device=device))
+            self.v_scale = (v_scale if v_scale is not None else
+                            torch.ones(sshape, dtype=torch.float32, device=device))
+            assert tuple(self.k_scale.shape) == sshape and tuple(self.v_scale.shape) == sshape
+            assert self.k_scale.dtype == torch.float32 and self.v_scale.dtype == torch.float32
+        else:
+            self.k_scale = self.v_scale = None
         self.batch, self.cap = batch, cap
         self.len = (ctypes.c_int32 * batch)(*([0] * batch if lengths is None else
                                               [int(x) for x in lengths]))
 
     @classmethod
     def from_host(cls, dims, cache, cap, device="cuda"):
+        if kv_is_fp8(dims):
+            k, v = (torch.from_numpy(np.stack(cache[n])).to(device) for n in ("k", "v"))
+            ks, vs = (torch.from_numpy(np.stack(cache[n]).astype(np.float32)).to(device)
+                      for n in ("k_scale", "v_scale"))
+            return cls(dims, k.shape[1], cap, device, k, v, cache["len"], ks, vs)
         k = torch.from_numpy(np.stack(cache["k"])).to(device=device, dtype=torch.bfloat16)
         v = torch.from_numpy(np.stack(cache["v"])).to(device=device, dtype=torch.bfloat16)
         return cls(dims, k.shape[1], cap, device, k, v, cache["len"])
 
     def struct(self):
-        return _lib.dg_kv(ptr(self.k), ptr(self.v), self.batch, self.cap, self.len)
+        if self.fp8:
+            return _lib.dg_kv(ptr(self.k), ptr(self.v), self.batch, self.cap, self.len,
+                              _lib.DG_FP8_E4M3, ptr(self.k_scale), ptr(self.v_scale))
+        return _lib.dg_kv(ptr(self.k), ptr(self.v), self.batch, self.cap, self.len,
+                          _lib.DG_BF16, None, None)
 
     def lengths(self):
         return [self.len[i] for i in range(self.batch)]

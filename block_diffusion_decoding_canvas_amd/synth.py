@@ -102,6 +102,55 @@ def make_cache(dims, batch, cap, length, seed=1):
     return dict(k=ks, v=vs, len=np.full(batch, length, dtype=np.int64))
 
 
+# e4m3 cache rows are drawn as codes, not by quantising anything: the exponent field e (0..15)
+# with weight 2^(e - 14) up to 14 and 0.35 for the top binade, the 3 mantissa bits uniform (the
+# top binade stops at mantissa 6: code 0x7F is NaN), the sign uniform.  That puts most codes in
+# the upper binades, as in a row scaled so that its largest magnitude is 448.  Row scales are
+# log-uniform in [2/448, 4/448], so a row's values are of order 1.
+_E4M3_EXP_W = np.array([2.0 ** (e - 14) for e in range(15)] + [0.35])
+_E4M3_EXP_W = _E4M3_EXP_W / _E4M3_EXP_W.sum()
+
+
+def e4m3_codes(rng, shape):
+    """Random e4m3 codes (uint8, never NaN) with the distribution described above."""
+    e = rng.choice(16, size=shape, p=_E4M3_EXP_W)
+    m = rng.integers(0, 8, size=shape)
+    m = np.where(e == 15, np.minimum(m, 6), m)
+    sign = rng.integers(0, 2, size=shape)
+    return ((sign << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def row_scales(rng, shape):
+    return (np.exp(rng.uniform(np.log(2.0), np.log(4.0), size=shape)) / 448.0).astype(np.float32)
+
+
+def make_cache_fp8(dims, batch, cap, length, seed=1):
+    """Per-layer e4m3 K, V codes [B, Hkv, cap, dh] (uint8) and fp32 row scales [B, Hkv, cap]
+    in [0, length) (codes 0 and scale 1 after)."""
+    rng = np.random.default_rng(seed)
+    out = dict(k=[], v=[], k_scale=[], v_scale=[])
+    for _ in range(dims["n_layers"]):
+        for n in ("k", "v"):
+            c = np.zeros((batch, dims["hkv"], cap, dims["dh"]), dtype=np.uint8)
+            sc = np.ones((batch, dims["hkv"], cap), dtype=np.float32)
+            c[:, :, :length] = e4m3_codes(rng, (batch, dims["hkv"], length, dims["dh"]))
+            sc[:, :, :length] = row_scales(rng, (batch, dims["hkv"], length))
+            out[n].append(c)
+            out[n + "_scale"].append(sc)
+    out["len"] = np.full(batch, length, dtype=np.int64)
+    return out
+
+
+def empty_cache_fp8(dims, batch, cap):
+    shape = (batch, dims["hkv"], cap, dims["dh"])
+    out = {n: [np.zeros(shape, dtype=np.uint8) for _ in range(dims["n_layers"])]
+           for n in ("k", "v")}
+    for n in ("k_scale", "v_scale"):
+        out[n] = [np.ones(shape[:-1], dtype=np.float32) for _ in range(dims["n_layers"])]
+    out["len"] = np.zeros(batch, dtype=np.int64)
+    return out
+
+
 def empty_cache(dims, batch, cap):
     z = [np.zeros((batch, dims["hkv"], cap, dims["dh"]), dtype=np.float32)
          for _ in range(dims["n_layers"])]
@@ -186,6 +235,44 @@ def make_model_device(dims, device, seed=0, lm_std=WEIGHT_STD):
                 embed=normal((dims["V"], dims["d"]), WEIGHT_STD),
                 final_norm=torch.ones((dims["d"],), device=device, dtype=torch.bfloat16),
                 w_lm=normal((dims["V"], dims["d"]), lm_std))
+
+
+def make_cache_fp8_device(dims, batch, cap, length, device, seed=1, chunk=1 << 26):
+    """Timing-size e4m3 cache drawn on the device with a seeded torch generator: codes with the
+    distribution of e4m3_codes (exponent field by inverse CDF of a uniform draw), row scales
+    log-uniform in [2/448, 4/448], rows [0, length) of every canvas (codes 0, scale 1 after).
+    Returns (k, v, k_scale, v_scale)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    L, hkv, dh = dims["n_layers"], dims["hkv"], dims["dh"]
+    shape = (L, batch, hkv, cap, dh)
+    cdf = torch.tensor(np.cumsum(_E4M3_EXP_W), device=device, dtype=torch.float32)
+
+    def codes(n):
+        out = torch.empty(n, dtype=torch.uint8, device=device)
+        for o in range(0, n, chunk):
+            m = min(chunk, n - o)
+            u = torch.rand(m, device=device, generator=g)
+            e = torch.searchsorted(cdf, u, right=True).clamp_(max=15)
+            mant = torch.randint(0, 8, (m,), device=device, generator=g)
+            mant = torch.where(e == 15, mant.clamp(max=6), mant)
+            sign = torch.randint(0, 2, (m,), device=device, generator=g)
+            out[o:o + m] = ((sign << 7) | (e << 3) | mant).to(torch.uint8)
+        return out
+
+    res = []
+    for _ in range(2):
+        c = torch.zeros(shape, dtype=torch.uint8, device=device)
+        for l in range(L):
+            for b in range(batch):
+                c[l, b, :, :length] = codes(hkv * length * dh).view(hkv, length, dh)
+        res.append(c)
+    for _ in range(2):
+        sc = torch.ones(shape[:-1], dtype=torch.float32, device=device)
+        u = torch.rand((L, batch, hkv, length), device=device, generator=g)
+        sc[:, :, :, :length] = torch.exp(np.log(2.0) + u * np.log(2.0)) / 448.0
+        res.append(sc)
+    return tuple(res)
 
 
 def make_cache_device(dims, batch, cap, length, device, seed=1):

@@ -112,11 +112,21 @@ dg_status dg_model_create(const dg_dims* dims, const dg_layer_w* layers, const v
 void dg_model_destroy(dg_model* model);
 
 /* Static KV cache (diffusers docs, "Static cache and compilation").
- * k, v: bf16 [n_layers][batch][Hkv][cap][dh]; len: HOST array [batch] of valid lengths. */
+ * k, v: [n_layers][batch][Hkv][cap][dh] device rows; len: HOST array [batch] of valid lengths.
+ * dtype DG_BF16 (0, the default of a zero-filled struct): k, v hold bf16 and the scale pointers
+ * are ignored.  dtype DG_FP8_E4M3 (the FP8 configuration the model card quotes its speed in,
+ * read here for the cache too; head_dim 128 or 256 only): k, v hold one e4m3 code (byte) per
+ * element and k_scale, v_scale [n_layers][batch][Hkv][cap] the fp32 scale of each row (one
+ * token, one KV head), so a row reads as codes * scale.  Every canvas query, key and value row
+ * is quantised the same way (scale amax / 448, codes nearest-even with saturation, decided in
+ * binary32) before the attention, and an encoder pass stores its quantised key and value rows.
+ * All pointers are borrowed; the library never allocates or frees them. */
 typedef struct {
   void *k, *v;
   int32_t batch, cap;
   int32_t* len;
+  int32_t dtype;            /* DG_BF16 or DG_FP8_E4M3                                         */
+  float *k_scale, *v_scale; /* DG_FP8_E4M3: row scales (device); ignored for DG_BF16          */
 } dg_kv;
 
 /* Sampler constants; defaults are the model card's (Best Practices section 1). */

@@ -175,19 +175,25 @@ def quantize_dequantize_rows(x):
     return q * s[..., None]
 
 
-def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
+def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal, rows=None):
     """First half of a layer: h + O-projection of the joint attention over RMSNorm(h).
 
     h [B, C, d]; k_cache, v_cache [B, Hkv, cap, dh] (this layer); cache_len [B].
     Returns (h after attention, k [B, C, Hkv, dh], v) -- k, v are the canvas keys/values.
+    rows: only these canvas positions' outputs (h after attention is then [B, len(rows), d]);
+    every position still makes its key and value, and a query's output depends on its own row
+    and the keys and values only.
 
-    fp8 KV configuration (reading; the pages only quote FP8 speed): the QKV product is taken in
-    its bf16 storage form, and every query, key and value row of dh values (one token, one head)
-    is replaced by its per-row e4m3 quantisation (codes times fp32 scale) before the attention;
-    the cache holds such rows.  The returned k, v are the quantised canvas rows."""
+    fp8 KV configuration (reading; the pages only quote FP8 speed): the normed input and the QKV
+    product are taken in their bf16 storage forms, and every query, key and value row of dh
+    values (one token, one head) is replaced by its per-row e4m3 quantisation (codes times fp32
+    scale) before the attention; the cache holds such rows.  The returned k, v are the quantised
+    canvas rows."""
     eps = dims["eps"]
     bsz, clen, d = h.shape
     u = rms_norm(h, lw["attn_norm"], eps)
+    if kv_fp8(dims):
+        u = round_bf16(u)
     qkv = u @ lw["w_qkv"].T
     if kv_fp8(dims):
         qkv = round_bf16(qkv)
@@ -195,12 +201,14 @@ def attention_block(h, lw, dims, layer, k_cache, v_cache, cache_len, causal):
     if kv_fp8(dims):
         q, k, v = (quantize_dequantize_rows(x) for x in (q, k, v))
     window = 0 if layer_is_global(layer, dims) else dims["window"]
-    o = np.zeros_like(q)
+    rows = np.arange(clen) if rows is None else np.asarray(rows)
+    o = np.zeros((bsz, rows.shape[0]) + q.shape[2:])
     for b in range(bsz):
         n = int(cache_len[b])
-        mask = visible_cache_mask(n, clen, window)
-        o[b] = attention(q[b], k_cache[b, :, :n], v_cache[b, :, :n], k[b], v[b], mask, causal)
-    return h + o.reshape(bsz, clen, -1) @ lw["w_o"].T, k, v
+        mask = visible_cache_mask(n, clen, window)[rows]
+        o[b] = attention(q[b, rows], k_cache[b, :, :n], v_cache[b, :, :n], k[b], v[b], mask,
+                         causal, q_pos=rows)
+    return h[:, rows] + o.reshape(bsz, rows.shape[0], -1) @ lw["w_o"].T, k, v
 
 
 def ffn_block(h, lw, dims, force_idx=None):

@@ -312,3 +312,29 @@ def prefill_chain(dims, model, kv, ws, prompt, split, embed):
     assert c0 == prompt.shape[0]
     return ([np.concatenate(x)[None] for x in idx], [np.concatenate(x) for x in logits],
             np.concatenate(h_after0))
+
+
+def oracle_encode_forced(dims, mnp, prompt, cap, force, window_split=None):
+    """The oracle's encoding of the prompt into an empty cache (one pass, or the given split),
+    with the GPU's expert sets; returns (cache, routing infos per layer)."""
+    from block_diffusion_decoding_canvas_amd import synth
+    from oracle import model as om
+    m64 = synth.model_to_f64(mnp)
+    ref = synth.empty_cache(dims, 1, cap)
+    ref = dict(k=[a.astype(np.float64) for a in ref["k"]], v=[a.astype(np.float64) for a in ref["v"]],
+               len=np.array(ref["len"]))
+    n_all = prompt.shape[0]
+    infos = [None] * dims["n_layers"]
+    parts = window_split or (n_all,)
+    c0 = 0
+    for n in parts:
+        f = [x[:, c0:c0 + n] for x in force]
+        h = m64["embed"][prompt[None, c0:c0 + n]]
+        for layer, lw in enumerate(m64["layers"]):
+            h, _, _, info = om.layer_forward(h, lw, dims, layer, ref["k"][layer], ref["v"][layer],
+                                             ref["len"], causal=True, force_idx=f[layer])
+            infos[layer] = info if infos[layer] is None else {
+                key: np.concatenate([infos[layer][key], info[key]]) for key in info}
+        om.encoder_append(prompt[None, c0:c0 + n], m64, ref, force_idx=f)
+        c0 += n
+    return ref, infos

@@ -290,3 +290,36 @@ def test_generate_validates():
 def test_prof_classes_named():
     t = driver.KernelTimer()
     assert "moe_gateup" in t.names and "lmhead" in t.names and "attention" in t.names
+
+
+def test_fp8_kv_validation_before_launch():
+    """An e4m3 cache needs both scale arrays and head_dim 128 or 256; an unknown dtype is an
+    error; all before any HIP call."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    lens = (ctypes.c_int32 * 1)(60)
+    p = driver.eb_params(max_steps=8)
+    state = _lib.dg_eb_state(*([0x1000] * 7))
+    out = _lib.dg_step_out(0x1000, 0x1000, 0x1000, 0x1000)
+
+    def step(h, kv, ws):
+        return lib.dg_decoder_step(h, ctypes.byref(kv), 8, ctypes.byref(p), ctypes.byref(state),
+                                   ctypes.byref(out), fake, ws, None)
+
+    st, h = _create(_tiny_dims())                  # head_dim 16
+    assert st == 0
+    ws = lib.dg_workspace_bytes(h, 1)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens, _lib.DG_FP8_E4M3, 0x2000, 0x3000)
+    assert step(h, kv, ws) == 2                    # DG_ERR_SHAPE: fp8 cache at head_dim 16
+    assert b"head_dim" in lib.dg_last_error()
+    lib.dg_model_destroy(h)
+    st, h = _create(_tiny_dims(hq=2, hkv=1, dh=128))
+    assert st == 0
+    ws = lib.dg_workspace_bytes(h, 1)
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens, _lib.DG_FP8_E4M3, 0x2000, None)
+    assert step(h, kv, ws) == 1                    # DG_ERR_NULL: missing value scales
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens, 7, 0x2000, 0x3000)
+    assert step(h, kv, ws) == 2                    # unknown dtype
+    kv = _lib.dg_kv(0x1000, 0x1000, 1, 64, lens, _lib.DG_FP8_E4M3, 0x2000, 0x3000)
+    assert step(h, kv, ws) == 6                    # valid cache: the step index (8 of 8) fails
+    lib.dg_model_destroy(h)

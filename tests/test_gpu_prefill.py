@@ -32,7 +32,8 @@ import torch
 from block_diffusion_decoding_canvas_amd import driver, synth
 from block_diffusion_decoding_canvas_amd._lib import DgError
 from oracle import model as om
-from tests.parity_util import assert_close_rel, check_forced_routing, prefill_chain
+from tests.parity_util import (assert_close_rel, check_forced_routing, oracle_encode_forced,
+                               prefill_chain)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -46,30 +47,6 @@ def _append_split(model, kv, prompt, split, ws):
         driver.kv_append_tokens(model, kv, tok, ws)
         c0 += n
     assert c0 == prompt.shape[0]
-
-
-def _oracle_forced(dims, mnp, prompt, cap, force, window_split=None):
-    """The oracle's encoding of the prompt into an empty cache (one pass, or the given split),
-    with the GPU's expert sets; returns (cache, routing infos per layer)."""
-    m64 = synth.model_to_f64(mnp)
-    ref = synth.empty_cache(dims, 1, cap)
-    ref = dict(k=[a.astype(np.float64) for a in ref["k"]], v=[a.astype(np.float64) for a in ref["v"]],
-               len=np.array(ref["len"]))
-    n_all = prompt.shape[0]
-    infos = [None] * dims["n_layers"]
-    parts = window_split or (n_all,)
-    c0 = 0
-    for n in parts:
-        f = [x[:, c0:c0 + n] for x in force]
-        h = m64["embed"][prompt[None, c0:c0 + n]]
-        for layer, lw in enumerate(m64["layers"]):
-            h, _, _, info = om.layer_forward(h, lw, dims, layer, ref["k"][layer], ref["v"][layer],
-                                             ref["len"], causal=True, force_idx=f[layer])
-            infos[layer] = info if infos[layer] is None else {
-                key: np.concatenate([infos[layer][key], info[key]]) for key in info}
-        om.encoder_append(prompt[None, c0:c0 + n], m64, ref, force_idx=f)
-        c0 += n
-    return ref, infos
 
 
 def _check_prefill(dims, mnp, model, prompt, split, cap, window_split=None):
@@ -86,7 +63,7 @@ def _check_prefill(dims, mnp, model, prompt, split, cap, window_split=None):
     torch.cuda.synchronize()
     assert kv.lengths() == kv2.lengths() == [n]
     assert torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)
-    ref, infos = _oracle_forced(dims, mnp, prompt, cap, idx, window_split)
+    ref, infos = oracle_encode_forced(dims, mnp, prompt, cap, idx, window_split)
     swaps = [check_forced_routing(info["router_logits"], rl, ix, dims["top_k"], f"layer {l}")
              for l, (info, rl, ix) in enumerate(zip(infos, logits, idx))]
     print(f"  near-tie expert swaps per layer: {swaps}", flush=True)

@@ -184,8 +184,8 @@ def test_quantize_dequantize_rows_matches_torch():
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_kv_attention_block_is_sdpa_on_quantised_rows(causal):
     """The fp8 KV attention half-layer equals torch SDPA (GQA by repeated KV heads, with the
-    visibility mask) over the e4m3 quantise-dequantised rows of the bf16 QKV product, then the O
-    projection."""
+    visibility mask) over the e4m3 quantise-dequantised rows of the bf16 QKV product of the bf16
+    normed input, then the O projection."""
     from block_diffusion_decoding_canvas_amd import synth
     import torch.nn.functional as F
     dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=32, E=4, top_k=2, F=32, Fs=32, V=50, C=8,
@@ -200,7 +200,7 @@ def test_fp8_kv_attention_block_is_sdpa_on_quantised_rows(causal):
     vc = _torch_qdq(rng.standard_normal((1, 2, 16, 32)))
     out, k, v = om.attention_block(h, lw, dims, 0, kc, vc, np.array([n]), causal)
     u = F.rms_norm(torch.from_numpy(h[0]), (64,), weight=torch.from_numpy(lw["attn_norm"]),
-                   eps=1e-6)
+                   eps=1e-6).to(torch.bfloat16).double()
     qkv = (u @ torch.from_numpy(lw["w_qkv"]).T).to(torch.bfloat16).double().numpy()
     q = _torch_qdq(qkv[:, :128].reshape(C, 4, 32))
     kn = _torch_qdq(qkv[:, 128:192].reshape(C, 2, 32))

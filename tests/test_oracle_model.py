@@ -367,3 +367,23 @@ def test_fp8_head_matches_torch_float8_composition():
     ref = (codes @ _t(mq["w_lm"]).T) * s.to(torch.float64) * _t(mq["s_lm"])[None]
     assert np.allclose(z64[0], ref.numpy(), rtol=1e-10, atol=1e-12)
     assert np.array_equal(zr[0], ref.to(torch.bfloat16).to(torch.float64).numpy())
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_block_rows_are_the_full_blocks_rows(kv_dtype, causal):
+    """The attention half-layer restricted to some canvas positions gives those positions' rows
+    of the full half-layer (and the same canvas keys and values)."""
+    dims = dict(synth.dims_tiny(), window=6, global_every=2, kv_dtype=kv_dtype)
+    m = synth.model_to_f64(synth.make_model(dims, seed=21, norm_gain_std=0.1))
+    lw = m["layers"][0]
+    cache = synth.make_cache(dims, 2, 40, 30, seed=22)
+    kc, vc = cache["k"][0].astype(np.float64), cache["v"][0].astype(np.float64)
+    h = np.random.default_rng(23).standard_normal((2, dims["C"], dims["d"]))
+    lens = np.array([30, 17])
+    rows = np.array([0, 3, 4, 15])
+    full, k, v = om.attention_block(h, lw, dims, 0, kc, vc, lens, causal)
+    part, k2, v2 = om.attention_block(h, lw, dims, 0, kc, vc, lens, causal, rows=rows)
+    assert part.shape == (2, 4, dims["d"])
+    assert np.array_equal(k, k2) and np.array_equal(v, v2)
+    assert np.allclose(part, full[:, rows], rtol=1e-12, atol=1e-13)
