@@ -47,8 +47,8 @@ struct AttnCfg {
 };
 
 // fp8 KV cache: K tiles are e4m3 bytes in LDS (S^T = K Q^T on the 16x16x128 e4m3 MFMA, Q
-// quantised per query row in the prologue), V tiles are dequantised to bf16 as they are staged
-// (P V stays on the bf16 MFMA)
+// quantised per query row in the prologue), V tiles are converted to bf16 as they are staged
+// (exact) and P V stays on the bf16 MFMA, with the value row scales applied to P
 template <int DH>
 struct AttnF8Cfg {
   static constexpr int K8S = DH + 32;        // bytes per K row in LDS (stride / 16 = 2 mod 4)
@@ -70,14 +70,6 @@ __device__ __forceinline__ f32x4 mfma_f8_128(u32x4 a0, u32x4 a1, u32x4 b0, u32x4
                    static_cast<int>(b1.z), static_cast<int>(b1.w)};
   // format 0 for both operands: OCP e4m3; no block scales
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// e4m3 code -> its value (exact in fp32): normals (8 + m) 2^(e - 10), subnormals m 2^-9
-__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
-  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
-                      : static_cast<float>(m) * 0.001953125f;
-  return (code & 0x80u) ? -mag : mag;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -116,7 +108,8 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   constexpr int QT = C::QT, NTHR = C::NTHR;
   __shared__ __align__(16) uint16_t ks[2][F8 ? 8 : C::KBUF];
   __shared__ __align__(16) uint8_t ks8[2][F8 ? KT * C8::K8S : 16];
-  __shared__ __align__(16) float sks[2][F8 ? KT : 4];
+  __shared__ __align__(16) float sks[2][F8 ? KT : 4];   // fp8: key row scales of the tile
+  __shared__ __align__(16) float svs[2][F8 ? KT : 4];   // fp8: value row scales of the tile
   __shared__ __align__(16) uint16_t vs[2][C::KBUF];
 
   // logical block -> (canvas, KV head, key split, query block); the query blocks that share a
@@ -179,8 +172,9 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     }
   }
   // fp8: the query row's e4m3 codes with its scale amax / 448 (decided in binary32); lane
-  // (r16, lg) holds dh [128 kb + 32 lg, + 32) of its row for every 128-wide block kb, the k order
-  // of the K fragments too
+  // (r16, lg) holds dh 128 kb + 16 lg + [0, 16) and 128 kb + 64 + 16 lg + [0, 16) of its row for
+  // every 128-wide block kb (the MFMA only needs the K fragments in the same k order; this one
+  // makes each 16-byte K read a 16-byte lane stride, as in the bf16 kernel)
   u32x4 qf8[F8 ? C8::NKB : 1][QT][2];
   float sq[QT];
   if constexpr (F8) {
@@ -193,7 +187,7 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       for (int kb = 0; kb < C8::NKB; ++kb)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          raw[kb][m] = ld16(qp + 128 * kb + 32 * lg + 8 * m);
+          raw[kb][m] = ld16(qp + 128 * kb + (m >> 1) * 64 + 16 * lg + 8 * (m & 1));
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[kb][m][w] << 16)),
@@ -271,17 +265,27 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
     return reinterpret_cast<const uint16_t*>((pc & m) | (pn & ~m));
   };
+  // K pieces: 16 bytes of a key row (8 bf16, or 16 e4m3 codes).  V pieces: 8 values of a row (16
+  // bf16 bytes, or 8 e4m3 codes that become 16 bf16 bytes in LDS, so that consecutive lanes store
+  // consecutive 16-byte pieces either way)
   constexpr int PIT = F8 ? C8::PIT : C::PIT;
   constexpr int NPC = F8 ? C8::NPC : C::NPC;
-  constexpr int PCH = F8 ? C8::PCH : C::KCH;   // pieces per key row
-  constexpr bool PFULL = NPC % NTHR == 0;      // every thread has all its pieces
-  // piece -> key in the tile and its first dh (a piece is 16 bytes: 8 bf16, or 16 e4m3 codes)
-  int p_key[PIT], p_off[PIT];
+  constexpr int PCH = F8 ? C8::PCH : C::KCH;   // K pieces per key row
+  constexpr bool PFULL = NPC % NTHR == 0;      // every thread has all its K pieces
+  constexpr bool VFULL = C::NPC % NTHR == 0;   // ... and all its V pieces
+  // piece -> key in the tile and its first dh
+  int p_key[PIT], p_off[PIT], v_key[C::PIT], v_off[C::PIT];
 #pragma unroll
   for (int it = 0; it < PIT; ++it) {
     const int pc = min(tid + it * NTHR, NPC - 1);
     p_key[it] = pc / PCH;
     p_off[it] = (pc % PCH) * (F8 ? 16 : 8);
+  }
+#pragma unroll
+  for (int it = 0; it < C::PIT; ++it) {
+    const int pc = min(tid + it * NTHR, C::NPC - 1);
+    v_key[it] = pc / C::KCH;
+    v_off[it] = (pc % C::KCH) * 8;
   }
   // fp8: rows of e4m3 codes (cache, or the call's quantised canvas rows) and their scales
   const uint8_t* kcache8 = reinterpret_cast<const uint8_t*>(a.kc) +
@@ -308,9 +312,9 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
     const uintptr_t m = -static_cast<uintptr_t>(kc < nc);
     return *reinterpret_cast<const float*>((pc & m) | (pn & ~m));
   };
-  u32x4 pk[PIT], pv[PIT];
-  float pvs[F8 ? PIT : 1];
-  float pks = 0.f;                             // fp8: thread t < KT stages key t's scale
+  u32x4 pk[PIT], pv[C::PIT];
+  uint2 pv8[F8 ? C::PIT : 1];
+  float pks = 0.f, pvsc = 0.f;                 // fp8: thread t < KT stages key t's scales
   auto fetch_k = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < PIT; ++it) {
@@ -325,20 +329,23 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
   };
   auto fetch_v = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < PIT; ++it) {
-      if constexpr (F8) {
-        pv[it] = ld16(kv_row8(tt * KT + p_key[it], vcache8, a.vq) + p_off[it]);
-        pvs[it] = row_scale(tt * KT + p_key[it], vcs, a.vqs);
-      } else {
-        pv[it] = ld16(kv_row(tt * KT + p_key[it], vcache, vcanvas) + p_off[it]);
-      }
+    for (int it = 0; it < C::PIT; ++it) {
+      if constexpr (F8)
+        pv8[it] = *reinterpret_cast<const uint2*>(
+            kv_row8(tt * KT + v_key[it], vcache8, a.vq) + v_off[it]);
+      else
+        pv[it] = ld16(kv_row(tt * KT + v_key[it], vcache, vcanvas) + v_off[it]);
+    }
+    if constexpr (F8) {
+      if (tid < KT) pvsc = row_scale(tt * KT + tid, vcs, a.vqs);
     }
   };
-  auto stage = [&](uint16_t* dst, const u32x4 (&pr)[PIT]) __attribute__((always_inline)) {
+  auto stage = [&](uint16_t* dst, const u32x4 (&pr)[C::PIT], const int (&key)[C::PIT],
+                   const int (&off)[C::PIT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < PIT; ++it) {
-      if (!PFULL && tid + it * NTHR >= NPC) continue;
-      st16(dst + p_key[it] * C::KS_STRIDE + p_off[it], pr[it]);
+    for (int it = 0; it < C::PIT; ++it) {
+      if (!VFULL && tid + it * NTHR >= C::NPC) continue;
+      st16(dst + key[it] * C::KS_STRIDE + off[it], pr[it]);
     }
   };
   auto stage_k = [&](int buf) __attribute__((always_inline)) {
@@ -350,30 +357,30 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       }
       if (tid < KT) sks[buf][tid] = pks;
     } else {
-      stage(ks[buf], pk);
+      stage(ks[buf], pk, p_key, p_off);
     }
   };
   auto stage_v = [&](int buf) __attribute__((always_inline)) {
     if constexpr (F8) {
-      // 16 codes of one key row -> their values times the row scale, rounded to bf16
+      // 8 codes of one key row -> their values in bf16 (exact: an e4m3 value has 4 significant
+      // bits); the row's scale is applied to the probabilities instead
 #pragma unroll
-      for (int it = 0; it < PIT; ++it) {
-        if (!PFULL && tid + it * NTHR >= NPC) continue;
-        uint32_t w[8];
+      for (int it = 0; it < C::PIT; ++it) {
+        if (!VFULL && tid + it * NTHR >= C::NPC) continue;
+        uint32_t w[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t x = pv[it][q4];
-          w[2 * q4] = cvt_pk_bf16(e4m3_to_f32(x & 0xffu) * pvs[it],
-                                  e4m3_to_f32((x >> 8) & 0xffu) * pvs[it]);
-          w[2 * q4 + 1] = cvt_pk_bf16(e4m3_to_f32((x >> 16) & 0xffu) * pvs[it],
-                                      e4m3_to_f32(x >> 24) * pvs[it]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int x = static_cast<int>(h2 ? pv8[it].y : pv8[it].x);
+          w[2 * h2] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+          w[2 * h2 + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
         }
-        uint16_t* d = vs[buf] + p_key[it] * C::KS_STRIDE + p_off[it];
-        st16(d, u32x4{w[0], w[1], w[2], w[3]});
-        st16(d + 8, u32x4{w[4], w[5], w[6], w[7]});
+        st16(vs[buf] + v_key[it] * C::KS_STRIDE + v_off[it], u32x4{w[0], w[1], w[2], w[3]});
       }
+      if (tid < KT) svs[buf][tid] = pvsc;
     } else {
-      stage(vs[buf], pv);
+      stage(vs[buf], pv, v_key, v_off);
     }
   };
 
@@ -422,16 +429,17 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       for (int nt = 0; nt < 4; ++nt) s[q][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (F8) {
       // S^T on the 16x16x128 e4m3 MFMA: fragment i = (dh block i / 4, key sub-tile i % 4), 32
-      // bytes per lane from two 16-byte LDS reads; then each raw product is scaled by its key's
+      // bytes per lane from two 16-byte LDS reads (dh 16 lg + [0, 16) and 64 + 16 lg + [0, 16)
+      // of the block, the query fragments' order); then each raw product is scaled by its key's
       // row scale (the query's scale is folded into the softmax multiplier below)
       constexpr int NS8 = 4 * C8::NKB;
-      const uint8_t* k8b = ks8[cur] + r16 * C8::K8S + 32 * lg;
+      const uint8_t* k8b = ks8[cur] + r16 * C8::K8S + 16 * lg;
       u32x4 kr8[NS8][2];
 #pragma unroll
       for (int i = 0; i < NS8; ++i) {
         const uint8_t* p = k8b + (i % 4) * 16 * C8::K8S + (i / 4) * 128;
         kr8[i][0] = ld16(p);
-        kr8[i][1] = ld16(p + 16);
+        kr8[i][1] = ld16(p + 64);
       }
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -503,6 +511,13 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
         kbase + KT <= nk &&
         (in_cache ? (a.window == 0 || c_lo + kbase >= len + qi_hi - a.window + 1)
                   : (kbase >= nc && (!a.causal || kbase + KT - 1 - nc <= qi_lo)));
+    // fp8: the value row scales of this lane's keys (nt*16 + 4 lg + j), applied to P
+    float4 svk[4];
+    if constexpr (F8) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        svk[nt] = *reinterpret_cast<const float4*>(&svs[cur][nt * 16 + 4 * lg]);
+    }
     u32x4 pb[QT][2];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
@@ -552,6 +567,11 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
           hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][2 * kp + 1][j], scq, neg_m));
         }
         l_run[q] += (lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]);
+        if constexpr (F8) {
+          const float4 a0 = svk[2 * kp], a1 = svk[2 * kp + 1];
+          lo[0] *= a0.x; lo[1] *= a0.y; lo[2] *= a0.z; lo[3] *= a0.w;
+          hi[0] *= a1.x; hi[1] *= a1.y; hi[2] *= a1.z; hi[3] *= a1.w;
+        }
         pb[q][kp] = u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
                           cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])};
       }
