@@ -258,7 +258,7 @@ def measured_traffic():
     scaled by the copy-kernel yardstick), or None when the kernel sources no longer hash to the
     ones the counters were taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "moe_gateup_pmc_traffic.txt")
+    path = os.path.join(ROOT, "profiles", "decoder_step_pmc_traffic.txt")
     try:
         fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                       if ": " in line and not line.startswith(" "))
