@@ -204,20 +204,36 @@ typedef struct {
 size_t dg_workspace_bytes(const dg_model* model, int32_t batch);
 size_t dg_eb_workspace_bytes(int32_t batch, int32_t canvas_len, int32_t vocab);
 
-/* Initial canvases: uniform placeholder tokens (uniform corruption, no mask token), committed = 0,
- * stable_count = 0, done = 0.  C <= 1024. */
+/* Initial canvases (diffusers DiffusionGemmaPipeline docs, class text: the corruption is uniform
+ * over the vocabulary and there is no mask token): every position a Philox4x32-10 draw uniform
+ * over [0, vocab) from params->seed and the canvas's id, committed = 0, prev_argmax = 0,
+ * stable_count = 0, done = 0, dev_status = 0.  batch >= 1, 1 <= canvas_len <= 1024, vocab >= 1.
+ * Errors: DG_ERR_NULL (params, state or one of its pointers), DG_ERR_SHAPE (a size out of
+ * range). */
 dg_status dg_canvas_init(const dg_eb_params* params, dg_eb_state* state, int32_t batch,
                          int32_t canvas_len, int32_t vocab, void* stream);
 
-/* One denoising step at step index `step` (0 <= step < max_steps): decoder forward over the
- * canvases (bidirectional canvas attention joined with cross-attention to kv, routed + shared
- * MoE, LM head), then the EB sampler update of `state`.  Writes out->logits/entropy/argmax/
- * commit_now.  kv is read only; kv->len[b] + canvas_len <= kv->cap is not required here. */
+/* One denoising step at step index `step` (0 <= step < max_steps).  The decoder forward over the
+ * canvases (DiffusionGemma model card, "Model overview": bidirectional attention over the canvas
+ * joined with cross-attention to the cached context in kv, routed + shared MoE, the LM head),
+ * then the entropy-bound sampler update of `state` (model card, Best Practices section 1: the
+ * temperature schedule, the lowest-entropy selection under the bound, renoising of the rest and
+ * the adaptive stop; diffusers docs, "Schedulers" and "Adaptive stopping").  Writes
+ * out->logits/entropy/argmax/commit_now for every canvas that is not frozen; a frozen canvas
+ * (state->done) keeps its state.  kv is read only; kv->len[b] + canvas_len <= kv->cap is not
+ * required here.  Errors: DG_ERR_NULL, DG_ERR_SHAPE (kv batch outside [1, 64], an fp8 kv at an
+ * unsupported head_dim), DG_ERR_CAPACITY (kv->len[b] outside [0, cap]), DG_ERR_STATE (step or
+ * params out of range), DG_ERR_WORKSPACE (ws_bytes < dg_workspace_bytes(model, kv->batch)). */
 dg_status dg_decoder_step(const dg_model* model, const dg_kv* kv, int32_t step,
                           const dg_eb_params* params, dg_eb_state* state, dg_step_out* out,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* The EB sampler alone on given bf16 logits [B, C, V] (out->logits is ignored). */
+/* The entropy-bound sampler alone (DiffusionGemma model card, Best Practices section 1;
+ * diffusers docs, "Schedulers" (EntropyBoundScheduler) and "Adaptive stopping") on given bf16
+ * logits [B, C, V] row-major, which the decoder returns (diffusers docs, class text).  The same
+ * update as in dg_decoder_step; out->logits is ignored.  vocab a multiple of 256, canvas_len
+ * <= 1024.  Errors: DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_STATE (step or params out of range),
+ * DG_ERR_WORKSPACE (ws_bytes < dg_eb_workspace_bytes(batch, canvas_len, vocab)). */
 dg_status dg_eb_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len, int32_t vocab,
                        int32_t step, const dg_eb_params* params, dg_eb_state* state,
                        dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
@@ -261,9 +277,14 @@ dg_status dg_sample(const uint16_t* logits, int32_t batch, int32_t canvas_len, i
                     int32_t step, const dg_sched_params* params, dg_eb_state* state,
                     dg_step_out* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Encoder pass over finished canvases tokens [B, C] (causal inside the canvas, sees the cache);
- * every layer writes its keys/values at [len[b], len[b] + C).  On DG_OK the HOST array kv->len
- * is advanced by C immediately (the device writes are enqueued). */
+/* Append of finished canvases (DiffusionGemma model card, "Model overview": a finished canvas is
+ * processed by the encoder and appended to the KV cache before the next canvas starts; the
+ * encoder and decoder share their weights, diffusers docs, "PEFT adapters").  Encoder pass over
+ * tokens [B, C] int32 (causal inside the canvas, sees the cache); every layer writes its
+ * keys/values (an fp8 kv: their e4m3 rows and scales) at [len[b], len[b] + C).  On DG_OK the
+ * HOST array kv->len is advanced by C immediately (the device writes are enqueued).  Errors:
+ * DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_CAPACITY (len[b] + C > cap), DG_ERR_WORKSPACE
+ * (ws_bytes < dg_workspace_bytes(model, kv->batch)). */
 dg_status dg_kv_append_canvas(const dg_model* model, dg_kv* kv, const int32_t* tokens,
                               void* ws, size_t ws_bytes, void* stream);
 
