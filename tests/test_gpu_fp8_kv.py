@@ -236,3 +236,114 @@ def test_fp8_kv_full_size_layer(full_case, layer):
     inc_r = (h_out - h64[:, ROWS]).reshape(len(sel), -1)
     assert_close_rel(inc_g, inc_r, what=f"fp8 kv layer {layer} increment (sampled rows)")
     print(f"  sampled rows {len(sel)}, near-tie expert swaps {swaps}", flush=True)
+
+
+# --- the generation loop on an e4m3 cache -----------------------------------------------------
+def _fp8_toy(B):
+    """A 2-layer model with head_dim 128 and a sharp LM head (commits and adaptive stops within
+    a few steps) on an e4m3 cache that a chunked prefill fills with a 32-token prompt each."""
+    dims = dict(n_layers=2, d=64, hq=4, hkv=2, dh=128, E=8, top_k=2, F=128, Fs=128, V=512, C=16,
+                window=0, global_every=1, eps=1e-6, kv_dtype="e4m3")
+    mnp = synth.make_model(dims, seed=11, norm_gain_std=0.1, lm_std=1.0)
+    for lw in mnp["layers"]:
+        lw["w_qkv"] = lw["w_qkv"] * 4
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    prompt = np.stack([synth.prompt_ids(32, dims["V"], seed=20 + b) for b in range(B)])
+    kv = driver.KVCache(dims, B, 128, DEV)
+    ws = driver.workspace(model.append_workspace_bytes(B, 32))
+    driver.kv_append_tokens(model, kv, torch.tensor(prompt, dtype=torch.int32, device=DEV), ws)
+    torch.cuda.synchronize()
+    return dims, model, kv
+
+
+@pytest.mark.parametrize("kind", ["entropy_bound", "discrete_ddim"])
+def test_fp8_kv_generate_compacted_matches_uncompacted(kind):
+    """dg_generate on an e4m3 cache, with and without frozen-canvas compaction: tokens, canvases,
+    steps per canvas and the cache (codes and scales) bit for bit."""
+    B = 3
+    p = driver.sched_params(kind, max_steps=10, seed=9, temperature=0.7, corrector_steps=2,
+                            corrector_k=3)
+    res = []
+    for compact in (False, True):
+        dims, model, kv = _fp8_toy(B)
+        st = driver.SamplerState(B, dims["C"], DEV)
+        out = driver.StepOut(B, dims["C"], dims["V"], DEV)
+        print(f"fp8 kv generate {kind} compact={compact}", flush=True)
+        tokens, n, steps = driver.generate(model, kv, p, st, out, 3 * dims["C"],
+                                           compact_frozen=compact)
+        torch.cuda.synchronize()
+        res.append((tokens.cpu().numpy(), n, steps, kv.k.clone(), kv.v.clone(),
+                    kv.k_scale.clone(), kv.v_scale.clone(), kv.lengths()))
+    a, b = res
+    assert np.array_equal(a[0], b[0]) and a[1] == b[1] and a[2] == b[2]
+    for x, y in zip(a[3:7], b[3:7]):
+        assert torch.equal(x, y)
+    assert a[7] == b[7] == [32 + a[1] * 16] * B
+    print(f"  {a[1]} canvases, steps {a[2]}", flush=True)
+
+
+def test_fp8_kv_generate_matches_python_loop():
+    """dg_generate on an e4m3 cache against the same loop over the step calls (canvas init,
+    decoder steps until every canvas is done, the append), bit for bit."""
+    B = 2
+    dims, model, kv = _fp8_toy(B)
+    _, _, kv2 = _fp8_toy(B)
+    p = driver.eb_params(max_steps=8, seed=3)
+    st = driver.SamplerState(B, dims["C"], DEV)
+    out = driver.StepOut(B, dims["C"], dims["V"], DEV)
+    tok, n, steps = driver.generate(model, kv, p, st, out, 2 * dims["C"])
+    torch.cuda.synchronize()
+    ws = driver.workspace(model.workspace_bytes(B))
+    ref, ref_steps = [], []
+    for c in range(2):
+        s2 = driver.SamplerState(B, dims["C"], DEV, canvas_ids=[c * B + b for b in range(B)])
+        driver.canvas_init(p, s2, dims["V"])
+        k = 0
+        for s in range(8):
+            driver.decoder_step(model, kv2, s, p, s2, out, ws)
+            k += 1
+            if bool(s2.done.all()):
+                break
+        driver.kv_append_canvas(model, kv2, s2.canvas, ws)
+        ref.append(s2.canvas.cpu().numpy())
+        ref_steps.append(k)
+    torch.cuda.synchronize()
+    assert n == 2 and steps == ref_steps
+    assert np.array_equal(tok.cpu().numpy(), np.concatenate(ref, axis=1))
+    for x, y in ((kv.k, kv2.k), (kv.v, kv2.v), (kv.k_scale, kv2.k_scale), (kv.v_scale, kv2.v_scale)):
+        assert torch.equal(x, y)
+
+
+def test_fp8_kv_compacted_steps_bit_identical_with_staggered_freezes():
+    """dg_decoder_step_live over the live canvases only, on an e4m3 cache, against the full
+    step: state and live outputs bit for bit while the canvases freeze at different steps (a
+    loose entropy bound and adaptive stop make them freeze early)."""
+    B = 3
+    dims, model, kv = _fp8_toy(B)
+    C, V = dims["C"], dims["V"]
+    kv.len[1] = 20   # different visible cache lengths per canvas
+    kv.len[2] = 27
+    ws = driver.workspace(model.workspace_bytes(B))
+    p = driver.sched_params("entropy_bound", max_steps=16, seed=4, entropy_bound=4.0,
+                            stop_entropy=0.5)
+    full, comp = (driver.SamplerState(B, C, DEV, canvas_ids=[5, 1, 9]) for _ in range(2))
+    driver.canvas_init(driver.eb_params(seed=4), full, V)
+    driver.canvas_init(driver.eb_params(seed=4), comp, V)
+    of, oc = driver.StepOut(B, C, V, DEV), driver.StepOut(B, C, V, DEV)
+    staggered = False
+    for s in range(16):
+        live = [b for b in range(B) if not bool(comp.done[b])]
+        if not live:
+            break
+        staggered |= 0 < len(live) < B
+        print(f"fp8 kv compaction step {s}: live canvases {live}", flush=True)
+        driver.decoder_step_sched(model, kv, s, p, full, of, ws)
+        driver.decoder_step_live(model, kv, s, p, comp, oc, live, ws)
+        torch.cuda.synchronize()
+        hf, hc = full.host(), comp.host()
+        for k in hf:
+            assert np.array_equal(hf[k], hc[k]), k
+        for b in live:
+            assert torch.equal(of.logits[b], oc.logits[b])
+            assert torch.equal(of.entropy[b], oc.entropy[b])
+    assert staggered, "the canvases froze together: the workload does not stagger"
