@@ -347,3 +347,50 @@ def test_fp8_kv_compacted_steps_bit_identical_with_staggered_freezes():
             assert torch.equal(of.logits[b], oc.logits[b])
             assert torch.equal(of.entropy[b], oc.entropy[b])
     assert staggered, "the canvases froze together: the workload does not stagger"
+
+
+def test_fp8_kv_decoder_step_and_append_under_graph_capture():
+    """A decoder step and a canvas append on an e4m3 cache enqueue kernels only (the canvas rows'
+    quantiser included): each call captured in a HIP graph and replayed 3 times from the same
+    state, with eager work between the replays, reproduces the eager call bit for bit."""
+    from tests.test_gpu_graph import _check_replays
+    B = 2
+    dims, model, kv = _fp8_toy(B)
+    C, V = dims["C"], dims["V"]
+    ws = driver.workspace(model.workspace_bytes(B))
+    p = driver.eb_params(max_steps=8, seed=5)
+    st = driver.SamplerState(B, C, DEV)
+    driver.canvas_init(p, st, V)
+    out = driver.StepOut(B, C, V, DEV)
+    for s in (0, 5):
+        print(f"fp8 kv graph: decoder step {s}", flush=True)
+        _check_replays(lambda: driver.decoder_step(model, kv, s, p, st, out, ws), st, out,
+                       f"fp8 kv step {s}")
+    # the append: the cache rows it writes, replayed from the same lengths
+    tokens = st.canvas.clone()
+    n0 = kv.lengths()
+    eager = None
+    for r in range(4):
+        for b in range(B):
+            kv.len[b] = n0[b]
+        if r == 0:
+            driver.kv_append_canvas(model, kv, tokens, ws)
+            torch.cuda.synchronize()
+            eager = [t.clone() for t in (kv.k, kv.v, kv.k_scale, kv.v_scale)]
+            for t in (kv.k, kv.v):
+                t[:, :, :, n0[0]:].zero_()
+            continue
+        if r == 1:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                driver.kv_append_canvas(model, kv, tokens, ws)
+            for b in range(B):
+                kv.len[b] = n0[b]
+        for t in (kv.k, kv.v):
+            t[:, :, :, n0[0]:].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, e in zip((kv.k, kv.v, kv.k_scale, kv.v_scale), eager):
+            assert torch.equal(a, e), f"append replay {r}"
+    del g
