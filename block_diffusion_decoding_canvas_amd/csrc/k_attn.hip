@@ -10,10 +10,11 @@
 // times the canvas positions, so the K/V tiles staged in LDS serve every query head that reads
 // them.  Keys are processed in tiles of 64 (K and V tiles [key][dh] in LDS, double buffered: tile
 // t + 1 is staged while tile t is computed, one barrier per tile).
-// Up to head_dim 128 there are 4 waves (one per SIMD), each holding 32 query rows as two 16-row
-// MFMA tiles, so every K and V^T fragment read from LDS feeds two MFMAs; at head_dim 256 the
-// registers hold one 16-row tile per wave and there are 8 waves.  Each wave computes S^T = K Q^T, so the probabilities come out of the MFMA in the
-// lane layout that the P V product takes as its B operand (O^T = V^T P^T) with no shuffle.
+// Up to head_dim 128 (the generic kernel) there are 4 waves (one per SIMD), each holding 32 query
+// rows as two 16-row MFMA tiles, so every K and V^T fragment read from LDS feeds two MFMAs; each
+// wave computes S^T = K Q^T, so the probabilities come out of the MFMA in the lane layout that
+// the P V product takes as its B operand (O^T = V^T P^T) with no shuffle.  Head_dim 256 has a
+// kernel of its own (score waves and P V waves, below).
 // Staging loads are coalesced (consecutive lanes on consecutive 16-byte pieces of a key row) and
 // both tiles are stored row-major with 16-byte stores; the V^T fragments of the P V product come
 // from CDNA4's transposing LDS read, 8 keys of one dh per lane from two 8-byte reads.  LDS rows
@@ -32,7 +33,8 @@ constexpr int QB = 128;              // query rows per workgroup
 
 template <int DH>
 struct AttnCfg {
-  static constexpr int QT = DH >= 256 ? 1 : 2;  // 16-row query tiles per wave
+  static_assert(DH <= 128, "head_dim 256 runs the score / P V kernel");
+  static constexpr int QT = 2;                  // 16-row query tiles per wave
   static constexpr int NWAVE = QB / (16 * QT);  // waves per workgroup
   static constexpr int NTHR = NWAVE * 64;
   static constexpr int KS_STRIDE = DH + 16;  // bf16 per K or V row in LDS
@@ -470,8 +472,8 @@ __global__ __launch_bounds__(AttnCfg<DH>::NTHR) void k_attn(AttnArgs a) {
       u32x4 kr[KR];
 #pragma unroll
       for (int i = 0; i < KR; ++i) kr[i] = kfrag(i);
-      // a wave in an MFMA loop takes issue priority over the wave sharing its SIMD, which is
-      // then left to its softmax (measured: 2% faster at head_dim 256)
+      // a wave in an MFMA loop takes issue priority over a wave sharing its SIMD, which is then
+      // left to its softmax
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -732,6 +734,590 @@ __global__ __launch_bounds__(256) void k_kv_quant(AttnArgs a, uint8_t* kq, uint8
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// head_dim 256: score waves and P V waves.
+//
+// At head_dim 256 a wave cannot hold 32 query rows of S^T and their 32 x 256 O^T together, and
+// a wave of 16 rows feeds every K and V^T fragment it reads from LDS to a single MFMA.  Here the
+// two waves that share a SIMD (waves w and w + 4) take different roles:
+//   * waves 0-3 (score waves) compute S^T = K Q^T and the online softmax for 32 query rows each
+//     (each K fragment feeds two MFMAs) and write P (bf16) and the rescale factors to LDS;
+//   * waves 4-7 (P V waves) each own O^T for 64 of the 256 dh over all 128 query rows of the
+//     block (each V^T fragment feeds 8 MFMAs and each P fragment 4), one key tile behind, and
+//     stage the K and V tiles (the score waves' softmax is the longer chain).
+// While a score wave runs its softmax, the P V wave beside it keeps the SIMD's MFMA unit busy,
+// and the LDS bytes read per flop are 40% fewer than with every wave computing both products.
+// Keys go in tiles of 32 with one barrier per tile: in phase p the score waves take tile p and
+// the P V waves tile p - 1.  K, V and P are double buffered in LDS.  The staging loads of a tile
+// are spread over the P V MFMAs of one phase into one of two register sets and stored to LDS at
+// the end of the next phase.  The visible cached keys and the canvas keys are tiled separately,
+// so that the rows of a tile are equally spaced in one buffer: a uniform base and stride, and a
+// per-lane row clamped to the tile's last valid one.  P is stored in the key order of the B
+// operand that the transposing V^T reads pair with, so that one 16-byte LDS write and one
+// 16-byte read move a lane's 8 probabilities.  A row's reference maximum moves only when a tile
+// exceeds it by more than a factor 2^8, so the P V waves rarely rescale O (with 128 rows per
+// wave, some row gains a new maximum in almost every tile).
+constexpr int PP_KT = 32;                  // keys per tile
+constexpr int PP_DH = 256;
+constexpr int PP_NTHR = 512;               // 8 waves
+constexpr int PP_KS = PP_DH + 16;          // bf16 per K / V row in LDS (544 B, /16 = 2 mod 4)
+constexpr int PP_K8S = PP_DH + 32;         // bytes per e4m3 K row (288 B, /16 = 2 mod 4)
+constexpr int PP_PST = PP_KT + 16;         // bf16 per P row (96 B, /16 = 2 mod 4)
+constexpr float PP_LAZY = 8.f;             // rescale threshold of the running maximum (log2 units)
+
+template <bool F8>
+__global__ __launch_bounds__(PP_NTHR) void k_attn_pp(AttnArgs a) {
+  constexpr int DH = PP_DH, KTP = PP_KT, KSS = PP_KS;
+  constexpr int EB = F8 ? 1 : 2;           // bytes per cached K / V element
+  __shared__ __align__(16) uint16_t ks[2][F8 ? 8 : KTP * KSS];
+  __shared__ __align__(16) uint8_t ks8[2][F8 ? KTP * PP_K8S : 16];
+  __shared__ __align__(16) float sks[2][F8 ? KTP : 4];   // fp8: key row scales of the tile
+  __shared__ __align__(16) float svs[2][F8 ? KTP : 4];   // fp8: value row scales of the tile
+  __shared__ __align__(16) uint16_t vs[2][KTP * KSS];
+  __shared__ __align__(16) uint16_t ps[2][QB * PP_PST];  // P of the tile [query row][key slot]
+  __shared__ __align__(16) float al[2][16 * 8];          // rescale factors [r16][query tile]
+  __shared__ float lsum[QB];                             // final softmax sums
+
+  const int R = (a.Hq / a.Hkv) * a.C;
+  const int n_qblk = (R + QB - 1) / QB;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int qblk = L % n_qblk;
+  int rest = L / n_qblk;
+  const int split = rest % a.n_split;
+  rest /= a.n_split;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  if (b >= a.B) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int hpg = a.Hq / a.Hkv;
+  const int ldqkv = (a.Hq + 2 * a.Hkv) * DH;
+
+  const int len = a.len[b];
+  const int c_lo = a.window > 0 ? max(0, len - a.window + 1) : 0;
+  const int nc = len - c_lo;           // cache keys in the union of the visible ranges
+  const int nk = nc + a.C;             // + canvas keys
+  // tiles: ceil(nc / 32) of cached keys (from c_lo), then the canvas keys that some query of the
+  // block sees (causal: canvas keys past the block's last canvas position are masked for all of
+  // its queries); keys are numbered cache first (0 .. nc - 1), then canvas (nc .. nk - 1)
+  const int tcache = (nc + KTP - 1) / KTP;
+  int cv = a.C;
+  if (a.causal) {
+    const int r0 = qblk * QB, r1 = min(R, r0 + QB) - 1;
+    cv = ((r0 / a.C == r1 / a.C) ? r1 % a.C : a.C - 1) + 1;
+  }
+  const int ntiles = tcache + (cv + KTP - 1) / KTP;
+  const int per = (ntiles + a.n_split - 1) / a.n_split;
+  const int t_beg = min(ntiles, split * per);
+  const int t_end = min(ntiles, t_beg + per);
+  const int n = t_end - t_beg;         // tiles of this split (>= 0)
+  const float sc = a.scale_log2e;
+
+  if (wave >= 4) {
+    // ---------------- P V waves: staging, and O^T for dh 64 pw + [0, 64) of all 128 rows -----
+    const int pw = wave - 4, vt = tid - 256;
+    // staging by the 256 P V threads: K in pieces of 16 bytes (8 bf16 or 16 codes), V in pieces
+    // of 8 values (16 bf16 bytes, or 8 codes that become 16 bf16 bytes in LDS); threads 0-31 also
+    // stage the key's K and V scales (fp8)
+    constexpr int KPIT = F8 ? 2 : 4;
+    constexpr int KPR = DH * EB / 16;            // K pieces per key row
+    constexpr int VPR = DH / 8;                  // V pieces per key row
+    constexpr int VB = 8 * EB;                   // bytes per V piece in the cache
+    const long long cb = (static_cast<long long>(a.kvb[b]) * a.Hkv + g) * a.cap;
+    const uint8_t* kc_base = reinterpret_cast<const uint8_t*>(a.kc) + (cb + c_lo) * (DH * EB);
+    const uint8_t* vc_base = reinterpret_cast<const uint8_t*>(a.vc) + (cb + c_lo) * (DH * EB);
+    const long long cq0 = static_cast<long long>(b) * a.C * a.Hkv + g;   // fp8 canvas row (i = 0)
+    const uint8_t* kcan = F8 ? a.kq + cq0 * DH
+                             : reinterpret_cast<const uint8_t*>(a.qkv + static_cast<long long>(b) *
+                                                                a.C * ldqkv + (a.Hq + g) * DH);
+    const uint8_t* vcan = F8 ? a.vq + cq0 * DH
+                             : reinterpret_cast<const uint8_t*>(a.qkv + static_cast<long long>(b) *
+                                                                a.C * ldqkv + (a.Hq + a.Hkv + g) * DH);
+    const long long can_stride = F8 ? static_cast<long long>(a.Hkv) * DH : 2ll * ldqkv;   // bytes
+    int k_key[KPIT], v_key[4], k_col[KPIT], v_col[4];   // key in the tile, byte in the row
+#pragma unroll
+    for (int it = 0; it < KPIT; ++it) {
+      const int pc = vt + it * 256;
+      k_key[it] = pc / KPR;
+      k_col[it] = (pc % KPR) * 16;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int pc = vt + it * 256;
+      v_key[it] = pc / VPR;
+      v_col[it] = (pc % VPR) * VB;
+    }
+    // tile tt: first row address, row stride (bytes) and the last valid row of the tile (uniform);
+    // every staging load is unconditional: a key past the range reads the range's last key,
+    // finite data whose score is masked
+    struct TileRows {
+      const uint8_t* k;
+      const uint8_t* v;
+      long long stride;
+      int last;
+    };
+    auto tile_rows = [&](int tt) -> TileRows {
+      TileRows t;
+      if (tt < tcache) {
+        const long long r0 = static_cast<long long>(tt) * KTP;
+        t.k = kc_base + r0 * (DH * EB);
+        t.v = vc_base + r0 * (DH * EB);
+        t.stride = DH * EB;
+        t.last = nc - 1 - tt * KTP;
+      } else {
+        const long long r0 = static_cast<long long>(tt - tcache) * KTP;
+        t.k = kcan + r0 * can_stride;
+        t.v = vcan + r0 * can_stride;
+        t.stride = can_stride;
+        t.last = a.C - 1 - (tt - tcache) * KTP;
+      }
+      return t;
+    };
+    const float* ksc_base = F8 ? a.ksc + cb + c_lo : nullptr;
+    const float* vsc_base = F8 ? a.vsc + cb + c_lo : nullptr;
+
+    // two register sets, alternating by phase parity
+    u32x4 pk[2][KPIT];
+    u32x4 pv[2][F8 ? 1 : 4];
+    uint2 pv8[2][F8 ? 4 : 1];
+    float pks[2] = {0.f, 0.f}, pvs[2] = {0.f, 0.f};
+    // piece it of tile tt (rows t) into set S; K piece 0 also brings the fp8 scales
+    auto load_k = [&](const TileRows& t, int tt, int it, auto set_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      pk[S][it] = ld16(t.k + (static_cast<uint32_t>(min(k_key[it], t.last)) *
+                               static_cast<uint32_t>(t.stride) +
+                           static_cast<uint32_t>(k_col[it])));
+      if constexpr (F8) {
+        if (it != 0) return;
+        if (vt < KTP) {
+          const int rr = min(vt, t.last);
+          if (tt < tcache) {
+            pks[S] = ksc_base[tt * KTP + rr];
+            pvs[S] = vsc_base[tt * KTP + rr];
+          } else {
+            const long long ci = cq0 + static_cast<long long>((tt - tcache) * KTP + rr) * a.Hkv;
+            pks[S] = a.kqs[ci];
+            pvs[S] = a.vqs[ci];
+          }
+        }
+      }
+    };
+    auto load_v = [&](const TileRows& t, int it, auto set_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      const uint8_t* p = t.v + (static_cast<uint32_t>(min(v_key[it], t.last)) *
+                                    static_cast<uint32_t>(t.stride) +
+                                static_cast<uint32_t>(v_col[it]));
+      if constexpr (F8)
+        pv8[S][it] = *reinterpret_cast<const uint2*>(p);
+      else
+        pv[S][it] = ld16(p);
+    };
+    // the pieces of K of tile tk and V of tile tv into set S, all at once
+    auto fetch = [&](int tk, int tv, auto set_tag) __attribute__((always_inline)) {
+      const TileRows rk = tile_rows(tk), rv = tile_rows(tv);
+#pragma unroll
+      for (int it = 0; it < KPIT; ++it) load_k(rk, tk, it, set_tag);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) load_v(rv, it, set_tag);
+    };
+    auto store_k = [&](int buf, auto set_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+#pragma unroll
+      for (int it = 0; it < KPIT; ++it) {
+        const int col = k_col[it];
+        if constexpr (F8)
+          st16(&ks8[buf][k_key[it] * PP_K8S + col], pk[S][it]);
+        else
+          st16(reinterpret_cast<uint8_t*>(ks[buf]) + k_key[it] * (KSS * 2) + col, pk[S][it]);
+      }
+      if constexpr (F8) {
+        if (vt < KTP) {
+          sks[buf][vt] = pks[S];
+          svs[buf][vt] = pvs[S];
+        }
+      }
+    };
+    auto store_v = [&](int buf, auto set_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int col = v_col[it] / EB;   // element
+        if constexpr (F8) {
+          // 8 codes -> their bf16 values (exact); the row's scale goes onto P
+          uint32_t w[4];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int x = static_cast<int>(h2 ? pv8[S][it].y : pv8[S][it].x);
+            w[2 * h2] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+            w[2 * h2 + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+          }
+          st16(vs[buf] + v_key[it] * KSS + col, u32x4{w[0], w[1], w[2], w[3]});
+        } else {
+          st16(vs[buf] + v_key[it] * KSS + col, pv[S][it]);
+        }
+      }
+    };
+
+    f32x4 o[4][8];
+#pragma unroll
+    for (int dl = 0; dl < 4; ++dl)
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) o[dl][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    if (n > 0) {
+      fetch(t_beg, t_beg, J0{});
+      store_k(0, J0{});
+      fetch(min(t_beg + 1, t_end - 1), t_beg, J0{});
+    }
+    __syncthreads();   // the first K tile
+    const uint16_t* vlane0 = &vs[0][0] + (4 * lg + (r16 >> 2)) * KSS + 4 * (r16 & 3) + pw * 64;
+    const uint16_t* pl0 = &ps[0][0] + r16 * PP_PST + 8 * lg;
+    // phase i (parity P): P V of tile i - 1 with the pieces of K of tile i + 2 and V of tile i + 1
+    // loaded into set P ^ 1 spread over its MFMAs, then K of tile i + 1 and V of tile i (loaded in
+    // the phase before, set P) stored to LDS (clamped: the last phases re-stage valid tiles that
+    // are never read)
+    auto vphase = [&](int i, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      using NX = std::integral_constant<int, P ^ 1>;
+      const int fk = min(t_beg + i + 2, t_end - 1), fv = min(t_beg + i + 1, t_end - 1);
+      if (i == 0) {
+        if (n > 0) fetch(fk, fv, NX{});
+      } else {
+        const TileRows rk = tile_rows(fk), rv = tile_rows(fv);
+        const int prev = (i - 1) & 1;
+        // rescale by the factors of tile i - 1, per query tile (wave-uniform tests)
+        const float4 a0 = *reinterpret_cast<const float4*>(&al[prev][r16 * 8]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&al[prev][r16 * 8 + 4]);
+        const float alr[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int qt = 0; qt < 8; ++qt) {
+          if (__builtin_amdgcn_ballot_w64(alr[qt] != 1.f)) {
+#pragma unroll
+            for (int dl = 0; dl < 4; ++dl) o[dl][qt] *= alr[qt];
+          }
+        }
+        // V^T fragment of dh tile 4 pw + dl: lane (dh r16, group lg) gets keys 4 lg + [0, 4) and
+        // 16 + 4 lg + [0, 4); the P fragment of query tile qt holds the same keys in that order
+        const uint16_t* vlane = vlane0 + prev * (KTP * KSS);
+        u32x4 vf[4];
+#pragma unroll
+        for (int dl = 0; dl < 4; ++dl) {
+          const s16x4 lo = lds_read_tr16(vlane + dl * 16);
+          const s16x4 hi = lds_read_tr16(vlane + 16 * KSS + dl * 16);
+          vf[dl] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        const uint16_t* pl = pl0 + prev * (QB * PP_PST);
+        u32x4 pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[j] = ld16(pl + j * 16 * PP_PST);
+#pragma unroll
+        for (int qt = 0; qt < 8; ++qt) {
+#pragma unroll
+          for (int dl = 0; dl < 4; ++dl) o[dl][qt] = mfma16x16x32(vf[dl], pr[qt % 4], o[dl][qt]);
+          if (qt + 4 < 8) pr[qt % 4] = ld16(pl + (qt + 4) * 16 * PP_PST);
+          if (qt < KPIT) load_k(rk, fk, qt, NX{});
+          else if (qt < KPIT + 4) load_v(rv, qt - KPIT, NX{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (n > 0) {
+        store_k((i + 1) & 1, par);
+        store_v(i & 1, par);
+      }
+      __syncthreads();
+    };
+    int i = 0;
+    for (; i + 1 <= n; i += 2) {
+      vphase(i, J0{});
+      vphase(i + 1, J1{});
+    }
+    if (i <= n) vphase(i, J0{});
+    __syncthreads();   // the score waves' sums
+#pragma unroll
+    for (int qt = 0; qt < 8; ++qt) {
+      const int rr = qblk * QB + 16 * qt + r16;
+      if (rr >= R) continue;
+      const int qi = rr % a.C, h = g * hpg + rr / a.C;
+      const long long qrow = static_cast<long long>(b) * a.C + qi;
+      if (a.n_split == 1) {
+        const float lq = lsum[16 * qt + r16];
+        const float inv = lq > 0.f ? 1.f / lq : 0.f;
+        uint16_t* op = a.out + qrow * (a.Hq * DH) + h * DH + pw * 64;
+#pragma unroll
+        for (int dl = 0; dl < 4; ++dl) {
+          uint2 pk2;
+          pk2.x = pack_bf2(o[dl][qt][0] * inv, o[dl][qt][1] * inv);
+          pk2.y = pack_bf2(o[dl][qt][2] * inv, o[dl][qt][3] * inv);
+          *reinterpret_cast<uint2*>(op + dl * 16 + 4 * lg) = pk2;
+        }
+      } else {
+        const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + rr;
+        uint16_t* op = a.o_part + prow * DH + pw * 64;
+#pragma unroll
+        for (int dl = 0; dl < 4; ++dl) {
+          uint2 pk2;
+          pk2.x = pack_bf2(o[dl][qt][0], o[dl][qt][1]);
+          pk2.y = pack_bf2(o[dl][qt][2], o[dl][qt][3]);
+          *reinterpret_cast<uint2*>(op + dl * 16 + 4 * lg) = pk2;
+        }
+      }
+    }
+    return;
+  }
+
+  // ---------------- score waves: rows 32 sw + 16 q + r16 of the block -------------------------
+  const int sw = wave;
+  int r[2], qi[2], h[2], win_lo[2];
+  long long qrow[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    r[q] = qblk * QB + 32 * sw + 16 * q + r16;
+    const int rr = r[q] < R ? r[q] : R - 1;
+    qi[q] = rr % a.C;
+    h[q] = g * hpg + rr / a.C;
+    qrow[q] = static_cast<long long>(b) * a.C + qi[q];
+    win_lo[q] = len + qi[q] - a.window + 1;   // first visible cache position (windowed)
+  }
+  // query fragments: bf16 (dh 32 ks + 8 lg + [0, 8)), or e4m3 codes with the row scale (lane
+  // holds dh 128 kb + 16 lg + [0, 16) and 128 kb + 64 + 16 lg + [0, 16))
+  u32x4 qf[F8 ? 1 : 8][2];
+  u32x4 qf8[F8 ? 2 : 1][2][2];
+  float sq[2] = {1.f, 1.f};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint16_t* qp = a.qkv + qrow[q] * ldqkv + h[q] * DH;
+    if constexpr (!F8) {
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) qf[k2][q] = ld16(qp + k2 * 32 + lg * 8);
+    } else {
+      u32x4 raw[2][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          raw[kb][m] = ld16(qp + 128 * kb + (m >> 1) * 64 + 16 * lg + 8 * (m & 1));
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[kb][m][w] << 16)),
+                                     fabsf(__uint_as_float(raw[kb][m][w] & 0xffff0000u))));
+        }
+      amax = lanes_max4(amax);
+      sq[q] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          uint32_t c[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            c[w] = f2e4m3(__uint_as_float(raw[kb][m][w] << 16) / sq[q]) |
+                   (f2e4m3(__uint_as_float(raw[kb][m][w] & 0xffff0000u) / sq[q]) << 8);
+          const uint32_t lo = c[0] | (c[1] << 16), hi = c[2] | (c[3] << 16);
+          u32x4& dst = qf8[kb][q][m >> 1];
+          if (m & 1) {
+            dst.z = lo;
+            dst.w = hi;
+          } else {
+            dst.x = lo;
+            dst.y = hi;
+          }
+        }
+    }
+  }
+  // wave-uniform range of the wave's canvas positions (tiles every query sees entirely need no
+  // per-element mask)
+  int qi_lo = min(qi[0], qi[1]), qi_hi = max(qi[0], qi[1]);
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    qi_lo = min(qi_lo, __shfl_xor(qi_lo, o2, 64));
+    qi_hi = max(qi_hi, __shfl_xor(qi_hi, o2, 64));
+  }
+  qi_lo = __builtin_amdgcn_readfirstlane(qi_lo);
+  qi_hi = __builtin_amdgcn_readfirstlane(qi_hi);
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // the query fragments stay in registers for the whole key range
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        asm volatile("" : "+v"(qf8[kb][q][0]));
+        asm volatile("" : "+v"(qf8[kb][q][1]));
+      }
+    } else {
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) asm volatile("" : "+v"(qf[k2][q]));
+    }
+  }
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  __syncthreads();
+  // phase i (parity P = i & 1): scores and softmax of tile i from buffer P
+  auto phase = [&](int i, auto par) __attribute__((always_inline)) {
+    constexpr int cur = decltype(par)::value;
+    const int tt = t_beg + i;
+    const bool cache_tile = tt < tcache;
+    const int kbase = cache_tile ? tt * KTP : nc + (tt - tcache) * KTP;   // first key
+    const int klim = cache_tile ? nc : nk;                                 // keys >= klim: none
+    f32x4 s[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) s[q][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F8) {
+      // fragment j = (dh block j / 2, key sub-tile j % 2): 32 bytes per lane, two reads
+      const uint8_t* k8b = ks8[cur] + r16 * PP_K8S + 16 * lg;
+      u32x4 kr8[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* p = k8b + (j % 2) * 16 * PP_K8S + (j / 2) * 128;
+        kr8[j][0] = ld16(p);
+        kr8[j][1] = ld16(p + 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          s[q][j % 2] = mfma_f8_128(kr8[j][0], kr8[j][1], qf8[j / 2][q][0], qf8[j / 2][q][1],
+                                    s[q][j % 2]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float4 skv = *reinterpret_cast<const float4*>(&sks[cur][nt * 16 + 4 * lg]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          s[q][nt][0] *= skv.x;
+          s[q][nt][1] *= skv.y;
+          s[q][nt][2] *= skv.z;
+          s[q][nt][3] *= skv.w;
+        }
+      }
+    } else {
+      // 16 K fragments (dh step j / 2, key sub-tile j % 2) through a 4-deep register ring, each
+      // read 4 fragments (8 MFMAs) ahead of use; each feeds both query tiles
+      const uint16_t* kl = ks[cur] + r16 * KSS + lg * 8;
+      auto kfrag = [&](int j) -> u32x4 { return ld16(kl + (j % 2) * 16 * KSS + (j / 2) * 32); };
+      u32x4 kr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[j] = kfrag(j);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) s[q][j % 2] = mfma16x16x32(kr[j % 4], qf[j / 2][q], s[q][j % 2]);
+        if (j + 4 < 16) kr[j % 4] = kfrag(j + 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // visibility (the lane's keys: nt * 16 + 4 lg + j)
+    const bool full =
+        kbase + KTP <= klim &&
+        (cache_tile ? (a.window == 0 || c_lo + kbase >= len + qi_hi - a.window + 1)
+                    : (!a.causal || kbase + KTP - 1 - nc <= qi_lo));
+    float4 svk[2];
+    if constexpr (F8) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        svk[nt] = *reinterpret_cast<const float4*>(&svs[cur][nt * 16 + 4 * lg]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float scq = sc;
+      if constexpr (F8) scq = sc * sq[q];
+      float tmax = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(s[q][nt][0], s[q][nt][1]), fmaxf(s[q][nt][2], s[q][nt][3])));
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kk = kbase + nt * 16 + 4 * lg + j;
+            bool vis = kk < klim;
+            if (cache_tile) {
+              if (a.window > 0) vis = vis && (c_lo + kk >= win_lo[q]);
+            } else if (a.causal) {
+              vis = vis && (kk - nc <= qi[q]);
+            }
+            s[q][nt][j] = vis ? s[q][nt][j] : -INFINITY;
+            tmax = fmaxf(tmax, s[q][nt][j]);
+          }
+        }
+      }
+      tmax = lanes_max4(tmax);
+      // the row's reference maximum moves only when the tile's maximum exceeds it by more
+      // than PP_LAZY (log2 units), so the probabilities stay <= 2^PP_LAZY and the P V waves
+      // rescale O only at the first tiles of a row (a wave-uniform test per query tile)
+      const float t_m = tmax * scq;
+      const float m_new = (t_m > m_run[q] + PP_LAZY) ? t_m : m_run[q];
+      const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[q] + neg_m);   // m_run = -inf: 0
+      m_run[q] = m_new;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][0][j], scq, neg_m));
+        hi[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][1][j], scq, neg_m));
+      }
+      l_run[q] = l_run[q] * alpha +
+                 ((lo[0] + lo[1]) + (lo[2] + lo[3]) + (hi[0] + hi[1]) + (hi[2] + hi[3]));
+      if constexpr (F8) {
+        lo[0] *= svk[0].x; lo[1] *= svk[0].y; lo[2] *= svk[0].z; lo[3] *= svk[0].w;
+        hi[0] *= svk[1].x; hi[1] *= svk[1].y; hi[2] *= svk[1].z; hi[3] *= svk[1].w;
+      }
+      // keys 4 lg + [0, 4) and 16 + 4 lg + [0, 4) go to slots 8 lg + [0, 8) of the row
+      st16(&ps[cur][(32 * sw + 16 * q + r16) * PP_PST + 8 * lg],
+           u32x4{cvt_pk_bf16(lo[0], lo[1]), cvt_pk_bf16(lo[2], lo[3]),
+                 cvt_pk_bf16(hi[0], hi[1]), cvt_pk_bf16(hi[2], hi[3])});
+      if (lg == 0) al[cur][r16 * 8 + 2 * sw + q] = alpha;
+    }
+    __syncthreads();
+  };
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    phase(i, I0{});
+    phase(i + 1, I1{});
+  }
+  if (i < n) phase(i, I0{});
+  __syncthreads();   // the P V waves take the last tile
+  float l[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    l[q] = lanes_sum4(l_run[q]);
+    if (lg == 0) lsum[32 * sw + 16 * q + r16] = l[q];
+  }
+  if (a.n_split > 1) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (r[q] >= R || lg != 0) continue;
+      const long long prow = ((static_cast<long long>(split) * a.B + b) * a.Hkv + g) * R + r[q];
+      a.ml_part[prow * 2] = m_run[q];
+      a.ml_part[prow * 2 + 1] = l[q];
+    }
+  }
+  __syncthreads();
+}
+
+template <bool F8>
+hipError_t launch_pp(const AttnArgs& a, hipStream_t s) {
+  const int R = (a.Hq / a.Hkv) * a.C;
+  int grid = ((R + QB - 1) / QB) * a.Hkv * a.B * a.n_split;
+  grid = (grid + 7) & ~7;
+  hipLaunchKernelGGL(k_attn_pp<F8>, dim3(grid), dim3(PP_NTHR), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const long long n = static_cast<long long>(a.B) * a.Hkv * R * (PP_DH / 4);
+  hipLaunchKernelGGL(k_attn_merge<PP_DH>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
 template <int DH, bool F8>
 hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   const int R = (a.Hq / a.Hkv) * a.C;
@@ -762,7 +1348,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.f8) {
     switch (a.dh) {   // the e4m3 QK^T runs 128 dh per MFMA
       case 128: return launch_dh<128, true>(a, s);
-      case 256: return launch_dh<256, true>(a, s);
+      case 256: return launch_pp<true>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -771,7 +1357,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     case 32: return launch_dh<32, false>(a, s);
     case 64: return launch_dh<64, false>(a, s);
     case 128: return launch_dh<128, false>(a, s);
-    case 256: return launch_dh<256, false>(a, s);
+    case 256: return launch_pp<false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -19,11 +19,11 @@ Workloads:
   (300 + 724), against four canvas appends of 256 tokens (the path the decoder tests compare with
   the oracle). Layer 0's keys and values come from the embedding, the norm and the QKV product
   alone, whose per-row arithmetic does not depend on the split, so they must agree bit for bit.
-  Layer 1's depend on attention over a different key split and on the routing. Both runs carry
-  their own rounding (each about 0.4% from fp64), so they are compared per token row: the
-  relative norm of a row's difference must be within the tolerance for at least 95% of the rows
-  (the rest are routing near-ties, measured at about 2%: a token whose 8th and 9th expert logits
-  nearly tie may take a different expert in each run), and over all rows.
+  Layer 1's depend on attention over a different key split and on the routing: they are
+  compared at the stated tolerance on every token whose layer-0 expert set is the same in both
+  runs (the layer chains of both runs, which write the same caches bit for bit, give the sets);
+  at least 95% of the tokens must have the same set (the rest are router near-ties: a token
+  whose 8th and 9th expert logits nearly tie may take a different, equally valid expert).
 """
 import numpy as np
 import pytest
@@ -99,13 +99,40 @@ def _full_cache(dims, cap, length):
     return driver.KVCache(dims, 1, cap, DEV, kc, vc, [length])
 
 
+def _chain_sets(dims, model, kv, ws, prompt, split):
+    """The prefill of prompt into canvas 0 of kv, layer by layer through dg_layer_forward_tokens
+    (the kernels and launch shapes of dg_kv_append_tokens / dg_kv_append_canvas), returning the
+    layer-0 expert set of every token, sorted [n, k]."""
+    embed = model.weights["embed"]
+    k = dims["top_k"]
+    sets, c0 = [], 0
+    for n in split:
+        rows = torch.tensor(prompt[c0:c0 + n], dtype=torch.int64, device=DEV)
+        h = torch.index_select(embed, 0, rows).float()
+        for layer in range(dims["n_layers"]):
+            rl = torch.zeros((n, dims["E"]), dtype=torch.float32, device=DEV)
+            ti = torch.zeros((n, k), dtype=torch.int32, device=DEV)
+            driver.layer_forward_tokens(model, kv, layer, h, ws, rl, ti)
+            if layer == 0:
+                sets.append(np.sort(ti.cpu().numpy(), axis=1))
+        kv.len[0] += n
+        c0 += n
+    torch.cuda.synchronize()
+    return np.concatenate(sets)
+
+
 @pytest.mark.parametrize("split", [(1024,), (300, 724)])
 def test_prefill_full_width_chunk_invariance(full_width, split):
+    """The split prefill against four canvas appends.  Layer 0's keys and values must agree bit
+    for bit.  Layer 1's are compared on every token whose layer-0 expert set is the same in both
+    runs (a token whose 8th and 9th router logits nearly tie may take a different expert in each
+    run: a different but valid routing); those differ only by rounding."""
     dims, model = full_width
     length, n = 512, 1024
     cap = length + n
     prompt = synth.prompt_ids(n, dims["V"], seed=7)
     print(f"prefill case full width split {split}", flush=True)
+    canvas_split = (dims["C"],) * (n // dims["C"])
     ref = _full_cache(dims, cap, length)
     ws_c = driver.workspace(model.workspace_bytes(1))
     for c0 in range(0, n, dims["C"]):
@@ -116,20 +143,26 @@ def test_prefill_full_width_chunk_invariance(full_width, split):
     _append_split(model, got, prompt, split, ws)
     torch.cuda.synchronize()
     assert got.lengths() == ref.lengths() == [cap]
+    # the layer chains of both runs write the same caches as the entry points, with their expert
+    # sets
+    ref_c = _full_cache(dims, cap, length)
+    sets_ref = _chain_sets(dims, model, ref_c, ws, prompt, canvas_split)
+    got_c = _full_cache(dims, cap, length)
+    sets_got = _chain_sets(dims, model, got_c, ws, prompt, split)
+    assert torch.equal(ref_c.k, ref.k) and torch.equal(ref_c.v, ref.v)
+    assert torch.equal(got_c.k, got.k) and torch.equal(got_c.v, got.v)
+    same = (sets_ref == sets_got).all(axis=1)
+    print(f"  tokens with the same layer-0 expert set: {int(same.sum())} of {n}", flush=True)
+    assert same.mean() >= 0.95
     sl = slice(length, cap)
     for name in ("k", "v"):
         a = getattr(got, name)[0][0, :, sl]
         b = getattr(ref, name)[0][0, :, sl]
         assert torch.equal(a, b), f"layer 0 {name}: split {split} differs from canvas appends"
-        a = getattr(got, name)[1][0, :, sl].float().cpu().numpy()      # [Hkv, n, dh]
-        b = getattr(ref, name)[1][0, :, sl].float().cpu().numpy()
-        rel = np.linalg.norm(a - b) / np.linalg.norm(b)
-        assert rel <= REL, f"layer 1 {name}: relative norm {rel:.3g}"
-        da = (a - b).transpose(1, 0, 2).reshape(n, -1)
-        row_rel = np.linalg.norm(da, axis=1) / np.linalg.norm(b.transpose(1, 0, 2).reshape(n, -1),
-                                                               axis=1)
-        ok = row_rel <= REL
-        assert ok.mean() >= 0.95, f"layer 1 {name}: {int((~ok).sum())} of {n} token rows differ"
+        a = getattr(got, name)[1][0, :, sl].float().cpu().numpy().transpose(1, 0, 2)[same]
+        b = getattr(ref, name)[1][0, :, sl].float().cpu().numpy().transpose(1, 0, 2)[same]
+        assert_close_rel(a.reshape(a.shape[0], -1), b.reshape(b.shape[0], -1),
+                         what=f"layer 1 {name} split {split} (same expert sets)")
 
 
 def test_prefill_errors_leave_cache_untouched(full_width):
