@@ -6,7 +6,8 @@ several workgroups and merged), 4 query / 2 KV heads, and compares the layer's i
 residual stream with the oracle on every row (the oracle takes the GPU's expert set at
 router near-ties, checked for validity).  Modes: global
 bidirectional (the decoder), a 48-position sliding window (decoder, windowed layer), and causal
-canvas keys (the encoder pass that appends a finished canvas).
+canvas keys (the encoder pass that appends a finished canvas).  At head_dim 128 and 256 the
+same cases also run on a 20-entry cache (shorter than the window) and an empty one.
 """
 import numpy as np
 import pytest
@@ -23,6 +24,18 @@ DEV = "cuda"
 @pytest.mark.parametrize("mode", ["global", "window", "causal"])
 @pytest.mark.parametrize("dh", [16, 32, 64, 128, 256])
 def test_attention_head_dims(dh, mode):
+    _attention_case(dh, mode, (700, 333), 760)
+
+
+@pytest.mark.parametrize("mode", ["global", "window", "causal"])
+@pytest.mark.parametrize("dh", [128, 256])
+def test_attention_short_and_empty_cache(dh, mode):
+    """A 20-entry cache (shorter than the 48-position window, so the window starts at position
+    0) and an empty one (canvas keys only)."""
+    _attention_case(dh, mode, (20, 0), 64)
+
+
+def _attention_case(dh, mode, lens, cap):
     window = 48 if mode == "window" else 0
     causal = 1 if mode == "causal" else 0
     dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=dh, E=8, top_k=2, F=64, Fs=64, V=256, C=40,
@@ -31,7 +44,6 @@ def test_attention_head_dims(dh, mode):
     mnp = dict(dims=dims, layers=[synth.make_layer(dims, rng, norm_gain_std=0.1)],
                embed=np.zeros((256, 64), np.float32), final_norm=np.ones(64, np.float32),
                w_lm=np.zeros((256, 64), np.float32))
-    lens, cap = (700, 333), 760
     B = len(lens)
     cache = synth.make_cache(dims, B, cap, max(lens), seed=32)
     for b, n in enumerate(lens):
@@ -41,7 +53,7 @@ def test_attention_head_dims(dh, mode):
     cache["len"] = np.array(lens, dtype=np.int64)
     T = B * dims["C"]
     h = synth.hidden_states(T, 64, seed=33)
-    print(f"attention case dh={dh} mode={mode}", flush=True)
+    print(f"attention case dh={dh} mode={mode} lens={lens}", flush=True)
     model = driver.Model(synth.model_to_device(mnp, DEV))
     kv = driver.KVCache.from_host(dims, cache, cap, DEV)
     ws = driver.workspace(model.workspace_bytes(B))

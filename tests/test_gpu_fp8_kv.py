@@ -67,6 +67,17 @@ def compare_rows(kv, layer, ref_k, ref_v, rows, what, rel=REL_TOL, min_same=0.99
 @pytest.mark.parametrize("mode", ["global", "window", "causal"])
 @pytest.mark.parametrize("dh", [128, 256])
 def test_fp8_kv_layer(dh, mode):
+    _fp8_layer_case(dh, mode, (700, 333), 760)
+
+
+@pytest.mark.parametrize("mode", ["global", "window", "causal"])
+def test_fp8_kv_layer_short_and_empty_cache(mode):
+    """Head_dim 256 on a 20-entry cache (the 48-position window then starts at position 0) and
+    an empty one (canvas keys only)."""
+    _fp8_layer_case(256, mode, (20, 0), 64)
+
+
+def _fp8_layer_case(dh, mode, lens, cap):
     window = 48 if mode == "window" else 0
     causal = 1 if mode == "causal" else 0
     dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=dh, E=8, top_k=2, F=64, Fs=64, V=256, C=40,
@@ -76,13 +87,12 @@ def test_fp8_kv_layer(dh, mode):
                embed=np.zeros((256, 64), np.float32), final_norm=np.ones(64, np.float32),
                w_lm=np.zeros((256, 64), np.float32))
     mnp["layers"][0]["w_qkv"] = mnp["layers"][0]["w_qkv"] * 4    # score std about 2
-    lens, cap = (700, 333), 760
     B, C = len(lens), dims["C"]
     cache = synth.make_cache_fp8(dims, B, cap, max(lens), seed=42)
     cache["len"] = np.array(lens, dtype=np.int64)
     T = B * C
     h = synth.hidden_states(T, 64, seed=43)
-    print(f"fp8 kv case dh={dh} mode={mode}", flush=True)
+    print(f"fp8 kv case dh={dh} mode={mode} lens={lens}", flush=True)
     model = driver.Model(synth.model_to_device(mnp, DEV))
     kv = driver.KVCache.from_host(dims, cache, cap, DEV)
     ws = driver.workspace(model.workspace_bytes(B))
