@@ -116,7 +116,8 @@ def measured_peaks(driver, mib=1024, launches=5, mfma_iters=20000):
     return dict(hbm_read_gbs=round(n / t_read / 1e9, 1), hbm_copy_gbs=round(2.0 * n / t_copy / 1e9, 1),
                 mfma_bf16_tfs=round(mfma_flops / t_mfma / 1e12, 1),
                 note=("library kernels: read stream and copy on 1 GiB buffers (bytes moved / s), "
-                      "16x16x32 bf16 MFMA loop at 2 waves per SIMD"))
+                      "16x16x32 bf16 MFMA loop at 2 waves per SIMD; frac_of_measured in the "
+                      "roofline lines divides by the read stream (GB/s) or the MFMA loop"))
 
 
 def moe_gateup_bytes(dims, n_touched):
@@ -661,8 +662,13 @@ def main():
     if not (args.no_sampler or args.decoder_only):
         log("timing the standalone EB sampler")
         rooflines["eb_sampler"] = sampler_roofline(driver, timer, dev, dims["V"])
-        # context only: what the library's plain read stream, copy and MFMA loop reach here
+        # what the library's plain read stream and MFMA loop reach on this machine: each line's rate
+        # over that ceiling, beside its fraction of the nominal peak
         peaks = measured_peaks(driver)
+        for line_ in [roofline] + list(rooflines.values()):
+            ceiling = (peaks["hbm_read_gbs"] if line_.get("unit") == "GB/s"
+                       else peaks["mfma_bf16_tfs"])
+            line_["frac_of_measured"] = round(line_["achieved"] / ceiling, 4)
 
     long_fp8 = None
     if not (args.no_long_fp8 or args.decoder_only):

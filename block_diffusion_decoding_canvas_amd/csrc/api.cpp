@@ -582,7 +582,17 @@ dg_status dg_prof_reset(void) {
 namespace {
 
 constexpr int kRouterSplit = 8;   // k-splits of the router projection (summed by topk)
-constexpr int kOProjSplit = 4;    // k-splits of the attention output projection
+constexpr int kOProjSplit = 4;    // most k-splits of the attention output projection
+
+// k-splits of the output projection for calls of `tokens` rows: enough (up to 4) for the
+// 128-token x 128-row tiles to give one workgroup per compute unit.  Large calls (a batch of
+// canvases, a long prefill chunk) take fewer fp32 partial planes, which both the projection
+// writes and the residual kernel reads.  A compacted step passes the whole batch's token count,
+// so its rounding matches the full step's.
+int o_proj_split(int tokens, int d_model) {
+  const int tiles = (tokens + 127) / 128, nblk = (d_model + 127) / 128;
+  return std::max(1, std::min(kOProjSplit, (256 + tiles * nblk - 1) / (tiles * nblk)));
+}
 
 struct DecWs {
   float* h;           // [T][d] residual stream (fp32)
@@ -794,10 +804,11 @@ dg_status run_layer(const dg_model* m, const dg_kv* kv, int l, int C, bool causa
   g.hot = w.hot;
   g.X = w.attn; g.ldx = d.n_q_heads * d.head_dim; g.W = static_cast<const uint16_t*>(lw.w_o);
   g.K = g.K_sh = d.n_q_heads * d.head_dim; g.N = g.N_sh = d.d_model; g.ntok = T;
-  g.out = w.proj_part; g.ldo = d.d_model; g.ksplit = kOProjSplit;
+  const int o_split = o_proj_split(kv->batch * C, d.d_model);
+  g.out = w.proj_part; g.ldo = d.d_model; g.ksplit = o_split;
   g.split_stride = static_cast<long long>(T) * d.d_model;
   DG_LAUNCH(PC_GEMM_O, s, dg::launch_dense_packed_f32(g, s));
-  DG_LAUNCH(PC_RMSNORM, s, dg::launch_resid_norm(w.h, w.proj_part, kOProjSplit, T, d.d_model,
+  DG_LAUNCH(PC_RMSNORM, s, dg::launch_resid_norm(w.h, w.proj_part, o_split, T, d.d_model,
                                                  static_cast<const uint16_t*>(lw.ffn_norm), w.u,
                                                  d.norm_eps, w.u8, w.u8s, s));
   return run_ffn(m, l, T, w, next_gain, next_q8, trace_logits, trace_idx, trace_gates, s);

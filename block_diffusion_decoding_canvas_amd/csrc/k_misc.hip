@@ -30,9 +30,14 @@ __global__ __launch_bounds__(256) void k_copy(u32x4* __restrict__ dst,
 
 // the read stream: grid-stride with one streaming (nontemporal) 16-byte load per thread per
 // iteration; measured here, this plain form reads faster than per-wave contiguous sweeps or
-// several loads per thread in flight
-__global__ __launch_bounds__(256) void k_read_stream(const u32x4* __restrict__ src, size_t n16,
-                                                     uint32_t* out) {
+// several loads per thread in flight.  Each block leaves the XOR of its words in its own slot of
+// g_read_part, and one small block combines the slots: one atomic per block on a single word
+// had added ~50 us of serialised atomics to every call, which held the measured rate ~10% under
+// the kernels it is meant to bound.
+constexpr int kReadBlocks = 256 * 16;
+__device__ uint32_t g_read_part[kReadBlocks];
+
+__global__ __launch_bounds__(256) void k_read_stream(const u32x4* __restrict__ src, size_t n16) {
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   uint32_t x = 0;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
@@ -45,11 +50,20 @@ __global__ __launch_bounds__(256) void k_read_stream(const u32x4* __restrict__ s
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  // one atomic per block (XOR is order-independent, so the result is deterministic)
-  if (threadIdx.x == 0) atomicXor(out, red[0] ^ red[1] ^ red[2] ^ red[3]);
+  if (threadIdx.x == 0) g_read_part[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
-__global__ void k_zero_word(uint32_t* p) { *p = 0u; }
+// XOR of the first nblk block slots (0 when there are none) into *out
+__global__ __launch_bounds__(256) void k_read_combine(int nblk, uint32_t* out) {
+  uint32_t x = 0;
+  for (int i = threadIdx.x; i < nblk; i += blockDim.x) x ^= g_read_part[i];
+  __shared__ uint32_t red[4];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
 
 // every wave runs `iters` rounds of kChains independent 16x16x32 bf16 MFMAs (operands from the
 // lane id, so nothing folds away) and writes one sum per lane.  The MFMAs are written as
@@ -90,13 +104,13 @@ hipError_t launch_copy(void* dst, const void* src, size_t n, hipStream_t s) {
 }
 
 hipError_t launch_read_stream(const void* src, size_t n, uint32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, out);
   const size_t n16 = n / 16;
-  if (n16 == 0) return hipGetLastError();
   const size_t want = (n16 + 255) / 256;
-  const unsigned grid = static_cast<unsigned>(std::min<size_t>(want, 256 * 16));
-  hipLaunchKernelGGL(k_read_stream, dim3(grid), dim3(256), 0, s,
-                     static_cast<const u32x4*>(src), n16, out);
+  const int grid = static_cast<int>(std::min<size_t>(want, kReadBlocks));
+  if (grid > 0)
+    hipLaunchKernelGGL(k_read_stream, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(src),
+                       n16);
+  hipLaunchKernelGGL(k_read_combine, dim3(1), dim3(256), 0, s, grid, out);
   return hipGetLastError();
 }
 

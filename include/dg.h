@@ -414,7 +414,9 @@ dg_status dg_copy_bytes(void* dst, const void* src, size_t n, void* stream);
 /* Measured ceilings for the benchmark's roofline lines (measurement only, not part of the
  * decoding path).
  * dg_bench_read_stream: reads the n bytes at device `src` (n a multiple of 16) and writes the XOR
- *   of all its 32-bit words to the device word `xor_out`; the read rate of a plain stream.
+ *   of all its 32-bit words to the device word `xor_out`; the read rate of a plain stream.  The
+ *   per-block XORs pass through a library-owned device array, so calls on one GPU that overlap
+ *   in time race (the benchmark issues them on one stream).
  * dg_bench_mfma_loop: dg_bench_mfma_loop_blocks() workgroups of 4 waves, each wave `iters` rounds
  *   of 8 independent 16x16x32 bf16 MFMAs (2 * 16 * 16 * 32 flops each), one float per thread
  *   written to device `out` (blocks * 256 floats); the matrix-core rate the chip sustains.
