@@ -60,20 +60,6 @@ struct AttnF8Cfg {
   static constexpr int PIT = (NPC + AttnCfg<DH>::NTHR - 1) / AttnCfg<DH>::NTHR;
 };
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// one 16x16x128 e4m3 MFMA: A and B hold 32 bytes per lane in the same k order
-__device__ __forceinline__ f32x4 mfma_f8_128(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
-  const i32x8 a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z),
-                   static_cast<int>(a0.w), static_cast<int>(a1.x), static_cast<int>(a1.y),
-                   static_cast<int>(a1.z), static_cast<int>(a1.w)};
-  const i32x8 b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
-                   static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
-                   static_cast<int>(b1.z), static_cast<int>(b1.w)};
-  // format 0 for both operands: OCP e4m3; no block scales
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

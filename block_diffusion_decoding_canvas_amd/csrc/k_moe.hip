@@ -80,6 +80,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
   constexpr int SSTEPS = SEG / KSTEP;
   static_assert(SSTEPS % PS == 0 && XL >= 1 && MT * (SEGB / 16) % NTHR == 0,
                 "segment must hold whole ring groups");
+  static_assert(!F8 || PS % 2 == 0, "e4m3 steps go in pairs through the ring");
   __shared__ __align__(16) uint8_t xs_lds[2][MT * STRIDE];
 
   // logical slot -> (token tile, k split, row block).  Consecutive slots run on one XCD (one L2):
@@ -248,8 +249,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   const int nsteps = s_last - s_first;
-  // one step: the token fragments of step s from LDS, the MFMAs with ring stage q (zero weights
-  // when the step is past the end), then the ring stage refilled with step s + PS
+  // e4m3 operands go through the 16x16x128 MFMA, twice the rate of the 16x16x32 e4m3 form:
+  // steps s and s + 1 (64 k each) make one MFMA.  A lane's 32 bytes are its 16 bytes of step s
+  // then its 16 of step s + 1, for the weights (two ring stages) and the tokens (two LDS reads)
+  // alike, so both operands list the same 128 k in the same order.  A pair always starts at an
+  // even step from the split's first, so every tile shape sums the same pairs in the same order.
+  // step_pair: the MFMAs with ring stages q, q + 1 (zero weights for a step past the end), then
+  // both stages refilled with steps s + PS and s + 1 + PS
+  auto step_pair = [&](const uint8_t* xb, int s, int s_beg, int q, bool live0, bool live1)
+      __attribute__((always_inline)) {
+    const int kin0 = (s - s_beg) * 64 + g * 16;
+    const int kin1 = live1 ? kin0 + 64 : kin0;   // past the end: any staged bytes (zero weights)
+    u32x4 w0[RT], w1[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      w0[rt] = live0 ? wst[q][rt] : zero4;
+      w1[rt] = live1 ? wst[q + 1][rt] : zero4;
+    }
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const uint8_t* xr = xb + (tb * 16 + r16) * STRIDE;
+      const u32x4 b0 = ld16(xr + kin0), b1 = ld16(xr + kin1);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][tb] = mfma_f8_128(w0[rt], w1[rt], b0, b1, acc[rt][tb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(s + PS, wst[q]);
+    load_step(s + 1 + PS, wst[q + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // one step (bf16): the token fragments of step s from LDS, the MFMAs with ring stage q (zero
+  // weights when the step is past the end), then the ring stage refilled with step s + PS
   auto step = [&](const uint8_t* xb, int s, int s_beg, int q, bool live)
       __attribute__((always_inline)) {
     const int kin = (s - s_beg) * 64 + g * 16;   // byte offset in the staged row
@@ -258,12 +288,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
     for (int rt = 0; rt < RT; ++rt) wv[rt] = live ? wst[q][rt] : zero4;
     auto mma = [&](const u32x4& bt, int tb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if constexpr (F8)
-          acc[rt][tb] = mfma_fp8_pair(wv[rt], bt, acc[rt][tb]);
-        else
-          acc[rt][tb] = mfma16x16x32(wv[rt], bt, acc[rt][tb]);
-      }
+      for (int rt = 0; rt < RT; ++rt) acc[rt][tb] = mfma16x16x32(wv[rt], bt, acc[rt][tb]);
     };
     if constexpr (NTB <= 4) {
       u32x4 b[NTB];
@@ -311,9 +336,52 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       // grouped expert products (2 token blocks, several waves per SIMD) keep their registers
       // for occupancy instead
       if constexpr (NTB < 4) {
+        if constexpr (F8) {
 #pragma unroll
-        for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
+          for (int u = 0; u < SSTEPS; u += 2) step_pair(xb, s_beg + u, s_beg, u % PS, true, true);
+        } else {
+#pragma unroll
+          for (int u = 0; u < SSTEPS; ++u) step(xb, s_beg + u, s_beg, u % PS, true);
+        }
         next_seg(sg);
+      } else if constexpr (F8) {
+        // as below, over pairs of steps: pair fragment f = pair p * NTB + block tb, each two LDS
+        // reads (steps 2p and 2p + 1) through a D-deep ring (2 deep: a pair fragment feeds RT
+        // MFMAs of 4x the work, and a deeper ring spills the 8-wave tiles)
+        constexpr int NF = SSTEPS / 2 * NTB;
+        constexpr int D = NF < 2 ? NF : 2;
+        static_assert(NF % XL == 0, "token pieces must spread evenly over the fragments");
+        constexpr int EVERY = NF / XL;
+        const uint8_t* xf = xb + r16 * STRIDE + g * 16;
+        u32x4 br0[D], br1[D];
+        auto read = [&](int f, int slot) __attribute__((always_inline)) {
+          const uint8_t* p = xf + (f % NTB) * 16 * STRIDE + (f / NTB) * 128;
+          br0[slot] = ld16(p);
+          br1[slot] = ld16(p + 64);
+        };
+#pragma unroll
+        for (int i = 0; i < D; ++i) read(i, i);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int u = 2 * (f / NTB), tb = f % NTB;
+          const u32x4 b0 = br0[f % D], b1 = br1[f % D];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            acc[rt][tb] = mfma_f8_128(wst[u % PS][rt], wst[(u + 1) % PS][rt], b0, b1, acc[rt][tb]);
+          if (f + D < NF) read(f + D, f % D);
+          __builtin_amdgcn_sched_barrier(0);
+          if (tb == NTB - 1) {
+            // the pair's last MFMAs have read its two ring stages: refill them
+            load_step(s_beg + u + PS, wst[u % PS]);
+            load_step(s_beg + u + 1 + PS, wst[(u + 1) % PS]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (f % EVERY == EVERY - 1) {
+            store_piece(f / EVERY, sg + 1);
+            load_piece(f / EVERY, sg + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       } else {
         constexpr int NF = SSTEPS * NTB;
         constexpr int D = NF < (NTB == 4 ? 8 : 4) ? NF : (NTB == 4 ? 8 : 4);
@@ -328,12 +396,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
           const int u = f / NTB, tb = f % NTB;
           const u32x4 bt = br[f % D];
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            if constexpr (F8)
-              acc[rt][tb] = mfma_fp8_pair(wst[u % PS][rt], bt, acc[rt][tb]);
-            else
-              acc[rt][tb] = mfma16x16x32(wst[u % PS][rt], bt, acc[rt][tb]);
-          }
+          for (int rt = 0; rt < RT; ++rt)
+            acc[rt][tb] = mfma16x16x32(wst[u % PS][rt], bt, acc[rt][tb]);
           if (f + D < NF)
             br[f % D] = ld16(xf + ((f + D) % NTB) * 16 * STRIDE + ((f + D) / NTB) * 64);
           __builtin_amdgcn_sched_barrier(0);
@@ -356,8 +420,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_stream(WGemmArgs a) {
       // barriers)
       const int s_end = wave_live ? min(nsteps, s_beg + SSTEPS) : s_beg;
       for (int s0 = s_beg; s0 < s_end; s0 += PS) {
+        if constexpr (F8) {
 #pragma unroll
-        for (int q = 0; q < PS; ++q) step(xb, s0 + q, s_beg, q, s0 + q < s_end);
+          for (int q = 0; q < PS; q += 2)
+            step_pair(xb, s0 + q, s_beg, q, s0 + q < s_end, s0 + q + 1 < s_end);
+        } else {
+#pragma unroll
+          for (int q = 0; q < PS; ++q) step(xb, s0 + q, s_beg, q, s0 + q < s_end);
+        }
       }
       next_seg(sg);
     }
