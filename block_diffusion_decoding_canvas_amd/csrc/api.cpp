@@ -584,11 +584,12 @@ namespace {
 constexpr int kRouterSplit = 8;   // k-splits of the router projection (summed by topk)
 constexpr int kOProjSplit = 4;    // most k-splits of the attention output projection
 
-// k-splits of the output projection for calls of `tokens` rows: enough (up to 4) for the
-// 128-token x 128-row tiles to give one workgroup per compute unit.  Large calls (a batch of
-// canvases, a long prefill chunk) take fewer fp32 partial planes, which both the projection
-// writes and the residual kernel reads.  A compacted step passes the whole batch's token count,
-// so its rounding matches the full step's.
+// k-splits of the output projection for calls of `tokens` rows: enough (up to 4) for units of
+// 128 tokens x 128 output rows to cover every compute unit once (calls of >= 1,024 tokens run
+// two such units per 8-wave workgroup).  Large calls (a batch of canvases, a long prefill
+// chunk) take fewer fp32 partial planes, which both the projection writes and the residual
+// kernel reads.  A compacted step passes the whole batch's token count, so its rounding matches
+// the full step's.
 int o_proj_split(int tokens, int d_model) {
   const int tiles = (tokens + 127) / 128, nblk = (d_model + 127) / 128;
   return std::max(1, std::min(kOProjSplit, (256 + tiles * nblk - 1) / (tiles * nblk)));

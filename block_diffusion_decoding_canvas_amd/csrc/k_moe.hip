@@ -612,13 +612,16 @@ hipError_t launch_moe_down(const WGemmArgs& a, int tile_rows, hipStream_t s) {
   // 3 waves per SIMD on the decoder shape)
   return launch_stream<EPI_BF16, 2, 256, 4, 2, false, 4>(a, s);
 }
+// Calls of >= 1,024 tokens (long prefill chunks, batches of four canvases): 128-token tiles halve
+// the weight re-reads (183 -> ~160 us per layer at 2,048 tokens), on 8 waves of 32 rows, so a
+// CU keeps twice the fragments in flight (8,192-token prefill 101.0 -> 94.6 ms, long-context
+// bench step 1,234 -> 1,212 ms against 4 waves, A/B on one box)
 hipError_t launch_dense_packed_bf16(const WGemmArgs& a, hipStream_t s) {
-  // long prefill chunks: 128-token tiles halve the weight re-reads (183 -> ~160 us per layer
-  // at 2,048 tokens)
-  if (a.ntok >= kMoeWideTokens) return launch_stream<EPI_BF16, 8, 256, 4, 4>(a, s);
+  if (a.ntok >= kMoeWideTokens) return launch_stream<EPI_BF16, 8, 256, 8, 4>(a, s);
   return launch_stream<EPI_BF16, 4, 256, 4, 8>(a, s);
 }
 hipError_t launch_dense_packed_f32(const WGemmArgs& a, hipStream_t s) {
+  if (a.ntok >= kMoeWideTokens) return launch_stream<EPI_F32, 8, 256, 8, 4>(a, s);
   return launch_stream<EPI_F32, 8, 256, 4, 4>(a, s);
 }
 hipError_t launch_lmhead_packed(const WGemmArgs& a, hipStream_t s) {
