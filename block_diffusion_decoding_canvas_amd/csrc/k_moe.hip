@@ -640,8 +640,10 @@ hipError_t launch_moe_down_fp8(const WGemmArgs& a, int tile_rows, hipStream_t s)
   if (tile_rows != 32) return hipErrorInvalidValue;
   return launch_stream<EPI_BF16, 2, 512, 4, 4, true>(a, s);
 }
+// 256-token tiles, as for bf16 weights: one weight pass per canvas, 4 for a batch of four (the
+// 128-token tiles took 8; long-context bench step 1,298.5 -> 1,290.1 ms, A/B on one box)
 hipError_t launch_lmhead_packed_fp8(const WGemmArgs& a, hipStream_t s) {
-  return launch_stream<EPI_LMHEAD, 8, 256, 8, 4, true>(a, s);
+  return launch_stream<EPI_LMHEAD, 16, 256, 8, 4, true>(a, s);
 }
 
 hipError_t launch_pack(const void* src, void* dst, long long rows, long long cols, hipStream_t s) {
