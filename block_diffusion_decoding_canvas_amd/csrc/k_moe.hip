@@ -62,7 +62,7 @@ __device__ __forceinline__ SoftStats stats_rows(const float* y, int n0) {
 // NTB: 16-token blocks per tile; SEG: k per staged token segment; WAVES per workgroup; PS: depth
 // of the weight register ring in steps; F8: e4m3 codes for X and W (with per-row scales)
 // instead of bf16.  A step is one 16-byte fragment load per lane and weight row tile: 32 k of
-// bf16 (one MFMA) or 64 k of e4m3 (two MFMAs).  EPI_SWIGLU: gate/up pairs, 16 features per
+// bf16 (one MFMA) or 64 k of e4m3 (two steps make one 16x16x128 MFMA).  EPI_SWIGLU: gate/up pairs, 16 features per
 // wave (bf16 output, fp32 with F8); otherwise 32 output rows per wave.  EPI_BF16 stores bf16;
 // EPI_F32 stores the fp32 partial of k-split ks in its own plane; EPI_LMHEAD stores bf16
 // logits and, per (token, workgroup block of rows), the softmax statistics of the rounded
