@@ -964,8 +964,8 @@ __global__ __launch_bounds__(PP_NTHR) void k_attn_pp(AttnArgs a) {
     const uint16_t* pl0 = &ps[0][0] + r16 * PP_PST + 8 * lg;
     // phase i (parity P): P V of tile i - 1 with the pieces of K of tile i + 2 and V of tile i + 1
     // loaded into set P ^ 1 spread over its MFMAs, and K of tile i + 1 and V of tile i (loaded in
-    // the phase before, set P) stored to LDS among them (bf16) or after them (e4m3) (clamped: the
-    // last phases re-stage valid tiles that are never read)
+    // the phase before, set P) stored to LDS among them (clamped: the last phases re-stage valid
+    // tiles that are never read)
     auto vphase = [&](int i, auto par) __attribute__((always_inline)) {
       constexpr int P = decltype(par)::value;
       using NX = std::integral_constant<int, P ^ 1>;
@@ -1007,20 +1007,18 @@ __global__ __launch_bounds__(PP_NTHR) void k_attn_pp(AttnArgs a) {
           if (qt + 4 < 8) pr[qt % 4] = ld16(pl + (qt + 4) * 16 * PP_PST);
           if (qt < KPIT) load_k(rk, fk, qt, NX{});
           else if (qt < KPIT + 4) load_v(rv, qt - KPIT, NX{});
-          // bf16 K and V: K of tile i + 1 and V of tile i go to LDS among the MFMAs rather than
-          // after them.  The K buffer was last read by the score waves in phase i - 1 and the V
-          // buffer by these waves in phase i - 1, so both are free once this phase has begun
-          // (56.3 against 58.4 us per call at the decoder shape).  e4m3 keeps them after the
-          // MFMAs: its V stores carry the code conversion, which slowed the long-context
-          // attention by 3.5% among the MFMAs
-          if constexpr (!F8) {
-            if (qt == 2) store_k((i + 1) & 1, par);
-            if (qt == 3) store_v(i & 1, par);
-          }
+          // K of tile i + 1 and V of tile i go to LDS among the MFMAs rather than after them.
+          // The K buffer was last read by the score waves in phase i - 1 and the V buffer by
+          // these waves in phase i - 1, so both are free once this phase has begun.  bf16: after
+          // query tiles 2 and 3 (56.3 against 58.4 us per call at the decoder shape).  e4m3:
+          // after query tiles 5 and 6, later since its V stores carry the code conversion (953
+          // against 938 TFLOP/s on the long-context step; after tiles 2 and 3: 847 against 877)
+          if (qt == (F8 ? 5 : 2)) store_k((i + 1) & 1, par);
+          if (qt == (F8 ? 6 : 3)) store_v(i & 1, par);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (n > 0 && (F8 || i == 0)) {
+      if (n > 0 && i == 0) {
         store_k((i + 1) & 1, par);
         store_v(i & 1, par);
       }
