@@ -143,14 +143,16 @@ def test_capacity_and_state_errors_enqueue_nothing():
         driver.decoder_step(model, kv, 6, driver.eb_params(max_steps=6), gs, out, ws)
 
 
-@pytest.mark.parametrize("d,top_k,E", [(1056, 10, 16), (3072, 8, 16), (256, 2, 6)])
+@pytest.mark.parametrize("d,top_k,E", [(1056, 10, 16), (3072, 8, 16), (256, 2, 6),
+                                         (256, 16, 256)])
 def test_layer_row_shapes(d, top_k, E):
     """One decoder layer over 2 canvases at model widths whose token rows end in a partial
     1024-column chunk (d 1056) or fill three chunks exactly (d 3072), with up to 10 routed
-    experts per token, and an expert count that is not a multiple of 4 (6: the router's output
-    rows are stored element by element): the per-token row kernels (residual + norm, combine +
-    next norm) and the routing against the oracle on every row (the oracle takes the GPU's
-    expert set at router near-ties, checked for validity)."""
+    experts per token, an expert count that is not a multiple of 4 (6: the router's output
+    rows are stored element by element), and the routing maxima the C ABI accepts (256
+    experts, 16 routed per token): the per-token row kernels (residual + norm, combine + next
+    norm) and the routing against the oracle on every row (the oracle takes the GPU's expert
+    set at router near-ties, checked for validity)."""
     dims = dict(n_layers=1, d=d, hq=4, hkv=2, dh=64, E=E, top_k=top_k, F=128, Fs=64, V=256,
                 C=40, window=0, global_every=1, eps=1e-6)
     rng = np.random.default_rng(11)
