@@ -1,4 +1,4 @@
-"""GPU parity at the largest shapes the C ABI accepts.
+"""GPU parity at the largest and smallest shapes the C ABI accepts.
 
 - A canvas of 1,024 positions, the canvas-length maximum of include/dg.h: one commit block sorts
   and prefix-sums the whole canvas. It runs in the standalone sampler, and in a decoder step of
@@ -6,6 +6,8 @@
 - A batch of 64 canvases, the cache-batch maximum, with ragged cache lengths (empty caches
   included). Its 1,024 tokens take the long-call kernel shapes: 128-row expert tiles and 8-wave
   dense products.
+- The canvas of one position, the minimum, in the sampler and in decoder steps on windowed
+  and global layers with caches of 0 to 20 entries, then appended.
 
 The routing maxima (256 experts, 16 routed per token) are a case of
 tests/test_gpu_variants.py::test_layer_row_shapes.
@@ -156,3 +158,72 @@ def test_decoder_step_batch_64():
     cache["len"] = np.array(lens, dtype=np.int64)
     ids = list(range(100, 100 + B))
     assert _lockstep(dims, mnp, cache, cap, ids, seed=34, steps=2, what="B=64") >= 1
+
+
+def _ragged_cache(dims, lens, cap, seed):
+    cache = synth.make_cache(dims, len(lens), cap, max(lens), seed=seed)
+    for b, n in enumerate(lens):               # entries past len[b] are zero
+        for lst in (cache["k"], cache["v"]):
+            for a in lst:
+                a[b, :, n:] = 0.0
+    cache["len"] = np.array(lens, dtype=np.int64)
+    return cache
+
+
+def test_decoder_step_and_append_canvas_1():
+    """The degenerate canvas of one position (the canvas-length minimum), three of them on caches
+    of 0, 5 and 20 entries, with a sliding window of 8 on the first layer (global second): 4
+    decoder steps in lockstep with the oracle, then the append of the final tokens, whose K/V
+    rows are compared with the oracle's encoder pass."""
+    dims = dict(synth.dims_tiny(), hkv=2, C=1, window=8, global_every=2)
+    mnp = synth.make_model(dims, seed=41, norm_gain_std=0.1, lm_std=1.0)
+    lens, cap = (0, 5, 20), 24
+    cache = _ragged_cache(dims, lens, cap, seed=42)
+    ids = [7, 8, 9]
+    assert _lockstep(dims, mnp, cache, cap, ids, seed=43, steps=4, what="C=1") >= 1
+    m64 = synth.model_to_f64(mnp)
+    c64 = dict(k=[a.astype(np.float64) for a in cache["k"]],
+               v=[a.astype(np.float64) for a in cache["v"]], len=np.array(cache["len"]))
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    kv = driver.KVCache.from_host(dims, cache, cap, DEV)
+    ws = driver.workspace(model.workspace_bytes(len(ids)))
+    tokens = np.random.default_rng(44).integers(0, dims["V"], size=(len(ids), 1))
+    chain = GpuChain(dims, model, kv, ws, tokens, mnp["embed"], causal=True)
+    driver.kv_append_canvas(model, kv, torch.tensor(tokens, dtype=torch.int32, device=DEV), ws)
+    torch.cuda.synchronize()
+    om.encoder_append(tokens, m64, c64, force_idx=chain.idx[:-1] + [None])
+    assert kv.lengths() == [n + 1 for n in lens]
+    for layer in range(dims["n_layers"]):
+        for b, n in enumerate(lens):
+            kg = kv.k[layer, b, :, n:n + 1].float().cpu().numpy()
+            vg = kv.v[layer, b, :, n:n + 1].float().cpu().numpy()
+            assert_close_rel(kg, c64["k"][layer][b, :, n:n + 1], what=f"K {layer} b {b}")
+            assert_close_rel(vg, c64["v"][layer][b, :, n:n + 1], what=f"V {layer} b {b}")
+
+
+@pytest.mark.parametrize("bound", [0.0, 0.5])
+def test_sampler_canvas_1(bound):
+    """dg_eb_sample on four canvases of one position, 6 steps with the state carried, against
+    the oracle (bound 0 commits nothing before the last step; 0.5 commits a position as soon as
+    its entropy is under it)."""
+    B, C, V = 4, 1, 512
+    params = dict(osamp.default_params(), entropy_bound=bound, max_steps=6)
+    seed, ids = 8, [1, 2, 3, 4]
+    st = osamp.new_state(osamp.init_canvas(seed, ids, C, V))
+    gs = _gpu_state_from_host(st, B, C, ids)
+    out = driver.StepOut(B, C, V, DEV, with_logits=False)
+    p = driver.eb_params_from_dict(params, seed)
+    compared = 0
+    for s in range(6):
+        z = _small_case(B, C, V, 400 + s, 1.0 + 3.0 * s)
+        driver.eb_sample(synth.to_device_bf16(z, DEV), s, p, gs, out)
+        torch.cuda.synchronize()
+        nxt = compare_step(z.astype(np.float64), s, params, seed, ids, st, gs, out,
+                           f"C=1 bound={bound} s={s}")
+        if nxt is None:
+            break
+        compared += 1
+        st = nxt
+        if st["done"].all():
+            break
+    assert compared >= 1
