@@ -8,6 +8,8 @@ module):
   lengths 700 / 333: 12 and 6 key tiles of 64 ending ragged, so the key range is split and merged)
   in the three attention modes: global bidirectional, a 48-position sliding window, and causal
   canvas keys (the encoder pass, whose cache rows [len, len + C) are compared too);
+- the same layer over the largest canvas the C ABI accepts (1,024 positions), global and causal,
+  on caches of 300 entries and of none;
 - a 2-layer model with head_dim 128: a 40-token prompt prefilled into an empty fp8 cache in two
   calls (16 + 24), then one decoder step over a 16-position canvas, against the oracle's encoding
   and decoder pass (the oracle takes the GPU's expert sets at router near-ties).
@@ -77,10 +79,19 @@ def test_fp8_kv_layer_short_and_empty_cache(mode):
     _fp8_layer_case(256, mode, (20, 0), 64)
 
 
-def _fp8_layer_case(dh, mode, lens, cap):
+@pytest.mark.parametrize("mode", ["global", "causal"])
+@pytest.mark.parametrize("dh", [128, 256])
+def test_fp8_kv_layer_canvas_1024(dh, mode):
+    """The largest canvas the C ABI accepts (1,024 positions: 32 canvas key tiles, and in causal
+    mode a canvas mask that ends in a different tile for each query block) on e4m3 caches of
+    300 entries and of none, decoder and encoder pass."""
+    _fp8_layer_case(dh, mode, (300, 0), 1400, C=1024)
+
+
+def _fp8_layer_case(dh, mode, lens, cap, C=40):
     window = 48 if mode == "window" else 0
     causal = 1 if mode == "causal" else 0
-    dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=dh, E=8, top_k=2, F=64, Fs=64, V=256, C=40,
+    dims = dict(n_layers=1, d=64, hq=4, hkv=2, dh=dh, E=8, top_k=2, F=64, Fs=64, V=256, C=C,
                 window=window, global_every=2, eps=1e-6, kv_dtype="e4m3")
     rng = np.random.default_rng(41 + dh)
     mnp = dict(dims=dims, layers=[synth.make_layer(dims, rng, norm_gain_std=0.1)],
@@ -92,7 +103,7 @@ def _fp8_layer_case(dh, mode, lens, cap):
     cache["len"] = np.array(lens, dtype=np.int64)
     T = B * C
     h = synth.hidden_states(T, 64, seed=43)
-    print(f"fp8 kv case dh={dh} mode={mode} lens={lens}", flush=True)
+    print(f"fp8 kv case dh={dh} mode={mode} lens={lens} C={C}", flush=True)
     model = driver.Model(synth.model_to_device(mnp, DEV))
     kv = driver.KVCache.from_host(dims, cache, cap, DEV)
     ws = driver.workspace(model.workspace_bytes(B))
