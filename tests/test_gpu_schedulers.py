@@ -4,7 +4,8 @@ oracle (oracle/schedulers.py), on identical bf16 logits.
 Workloads: the standalone sampler's row mix (peaked rows with one logit 12 over N(0,1), N(0, 2)
 rows and N(0, 0.1) rows) at V 262,144 (block refinement) and V 65,536 (DDIM, whose every row
 draws from its posterior each step), greedy and sampled temperatures, threshold, quota, editing,
-predictor, corrector and final steps; and the toy decoder with a sharp LM head run through
+predictor, corrector and final steps; both schedulers on canvases of 1 and 1,024 positions (the
+C ABI's canvas-length extremes) at V 512; and the toy decoder with a sharp LM head run through
 dg_decoder_step_sched in lockstep with the oracle.
 
 Integers are compared exactly wherever the oracle's decision is robust to the GPU's float error:
@@ -231,3 +232,62 @@ def test_decoder_step_sched_lockstep(kind):
         if st["done"].all():
             break
     assert st["done"].all()
+
+
+@pytest.mark.parametrize("C", [1, 1024])
+def test_block_refinement_canvas_extremes(C):
+    """Block refinement on the smallest and the largest canvas the C ABI accepts (1 and 1,024
+    positions; at 1,024 the confidence order spans the whole commit block), sampled with
+    editing, against the oracle exactly where robust."""
+    B, V = 2, 512
+    z = _logits(B, C, V, seed=51 + C)
+    zt = torch.from_numpy(z).to(DEV, torch.bfloat16)
+    z64 = z.astype(np.float64)
+    params = osch.default_params(osch.BLOCK_REFINEMENT)
+    params.update(max_steps=8, temperature=0.5, editing_threshold=0.3, stop_entropy=-1.0)
+    seed, ids = 6, [2, 5]
+    rng = np.random.default_rng(52)
+    exact_total = 0
+    for step, frac in [(0, 0.0), (3, 0.4), (6, 0.7)]:
+        print(f"BR C={C} step {step}", flush=True)
+        st = _state_with_commits(z, ids, seed, frac, rng)
+        exact, commits, edits = _compare_br(zt, z64, step, params, seed, ids, st)
+        print(f"  exact canvases {exact}/{B}, commits {commits}, edits {edits}", flush=True)
+        exact_total += exact
+    assert exact_total >= 1
+
+
+@pytest.mark.parametrize("C,k", [(1, 1), (1024, 300)])
+def test_discrete_ddim_canvas_extremes(C, k):
+    """Discrete DDIM with its leave-one-out corrector on the smallest and the largest canvas
+    (1 and 1,024 positions; the corrector re-draws the k least confident), predictor,
+    corrector and final steps, against the oracle exactly where robust."""
+    B, V, S = 2, 512, 10
+    z = _logits(B, C, V, seed=61 + C)
+    zt = torch.from_numpy(z).to(DEV, torch.bfloat16)
+    z64 = z.astype(np.float64)
+    params = osch.default_params(osch.DISCRETE_DDIM)
+    params.update(max_steps=S, temperature=0.8, corrector_steps=3, corrector_k=k,
+                  stop_entropy=-1.0)
+    seed, ids = 11, [0, 3]
+    inv_t = osch.inv_temperature_f32(0.8)
+    st = osamp.new_state(osamp.init_canvas(seed, ids, C, V))
+    exact = 0
+    for step in (0, 3, 5, 6, 8, 9):       # predictor, predictor, predictor, corrector x2, final
+        print(f"DDIM C={C} step {step}", flush=True)
+        before = copy.deepcopy(st)
+        gs, out = _run_gpu(zt, step, params, seed, ids, st)
+        ref = osch.discrete_ddim_step(z64, step, params, st, seed, ids)
+        assert_entropy_close(out.entropy.cpu().numpy(), ref["entropy"], f"DDIM entropy s={step}")
+        g = gs.host()
+        cn = out.commit_now.cpu().numpy().astype(bool)
+        assert np.array_equal(cn, ref["commit_now"])
+        for b in range(B):
+            if not _ddim_robust(ref, None, b, before, z64, params, inv_t):
+                st["canvas"][b] = g["canvas"][b]          # continue from the GPU's valid draw
+                continue
+            for key in ("canvas", "committed", "done", "stable_count", "prev_argmax"):
+                assert np.array_equal(g[key][b], st[key][b]), f"{key} b={b} s={step}"
+            exact += 1
+    assert exact >= 6
+    assert st["done"].all() and st["committed"].all()
