@@ -4,7 +4,8 @@ step does, and leaves the frozen canvases alone.
 
 Workloads: the toy decoder with a sharp LM head (commits mid-run, so the canvases of a batch of 3
 freeze at different steps), run step by step with and without compaction and through the
-generation loop; and two full-width layers with the 262,144-entry vocabulary, a batch of 4
+generation loop; the same toy decoder over 64 canvases, whose live steps drop from the long-call
+kernel shapes to the decoder-step ones as canvases freeze; and two full-width layers with the 262,144-entry vocabulary, a batch of 4
 canvases (1,024 tokens: the wide tile configurations) against 2 live ones (512 tokens).
 """
 import numpy as np
@@ -116,3 +117,46 @@ def test_compacted_full_width_bit_identical():
         comp.canvas.copy_(full.canvas)
         comp.prev_argmax.copy_(full.prev_argmax)
         comp.stable_count.copy_(full.stable_count)
+
+
+def test_compacted_steps_batch_64_across_tile_shapes():
+    """64 toy canvases (1,024 tokens: the long-call expert tiles and dense shapes) on caches of
+    ragged lengths from 0 to 40; as canvases freeze, the live steps fall under 1,024 tokens and
+    take the decoder-step shapes while the full step keeps the long-call ones.  State and live
+    outputs bit for bit, step by step."""
+    dims = synth.dims_tiny()
+    mnp = synth.make_model(dims, seed=0, norm_gain_std=0.1, lm_std=1.0)
+    model = driver.Model(synth.model_to_device(mnp, DEV))
+    B, C, V, cap = 64, dims["C"], dims["V"], 64
+    cache = synth.make_cache(dims, B, cap, 40, seed=2)
+    lens = np.random.default_rng(3).integers(0, 41, size=B)
+    for b, n in enumerate(lens):
+        for lst in (cache["k"], cache["v"]):
+            for a in lst:
+                a[b, :, n:] = 0.0
+    cache["len"] = lens
+    kv = driver.KVCache.from_host(dims, cache, cap, DEV)
+    ws = driver.workspace(model.workspace_bytes(B))
+    p = driver.sched_params("entropy_bound", max_steps=12, seed=6, temperature=0.6)
+    ids = list(range(200, 200 + B))
+    full, comp = (driver.SamplerState(B, C, DEV, canvas_ids=ids) for _ in range(2))
+    driver.canvas_init(driver.eb_params(seed=6), full, V)
+    driver.canvas_init(driver.eb_params(seed=6), comp, V)
+    of, oc = driver.StepOut(B, C, V, DEV), driver.StepOut(B, C, V, DEV)
+    n_live = []
+    for s in range(12):
+        live = [b for b in range(B) if not bool(comp.done[b])]
+        if not live:
+            break
+        n_live.append(len(live))
+        driver.decoder_step_sched(model, kv, s, p, full, of, ws)
+        driver.decoder_step_live(model, kv, s, p, comp, oc, live, ws)
+        torch.cuda.synchronize()
+        _state_equal(full, comp)
+        lv = torch.tensor(live, device=DEV)
+        for a, b in ((of.logits, oc.logits), (of.entropy, oc.entropy), (of.argmax, oc.argmax),
+                     (of.commit_now, oc.commit_now)):
+            assert torch.equal(a[lv], b[lv])
+    print(f"live canvases per step: {n_live}", flush=True)
+    assert any(0 < n < B for n in n_live), "the canvases froze together: no compacted step"
+    assert bool(full.done.all())
