@@ -65,9 +65,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // CDNA4 transposing LDS read of 16-bit data: within each group of 16 lanes, lane 4a + b receives
 // element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12 (in that order)
-// streaming (non-temporal) 16-byte load for the K/V tiles of the head_dim-256 kernel: a step reads
-// each cached row once, and with the hint the 67 MB of cache rows of a layer stop displacing the
-// rows other kernels re-read from L2 (a decoder step measured 11.81 against 11.91 ms)
+// streaming (non-temporal) 16-byte load for the bf16 K/V tiles of the head_dim-256 kernel: a step
+// reads each cached row once, and with the hint the 67 MB of cache rows of a layer stop displacing
+// the rows other kernels re-read from L2 (a decoder step measured 11.81 against 11.91 ms).  The
+// e4m3 tiles keep plain loads: on 4 x 131,072-key caches the hint cost 1% of attention time
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -878,9 +879,10 @@ __global__ __launch_bounds__(PP_NTHR) void k_attn_pp(AttnArgs a) {
     // piece it of tile tt (rows t) into set S; K piece 0 also brings the fp8 scales
     auto load_k = [&](const TileRows& t, int tt, int it, auto set_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(set_tag)::value;
-      pk[S][it] = ld16_stream(t.k + (static_cast<uint32_t>(min(k_key[it], t.last)) *
-                                      static_cast<uint32_t>(t.stride) +
-                                  static_cast<uint32_t>(k_col[it])));
+      const uint8_t* kp = t.k + (static_cast<uint32_t>(min(k_key[it], t.last)) *
+                                     static_cast<uint32_t>(t.stride) +
+                                 static_cast<uint32_t>(k_col[it]));
+      pk[S][it] = F8 ? ld16(kp) : ld16_stream(kp);
       if constexpr (F8) {
         if (it != 0) return;
         if (vt < KTP) {
